@@ -1,0 +1,217 @@
+/*
+ * svg2.h - C ABI of the SVG2 semantic-aware-permutation sparse attention path
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow the method as the page "Sparse VideoGen2: Accelerate
+ * Video Generation with Sparse Attention via Semantic-Aware Permutation" (a
+ * paper-wiki summary) states it, per attention head and layer:
+ *   svg2_kmeans        k-means on the Q tokens or the K tokens, seeded by
+ *                      k-means++ or warm-started from cached centroids
+ *                      [Method, stage (1); Key claims, §4.1, §4.3 / Fig. 7(a)]
+ *   svg2_permute       reorder rows into contiguous cluster blocks; K and V
+ *                      share one permutation   [Method, stage (2)]
+ *   svg2_select_topp   centroid-based score estimate weighted by cluster
+ *                      size, top-p K-cluster selection per Q-cluster
+ *                      [Method, stage (3); Key claims, §4.2, Eq. 1, Eq. 2]
+ *   svg2_varblock_attn attention over variable-sized cluster blocks with no
+ *                      padding to a fixed block size
+ *                      [Method, stage (4); Key claims, §4.3 / Fig. 7(b)]
+ *   svg2_unpermute     the inverse permutation of the output rows
+ *                      [Method, stage (2)]
+ *
+ * Conventions shared by every call
+ *   - Tensor arguments are DEVICE pointers allocated by the caller, 16-byte
+ *     aligned.  Head_dim is innermost.  "bh" is batch * heads: the calls
+ *     batch independent (batch, head) problems.
+ *   - Ownership: every buffer belongs to the caller; the library keeps no
+ *     pointer after a call returns and holds no state between calls.
+ *   - Every call is asynchronous on `stream` (0 = the null stream); none
+ *     allocates device memory, frees or synchronises.  Buffers must stay
+ *     alive until the queued work has finished.
+ *   - Errors: a call returns SVG2_OK or an error status.  All arguments are
+ *     validated on the host before any HIP call; on an error nothing is
+ *     enqueued.  A failing kernel launch returns SVG2_ERR_HIP and
+ *     svg2_last_hip_error() gives the hipError_t (per thread).
+ *   - Workspace: calls that need scratch memory take (workspace,
+ *     workspace_bytes); svg2_*_workspace_size gives the minimum.  Its content
+ *     on entry does not matter and on exit is unspecified.
+ *   - Results are bitwise reproducible run to run (no floating-point atomics).
+ *   - Supported: head_dim 64 or 128; dtype fp32 or bf16; 1 <= n_clusters <=
+ *     min(n_tokens, 4096); 1 <= n_tokens <= 2^24.
+ */
+#ifndef SVG2_H
+#define SVG2_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum svg2_status {
+  SVG2_OK = 0,
+  SVG2_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, size out of range  */
+  SVG2_ERR_UNSUPPORTED = 2,   /* valid but unsupported shape or dtype        */
+  SVG2_ERR_WORKSPACE = 3,     /* workspace smaller than *_workspace_size()   */
+  SVG2_ERR_HIP = 4            /* a HIP call failed; see svg2_last_hip_error  */
+} svg2_status;
+
+typedef enum svg2_dtype {
+  SVG2_F32 = 0,               /* IEEE binary32                               */
+  SVG2_BF16 = 1               /* bfloat16 (upper half of a binary32)         */
+} svg2_dtype;
+
+const char* svg2_version(void);
+const char* svg2_status_string(int status);
+int svg2_last_hip_error(void);
+
+/* ------------------------------------------------------------------------
+ * svg2_kmeans - k-means of the rows of x, independently for each of the bh
+ * problems  [Method, stage (1); Key claims, §4.3 / Fig. 7(a)].
+ *
+ *   x               [bh, n_tokens, head_dim] dtype, contiguous.
+ *   init_centroids  [bh, n_clusters, head_dim] fp32 (warm start, the centroid
+ *                   cache of the previous denoising step), or NULL: cold start
+ *                   by k-means++ (first centre floor(u_0 N), each further
+ *                   centre the smallest token t whose running sum of D^2
+ *                   exceeds u_k * sum D^2, D^2 = squared distance to the
+ *                   nearest chosen centre; u_k = top 53 bits of
+ *                   splitmix64(seed ^ (problem * 2^32 + k)) * 2^-53).
+ *   n_iters         T in [0, 100] Lloyd rounds, each = assign every token to
+ *                   its nearest centroid (squared Euclidean, ties to the lowest
+ *                   index), then set every non-empty centroid to the mean of
+ *                   its members (an empty one keeps its value).  T = 0 only
+ *                   seeds (or copies init_centroids).
+ *   centroids       out [bh, n_clusters, head_dim] fp32; may alias
+ *                   init_centroids (in-place cache update).
+ *   labels          out [bh, n_tokens] int32: labels of the T-th assignment
+ *                   (not written when T = 0; may then be NULL).
+ *   counts          out [bh, n_clusters] int32: member counts of those labels
+ *                   (not written when T = 0; may then be NULL).
+ *   min_dist        out [bh, n_tokens] fp32 or NULL: ||x - c_label||^2 at the
+ *                   T-th assignment.
+ *   seed_index      out [bh, n_clusters] int32 or NULL: token index of each
+ *                   k-means++ pick (cold start only).
+ * Limits: k-means++ (init_centroids NULL) needs n_tokens <= 262144.
+ * ---------------------------------------------------------------------- */
+size_t svg2_kmeans_workspace_size(int32_t bh, int32_t n_tokens, int32_t head_dim,
+                                  int32_t n_clusters);
+int svg2_kmeans(const void* x, int32_t dtype, int32_t bh, int32_t n_tokens,
+                int32_t head_dim, int32_t n_clusters, int32_t n_iters,
+                const float* init_centroids, uint64_t seed,
+                float* centroids, int32_t* labels, int32_t* counts,
+                float* min_dist, int32_t* seed_index,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * svg2_permute - build the permutation of each problem from its cluster
+ * labels and gather rows into contiguous cluster blocks; with n_tensors = 2
+ * the same permutation is applied to both (K and V)  [Method, stage (2)].
+ *
+ *   labels          [bh, n_tokens] int32 in [0, n_clusters).  A label out of
+ *                   range is clamped into it (memory stays safe; the result
+ *                   is then unspecified).
+ *   src[t]          host array of n_tensors device pointers; element (p, i, e)
+ *                   of source t is at
+ *                   src[t] + (p / heads) * src_b_stride + (p % heads) *
+ *                   src_h_stride + i * src_token_stride + e   (in elements),
+ *                   which covers [B,H,N,d] and [B,N,H,d] layouts.
+ *   dst[t]          host array of device pointers, contiguous
+ *                   [bh, n_tokens, head_dim].
+ *   perm            out [bh, n_tokens] int32: perm[i] = original token placed
+ *                   at slot i; clusters in ascending label order, tokens of a
+ *                   cluster in ascending original index.
+ *   offsets         out [bh, n_clusters + 1] int32: cluster c occupies slots
+ *                   [offsets[c], offsets[c+1]).
+ * Strides must be multiples of 16 bytes / element size.
+ * ---------------------------------------------------------------------- */
+size_t svg2_permute_workspace_size(int32_t bh, int32_t n_tokens, int32_t n_clusters);
+int svg2_permute(const int32_t* labels, int32_t bh, int32_t n_tokens,
+                 int32_t n_clusters, int32_t n_tensors, const void* const* src,
+                 int32_t heads, int64_t src_b_stride, int64_t src_h_stride,
+                 int64_t src_token_stride, void* const* dst, int32_t dtype,
+                 int32_t head_dim, int32_t* perm, int32_t* offsets,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * svg2_select_topp - per Q-cluster i, estimate the attention mass of every
+ * K-cluster j from the centroids and choose the fewest K-clusters whose
+ * estimated mass reaches top_p  [Method, stage (3); Key claims, §4.2].
+ *
+ *   l_ij = scale * cq_i . ck_j;  w_ij = |K_j| exp(l_ij - max_l l_il) over
+ *   non-empty K-clusters;  P_ij = w_ij / sum_l w_il.  Sort by (-P, j), keep
+ *   the shortest prefix whose running sum is >= top_p (top_p >= 1 keeps every
+ *   non-empty cluster).  Computed in fp64.
+ *
+ *   q_centroids     [bh, n_q, head_dim] fp32;  q_counts [bh, n_q] int32.
+ *   k_centroids     [bh, n_k, head_dim] fp32;  k_counts [bh, n_k] int32.
+ *   scale           > 0 (the pipeline uses 1/sqrt(head_dim)); top_p in (0, 1].
+ *   sel_count       out [bh, n_q] int32.
+ *   sel_idx         out [bh, n_q, n_k] int32: row i holds the sel_count[i]
+ *                   chosen K-clusters in ascending order; the rest of the row
+ *                   is left unspecified.
+ *   probs           out [bh, n_q, n_k] fp32 or NULL: P (0 for empty clusters).
+ *   pair_count      out [bh] int64 or NULL: sum_i |Q_i| sum_{j in S_i} |K_j|.
+ * ---------------------------------------------------------------------- */
+size_t svg2_select_topp_workspace_size(int32_t bh, int32_t n_q, int32_t n_k);
+int svg2_select_topp(const float* q_centroids, const int32_t* q_counts, int32_t n_q,
+                     const float* k_centroids, const int32_t* k_counts, int32_t n_k,
+                     int32_t bh, int32_t head_dim, float scale, float top_p,
+                     int32_t* sel_count, int32_t* sel_idx, float* probs,
+                     int64_t* pair_count, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * svg2_varblock_attn - block-sparse attention over variable-sized cluster
+ * blocks of permuted Q', K', V'  [Method, stage (4); Key claims, §4.3].
+ *
+ *   Row r of Q-cluster i (r in [q_offsets[i], q_offsets[i+1])) attends to the
+ *   key rows of its selected K-clusters, K(i) = union over j in S_i of
+ *   [k_offsets[j], k_offsets[j+1]):
+ *     out_r = sum_{u in K(i)} softmax_u(scale * q_r . k_u) v_u,
+ *     lse_r = log sum_{u in K(i)} exp(scale * q_r . k_u)   (natural log).
+ *   A row whose selection holds no key gets out = 0, lse = -inf.
+ *   bf16: products on bf16 matrix cores with fp32 accumulation, softmax in
+ *   fp32, probabilities rounded to bf16 before the P.V product, output
+ *   rounded to bf16.  fp32: fp32 throughout.
+ *
+ *   q, k, v         [bh, n_tokens, head_dim] dtype, contiguous (permuted).
+ *   q_offsets       [bh, n_q + 1], k_offsets [bh, n_k + 1] int32 (monotone,
+ *                   0 .. n_tokens).
+ *   sel_count       [bh, n_q] int32; sel_idx [bh, n_q, n_k] int32 (indices in
+ *                   [0, n_k); order is free; a repeated index is attended twice).
+ *   out             out [bh, n_tokens, head_dim] dtype, permuted order.
+ *   lse             out [bh, n_tokens] fp32 or NULL.
+ * Dense attention is the special case n_q = n_k = 1, offsets {0, N}, sel {0}.
+ * ---------------------------------------------------------------------- */
+size_t svg2_varblock_attn_workspace_size(int32_t bh, int32_t n_tokens, int32_t n_q,
+                                         int32_t n_k, int32_t head_dim);
+int svg2_varblock_attn(const void* q, const void* k, const void* v, int32_t dtype,
+                       int32_t bh, int32_t n_tokens, int32_t head_dim,
+                       const int32_t* q_offsets, int32_t n_q,
+                       const int32_t* k_offsets, int32_t n_k,
+                       const int32_t* sel_count, const int32_t* sel_idx, float scale,
+                       void* out, float* lse, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * svg2_unpermute - scatter rows back to the original token order:
+ * dst row perm[i] = src row i  [Method, stage (2)].
+ *
+ *   src             [bh, n_tokens, head_dim] dtype, contiguous.
+ *   perm            [bh, n_tokens] int32, a permutation of 0..n_tokens-1 (an
+ *                   index out of range is skipped).
+ *   dst             element (p, t, e) at dst + (p / heads) * dst_b_stride +
+ *                   (p % heads) * dst_h_stride + t * dst_token_stride + e.
+ * ---------------------------------------------------------------------- */
+int svg2_unpermute(const void* src, int32_t dtype, int32_t bh, int32_t n_tokens,
+                   int32_t head_dim, const int32_t* perm, void* dst, int32_t heads,
+                   int64_t dst_b_stride, int64_t dst_h_stride, int64_t dst_token_stride,
+                   hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SVG2_H */

@@ -1,0 +1,294 @@
+"""Python binding of libsvg2 (ctypes).
+
+Argument marshalling only: these wrappers check shapes and dtypes, allocate
+outputs and workspace with torch on the tensors' device, and pass raw device
+pointers plus torch's current HIP stream to the C ABI declared in
+include/svg2.h.  Every step of the computation runs in the library's HIP
+kernels; nothing here computes, and there is no fallback: without the built
+library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsvg2.so")
+_lib = None
+
+F32, BF16 = 0, 1
+_c_int, _c_i64, _c_u64, _c_sz, _c_p = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_size_t, ctypes.c_void_p
+
+EXPORTED = [
+    "svg2_version", "svg2_status_string", "svg2_last_hip_error",
+    "svg2_kmeans_workspace_size", "svg2_kmeans",
+    "svg2_permute_workspace_size", "svg2_permute",
+    "svg2_select_topp_workspace_size", "svg2_select_topp",
+    "svg2_varblock_attn_workspace_size", "svg2_varblock_attn",
+    "svg2_unpermute",
+]
+
+
+class Svg2Error(RuntimeError):
+    pass
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Loads libsvg2.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise Svg2Error(f"{_LIB_PATH} is missing: build it with "
+                        "`python -m sparse_attention_video_head_amd.build`")
+    L = ctypes.CDLL(_LIB_PATH)
+    L.svg2_version.restype = ctypes.c_char_p
+    L.svg2_status_string.restype = ctypes.c_char_p
+    L.svg2_status_string.argtypes = [ctypes.c_int]
+    L.svg2_last_hip_error.restype = ctypes.c_int
+    L.svg2_kmeans_workspace_size.restype = _c_sz
+    L.svg2_kmeans_workspace_size.argtypes = [_c_int] * 4
+    L.svg2_kmeans.restype = ctypes.c_int
+    L.svg2_kmeans.argtypes = [_c_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_p, _c_u64,
+                              _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]
+    L.svg2_permute_workspace_size.restype = _c_sz
+    L.svg2_permute_workspace_size.argtypes = [_c_int] * 3
+    L.svg2_permute.restype = ctypes.c_int
+    L.svg2_permute.argtypes = [_c_p, _c_int, _c_int, _c_int, _c_int, _c_p, _c_int, _c_i64, _c_i64, _c_i64,
+                               _c_p, _c_int, _c_int, _c_p, _c_p, _c_p, _c_sz, _c_p]
+    L.svg2_select_topp_workspace_size.restype = _c_sz
+    L.svg2_select_topp_workspace_size.argtypes = [_c_int] * 3
+    L.svg2_select_topp.restype = ctypes.c_int
+    L.svg2_select_topp.argtypes = [_c_p, _c_p, _c_int, _c_p, _c_p, _c_int, _c_int, _c_int, ctypes.c_float,
+                                   ctypes.c_float, _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]
+    L.svg2_varblock_attn_workspace_size.restype = _c_sz
+    L.svg2_varblock_attn_workspace_size.argtypes = [_c_int] * 5
+    L.svg2_varblock_attn.restype = ctypes.c_int
+    L.svg2_varblock_attn.argtypes = [_c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_p, _c_int, _c_p,
+                                     _c_int, _c_p, _c_p, ctypes.c_float, _c_p, _c_p, _c_p, _c_sz, _c_p]
+    L.svg2_unpermute.restype = ctypes.c_int
+    L.svg2_unpermute.argtypes = [_c_p, _c_int, _c_int, _c_int, _c_int, _c_p, _c_p, _c_int, _c_i64, _c_i64,
+                                 _c_i64, _c_p]
+    _lib = L
+    return L
+
+
+def version() -> str:
+    return lib().svg2_version().decode()
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        L = lib()
+        msg = L.svg2_status_string(status).decode()
+        raise Svg2Error(f"{what}: {msg} (status {status}, hip error {L.svg2_last_hip_error()})")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise Svg2Error(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise Svg2Error("svg2 operates on GPU tensors only")
+
+
+def _workspace(nbytes: int, dev, workspace: Optional[torch.Tensor]):
+    if nbytes == 0:
+        return None
+    if workspace is not None and workspace.numel() * workspace.element_size() >= nbytes:
+        return workspace
+    return torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+
+# ---------------------------------------------------------------- kmeans
+def kmeans(x: torch.Tensor, n_clusters: int, n_iters: int, init: Optional[torch.Tensor] = None,
+           seed: int = 0, min_dist: bool = False, seed_index: bool = False,
+           centroids: Optional[torch.Tensor] = None, labels: Optional[torch.Tensor] = None,
+           counts: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """k-means of x [bh, N, d] (contiguous).  Returns dict(centroids [bh,n,d] fp32,
+    labels [bh,N] int32, counts [bh,n] int32, min_dist, seed_index)."""
+    _need_cuda(x, init)
+    if x.dim() != 3 or not x.is_contiguous():
+        raise Svg2Error("x must be a contiguous [bh, N, d] tensor")
+    bh, N, d = x.shape
+    dev = x.device
+    if centroids is None:
+        centroids = torch.empty(bh, n_clusters, d, dtype=torch.float32, device=dev)
+    if init is not None and (init.dtype != torch.float32 or not init.is_contiguous()
+                             or tuple(init.shape) != (bh, n_clusters, d)):
+        raise Svg2Error("init must be a contiguous fp32 [bh, n_clusters, d] tensor")
+    if labels is None and n_iters > 0:
+        labels = torch.empty(bh, N, dtype=torch.int32, device=dev)
+    if counts is None and n_iters > 0:
+        counts = torch.empty(bh, n_clusters, dtype=torch.int32, device=dev)
+    md = torch.empty(bh, N, dtype=torch.float32, device=dev) if min_dist else None
+    si = torch.empty(bh, n_clusters, dtype=torch.int32, device=dev) if seed_index else None
+    L = lib()
+    ws_n = L.svg2_kmeans_workspace_size(bh, N, d, n_clusters)
+    ws = _workspace(ws_n, dev, workspace)
+    st = L.svg2_kmeans(_ptr(x), _dtype_code(x), bh, N, d, n_clusters, n_iters, _ptr(init),
+                       ctypes.c_uint64(seed & ((1 << 64) - 1)), _ptr(centroids), _ptr(labels),
+                       _ptr(counts), _ptr(md), _ptr(si), _ptr(ws), ws_n, _stream(dev))
+    _check(st, "svg2_kmeans")
+    return dict(centroids=centroids, labels=labels, counts=counts, min_dist=md, seed_index=si)
+
+
+# ---------------------------------------------------------------- permute
+def _strided_view(t: torch.Tensor):
+    """(bh, N, d, heads, sb, sh, st) of a [bh,N,d] or [B,H,N,d] view whose
+    last dimension is contiguous."""
+    if t.stride(-1) != 1:
+        raise Svg2Error("the head dimension must be contiguous")
+    if t.dim() == 3:
+        bh, N, d = t.shape
+        return bh, N, d, 1, t.stride(0), 0, t.stride(1)
+    if t.dim() == 4:
+        B, H, N, d = t.shape
+        return B * H, N, d, H, t.stride(0), t.stride(1), t.stride(2)
+    raise Svg2Error("expected a [bh, N, d] or [B, H, N, d] tensor")
+
+
+def permute(labels: torch.Tensor, n_clusters: int, *tensors: torch.Tensor,
+            outs: Optional[Sequence[torch.Tensor]] = None, perm: Optional[torch.Tensor] = None,
+            offsets: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Gathers rows of 1 or 2 tensors into cluster order.  Returns
+    (list of contiguous [bh, N, d] tensors, perm [bh,N] int32, offsets [bh,n+1] int32)."""
+    _need_cuda(labels, *tensors)
+    if not 1 <= len(tensors) <= 2:
+        raise Svg2Error("permute takes one or two tensors")
+    views = [_strided_view(t) for t in tensors]
+    if len(set(views)) != 1 or len({t.dtype for t in tensors}) != 1:
+        raise Svg2Error("permuted tensors must share shape, strides and dtype")
+    bh, N, d, heads, sb, sh, st = views[0]
+    if labels.dtype != torch.int32 or not labels.is_contiguous() or tuple(labels.shape) != (bh, N):
+        raise Svg2Error("labels must be contiguous int32 [bh, N]")
+    dev = labels.device
+    if outs is None:
+        outs = [torch.empty(bh, N, d, dtype=tensors[0].dtype, device=dev) for _ in tensors]
+    for o in outs:
+        if tuple(o.shape) != (bh, N, d) or not o.is_contiguous() or o.dtype != tensors[0].dtype:
+            raise Svg2Error("permute outputs must be contiguous [bh, N, d] of the input dtype")
+    if perm is None:
+        perm = torch.empty(bh, N, dtype=torch.int32, device=dev)
+    if offsets is None:
+        offsets = torch.empty(bh, n_clusters + 1, dtype=torch.int32, device=dev)
+    L = lib()
+    ws_n = L.svg2_permute_workspace_size(bh, N, n_clusters)
+    ws = _workspace(ws_n, dev, workspace)
+    src = (ctypes.c_void_p * 2)(*[t.data_ptr() for t in tensors], *([0] * (2 - len(tensors))))
+    dst = (ctypes.c_void_p * 2)(*[t.data_ptr() for t in outs], *([0] * (2 - len(outs))))
+    s = L.svg2_permute(_ptr(labels), bh, N, n_clusters, len(tensors), src, heads, sb, sh, st, dst,
+                       _dtype_code(tensors[0]), d, _ptr(perm), _ptr(offsets), _ptr(ws), ws_n, _stream(dev))
+    _check(s, "svg2_permute")
+    return outs, perm, offsets
+
+
+# ---------------------------------------------------------------- select
+def select_topp(q_centroids: torch.Tensor, q_counts: torch.Tensor, k_centroids: torch.Tensor,
+                k_counts: torch.Tensor, top_p: float, scale: Optional[float] = None,
+                probs: bool = False, sel_count: Optional[torch.Tensor] = None,
+                sel_idx: Optional[torch.Tensor] = None, pair_count: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None):
+    """Top-p K-cluster selection per Q-cluster.  Returns dict(sel_count [bh,n_q],
+    sel_idx [bh,n_q,n_k], probs, pair_count [bh] int64)."""
+    _need_cuda(q_centroids, q_counts, k_centroids, k_counts)
+    bh, n_q, d = q_centroids.shape
+    n_k = k_centroids.shape[1]
+    for t, dt in ((q_centroids, torch.float32), (k_centroids, torch.float32), (q_counts, torch.int32),
+                  (k_counts, torch.int32)):
+        if t.dtype != dt or not t.is_contiguous():
+            raise Svg2Error("centroids must be contiguous fp32, counts contiguous int32")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dev = q_centroids.device
+    if sel_count is None:
+        sel_count = torch.empty(bh, n_q, dtype=torch.int32, device=dev)
+    if sel_idx is None:
+        sel_idx = torch.empty(bh, n_q, n_k, dtype=torch.int32, device=dev)
+    pr = torch.empty(bh, n_q, n_k, dtype=torch.float32, device=dev) if probs else None
+    pairs = pair_count if pair_count is not None else torch.empty(bh, dtype=torch.int64, device=dev)
+    L = lib()
+    ws_n = L.svg2_select_topp_workspace_size(bh, n_q, n_k)
+    ws = _workspace(ws_n, dev, workspace)
+    s = L.svg2_select_topp(_ptr(q_centroids), _ptr(q_counts), n_q, _ptr(k_centroids), _ptr(k_counts), n_k,
+                           bh, d, ctypes.c_float(scale), ctypes.c_float(top_p), _ptr(sel_count),
+                           _ptr(sel_idx), _ptr(pr), _ptr(pairs), _ptr(ws), ws_n, _stream(dev))
+    _check(s, "svg2_select_topp")
+    return dict(sel_count=sel_count, sel_idx=sel_idx, probs=pr, pair_count=pairs)
+
+
+# ---------------------------------------------------------------- attention
+def varblock_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_offsets: torch.Tensor,
+                  k_offsets: torch.Tensor, sel_count: torch.Tensor, sel_idx: torch.Tensor,
+                  scale: Optional[float] = None, lse: bool = False, out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None):
+    """Variable-block sparse attention on permuted contiguous [bh, N, d]
+    tensors.  Returns (out [bh,N,d], lse [bh,N] fp32 or None)."""
+    _need_cuda(q, k, v, q_offsets, k_offsets, sel_count, sel_idx)
+    for t in (q, k, v):
+        if t.dim() != 3 or not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype:
+            raise Svg2Error("q, k, v must be contiguous [bh, N, d] tensors of one dtype")
+    bh, N, d = q.shape
+    n_q = q_offsets.shape[1] - 1
+    n_k = k_offsets.shape[1] - 1
+    for t in (q_offsets, k_offsets, sel_count, sel_idx):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise Svg2Error("offsets and lists must be contiguous int32")
+    if tuple(sel_count.shape) != (bh, n_q) or tuple(sel_idx.shape) != (bh, n_q, n_k):
+        raise Svg2Error("sel_count [bh, n_q] and sel_idx [bh, n_q, n_k] expected")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    ls = torch.empty(bh, N, dtype=torch.float32, device=dev) if lse else None
+    L = lib()
+    ws_n = L.svg2_varblock_attn_workspace_size(bh, N, n_q, n_k, d)
+    ws = _workspace(ws_n, dev, workspace)
+    s = L.svg2_varblock_attn(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), bh, N, d, _ptr(q_offsets), n_q,
+                             _ptr(k_offsets), n_k, _ptr(sel_count), _ptr(sel_idx), ctypes.c_float(scale),
+                             _ptr(out), _ptr(ls), _ptr(ws), ws_n, _stream(dev))
+    _check(s, "svg2_varblock_attn")
+    return out, ls
+
+
+# ---------------------------------------------------------------- unpermute
+def unpermute(src: torch.Tensor, perm: torch.Tensor, out: Optional[torch.Tensor] = None):
+    """Scatters rows back: out row perm[i] = src row i.  ``out`` may be a
+    strided [bh,N,d] or [B,H,N,d] view (default: new contiguous tensor)."""
+    _need_cuda(src, perm, out)
+    if src.dim() != 3 or not src.is_contiguous():
+        raise Svg2Error("src must be a contiguous [bh, N, d] tensor")
+    bh, N, d = src.shape
+    if perm.dtype != torch.int32 or not perm.is_contiguous() or tuple(perm.shape) != (bh, N):
+        raise Svg2Error("perm must be contiguous int32 [bh, N]")
+    if out is None:
+        out = torch.empty_like(src)
+    obh, oN, od, heads, sb, sh, st = _strided_view(out)
+    if (obh, oN, od) != (bh, N, d) or out.dtype != src.dtype:
+        raise Svg2Error("out does not match src")
+    s = lib().svg2_unpermute(_ptr(src), _dtype_code(src), bh, N, d, _ptr(perm), _ptr(out), heads, sb, sh, st,
+                             _stream(src.device))
+    _check(s, "svg2_unpermute")
+    return out

@@ -1,0 +1,286 @@
+// C ABI of libsvg2: argument validation (always before any HIP call),
+// workspace carving and kernel dispatch.  The operations are specified in
+// include/svg2.h.
+#include "svg2.h"
+
+#include <math.h>
+#include <string.h>
+
+#include "internal.hpp"
+
+using namespace svg2;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kMaxTokens = 1 << 24;
+constexpr int kMaxSeedTokens = 262144;     // k-means++ keeps 64-token block sums in LDS
+constexpr size_t kAlign = 256;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return SVG2_OK;
+  g_last_hip_error = (int)e;
+  return SVG2_ERR_HIP;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+bool dtype_ok(int32_t dt) { return dt == SVG2_F32 || dt == SVG2_BF16; }
+int esize(int32_t dt) { return dt == SVG2_F32 ? 4 : 2; }
+bool dim_ok(int32_t d) { return d == 64 || d == 128; }
+
+// Bump allocator over the caller's workspace; with base == nullptr it only
+// measures.
+struct Carve {
+  char* base;
+  size_t off = 0;
+  explicit Carve(void* b) : base(static_cast<char*>(b)) {}
+  template <typename T>
+  T* take(size_t count) {
+    off = (off + kAlign - 1) / kAlign * kAlign;
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+};
+
+struct KmeansWs {
+  double* d2;
+  int32_t* near;      // 2 * bh * N ints: nearest pick, then ||x||^2 as float
+  int32_t* seed_idx;
+  uint16_t* c_hi;
+  uint16_t* c_lo;
+  float* c_norm;
+  int32_t* hist;
+  int32_t* perm;
+  int32_t* offsets;
+};
+
+KmeansWs carve_kmeans(Carve& c, int bh, int N, int d, int n) {
+  KmeansWs w;
+  const size_t bN = (size_t)bh * N;
+  w.d2 = c.take<double>(bN);
+  w.near = c.take<int32_t>(2 * bN);
+  w.seed_idx = c.take<int32_t>((size_t)bh * n);
+  w.c_hi = c.take<uint16_t>((size_t)bh * n * d);
+  w.c_lo = c.take<uint16_t>((size_t)bh * n * d);
+  w.c_norm = c.take<float>((size_t)bh * n);
+  w.hist = c.take<int32_t>((size_t)bh * sort_chunks(N) * n);
+  w.perm = c.take<int32_t>(bN);
+  w.offsets = c.take<int32_t>((size_t)bh * (n + 1));
+  return w;
+}
+
+bool shape_ok(int32_t bh, int32_t N, int32_t n) {
+  return bh >= 1 && N >= 1 && N <= kMaxTokens && n >= 1 && n <= kMaxClusters && n <= N;
+}
+
+bool strides_ok(int32_t heads, int32_t bh, int64_t sb, int64_t sh, int64_t st, int es) {
+  if (heads < 1 || bh % heads != 0) return false;
+  const int64_t q = 16 / es;
+  if (sb < 0 || sh < 0 || st < 0) return false;
+  return sb % q == 0 && sh % q == 0 && st % q == 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* svg2_version(void) { return "svg2-mi355x 0.1.0 (gfx950)"; }
+
+const char* svg2_status_string(int status) {
+  switch (status) {
+    case SVG2_OK: return "ok";
+    case SVG2_ERR_INVALID_ARG: return "invalid argument";
+    case SVG2_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case SVG2_ERR_WORKSPACE: return "workspace too small";
+    case SVG2_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+int svg2_last_hip_error(void) { return g_last_hip_error; }
+
+// ------------------------------------------------------------------ kmeans
+size_t svg2_kmeans_workspace_size(int32_t bh, int32_t n_tokens, int32_t head_dim, int32_t n_clusters) {
+  if (!shape_ok(bh, n_tokens, n_clusters) || !dim_ok(head_dim)) return 0;
+  Carve c(nullptr);
+  carve_kmeans(c, bh, n_tokens, head_dim, n_clusters);
+  return c.off;
+}
+
+int svg2_kmeans(const void* x, int32_t dtype, int32_t bh, int32_t n_tokens, int32_t head_dim,
+                int32_t n_clusters, int32_t n_iters, const float* init_centroids, uint64_t seed,
+                float* centroids, int32_t* labels, int32_t* counts, float* min_dist,
+                int32_t* seed_index, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!dtype_ok(dtype)) return SVG2_ERR_INVALID_ARG;
+  if (!shape_ok(bh, n_tokens, n_clusters)) return SVG2_ERR_INVALID_ARG;
+  if (!dim_ok(head_dim)) return SVG2_ERR_UNSUPPORTED;
+  if (n_iters < 0 || n_iters > 100) return SVG2_ERR_INVALID_ARG;
+  if (!x || !aligned(x, 16) || !centroids || !aligned(centroids, 16)) return SVG2_ERR_INVALID_ARG;
+  if (init_centroids && !aligned(init_centroids, 16)) return SVG2_ERR_INVALID_ARG;
+  if (n_iters > 0 && (!labels || !counts)) return SVG2_ERR_INVALID_ARG;
+  if ((labels && !aligned(labels, 4)) || (counts && !aligned(counts, 4)) ||
+      (min_dist && !aligned(min_dist, 4)) || (seed_index && !aligned(seed_index, 4)))
+    return SVG2_ERR_INVALID_ARG;
+  if (!init_centroids && n_tokens > kMaxSeedTokens) return SVG2_ERR_UNSUPPORTED;
+  const size_t need = svg2_kmeans_workspace_size(bh, n_tokens, head_dim, n_clusters);
+  if (workspace_bytes < need || (need && !workspace)) return SVG2_ERR_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return SVG2_ERR_INVALID_ARG;
+
+  Carve c(workspace);
+  const KmeansWs w = carve_kmeans(c, bh, n_tokens, head_dim, n_clusters);
+  const bool bf16 = dtype == SVG2_BF16;
+  const int N = n_tokens, n = n_clusters, d = head_dim;
+  int st;
+  if (!init_centroids) {
+    st = hip_status(launch_kmeanspp(x, bf16, bh, N, d, n, seed, w.d2, w.near, centroids,
+                                    seed_index ? seed_index : w.seed_idx, stream));
+    if (st) return st;
+  } else if (init_centroids != centroids) {
+    st = hip_status(hipMemcpyAsync(centroids, init_centroids, (size_t)bh * n * d * sizeof(float),
+                                   hipMemcpyDeviceToDevice, stream));
+    if (st) return st;
+  }
+  for (int it = 0; it < n_iters; ++it) {
+    if (bf16) {
+      st = hip_status(launch_prep_centroids(centroids, bh, n, d, w.c_hi, w.c_lo, w.c_norm, stream));
+      if (st) return st;
+    }
+    st = hip_status(launch_assign(x, bf16, bh, N, d, n, centroids, w.c_hi, w.c_lo, w.c_norm, labels,
+                                  it == n_iters - 1 ? min_dist : nullptr, stream));
+    if (st) return st;
+    st = hip_status(launch_counting_sort(labels, bh, N, n, w.hist, w.perm, w.offsets, counts, stream));
+    if (st) return st;
+    st = hip_status(launch_centroid_mean(x, bf16, bh, N, d, n, w.perm, w.offsets, centroids, stream));
+    if (st) return st;
+  }
+  return SVG2_OK;
+}
+
+// ------------------------------------------------------------------ permute
+size_t svg2_permute_workspace_size(int32_t bh, int32_t n_tokens, int32_t n_clusters) {
+  if (!shape_ok(bh, n_tokens, n_clusters)) return 0;
+  Carve c(nullptr);
+  c.take<int32_t>((size_t)bh * sort_chunks(n_tokens) * n_clusters);
+  return c.off;
+}
+
+int svg2_permute(const int32_t* labels, int32_t bh, int32_t n_tokens, int32_t n_clusters,
+                 int32_t n_tensors, const void* const* src, int32_t heads, int64_t src_b_stride,
+                 int64_t src_h_stride, int64_t src_token_stride, void* const* dst, int32_t dtype,
+                 int32_t head_dim, int32_t* perm, int32_t* offsets, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream) {
+  if (!dtype_ok(dtype)) return SVG2_ERR_INVALID_ARG;
+  if (!shape_ok(bh, n_tokens, n_clusters)) return SVG2_ERR_INVALID_ARG;
+  if (!dim_ok(head_dim)) return SVG2_ERR_UNSUPPORTED;
+  if (n_tensors < 1 || n_tensors > 2 || !src || !dst) return SVG2_ERR_INVALID_ARG;
+  if (!labels || !aligned(labels, 4) || !perm || !aligned(perm, 4) || !offsets || !aligned(offsets, 4))
+    return SVG2_ERR_INVALID_ARG;
+  for (int t = 0; t < n_tensors; ++t)
+    if (!src[t] || !dst[t] || !aligned(src[t], 16) || !aligned(dst[t], 16)) return SVG2_ERR_INVALID_ARG;
+  if (!strides_ok(heads, bh, src_b_stride, src_h_stride, src_token_stride, esize(dtype)))
+    return SVG2_ERR_INVALID_ARG;
+  const size_t need = svg2_permute_workspace_size(bh, n_tokens, n_clusters);
+  if (workspace_bytes < need || !workspace) return SVG2_ERR_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return SVG2_ERR_INVALID_ARG;
+
+  Carve c(workspace);
+  int32_t* hist = c.take<int32_t>((size_t)bh * sort_chunks(n_tokens) * n_clusters);
+  int st = hip_status(launch_counting_sort(labels, bh, n_tokens, n_clusters, hist, perm, offsets,
+                                           nullptr, stream));
+  if (st) return st;
+  return hip_status(launch_gather_rows(n_tensors, src, dst, esize(dtype), head_dim, bh, n_tokens, heads,
+                                       src_b_stride, src_h_stride, src_token_stride, perm, stream));
+}
+
+// ------------------------------------------------------------------ select
+size_t svg2_select_topp_workspace_size(int32_t bh, int32_t n_q, int32_t n_k) {
+  if (bh < 1 || n_q < 1 || n_q > kMaxClusters || n_k < 1 || n_k > kMaxClusters) return 0;
+  Carve c(nullptr);
+  c.take<int64_t>((size_t)bh * n_q);
+  return c.off;
+}
+
+int svg2_select_topp(const float* q_centroids, const int32_t* q_counts, int32_t n_q,
+                     const float* k_centroids, const int32_t* k_counts, int32_t n_k, int32_t bh,
+                     int32_t head_dim, float scale, float top_p, int32_t* sel_count, int32_t* sel_idx,
+                     float* probs, int64_t* pair_count, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+  if (bh < 1 || n_q < 1 || n_q > kMaxClusters || n_k < 1 || n_k > kMaxClusters) return SVG2_ERR_INVALID_ARG;
+  if (!dim_ok(head_dim)) return SVG2_ERR_UNSUPPORTED;
+  if (!(isfinite(scale) && scale > 0.f)) return SVG2_ERR_INVALID_ARG;
+  if (!(isfinite(top_p) && top_p > 0.f && top_p <= 1.f)) return SVG2_ERR_INVALID_ARG;
+  if (!q_centroids || !k_centroids || !q_counts || !k_counts || !sel_count || !sel_idx)
+    return SVG2_ERR_INVALID_ARG;
+  if (!aligned(q_centroids, 16) || !aligned(k_centroids, 16) || !aligned(q_counts, 4) ||
+      !aligned(k_counts, 4) || !aligned(sel_count, 4) || !aligned(sel_idx, 4) ||
+      (probs && !aligned(probs, 4)) || (pair_count && !aligned(pair_count, 8)))
+    return SVG2_ERR_INVALID_ARG;
+  const size_t need = svg2_select_topp_workspace_size(bh, n_q, n_k);
+  if (workspace_bytes < need || !workspace) return SVG2_ERR_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return SVG2_ERR_INVALID_ARG;
+  Carve c(workspace);
+  int64_t* row_pairs = c.take<int64_t>((size_t)bh * n_q);
+  return hip_status(launch_select_topp(q_centroids, q_counts, n_q, k_centroids, k_counts, n_k, bh, head_dim,
+                                       (double)scale, (double)top_p, sel_count, sel_idx, probs, row_pairs,
+                                       pair_count, stream));
+}
+
+// ------------------------------------------------------------------ attention
+size_t svg2_varblock_attn_workspace_size(int32_t bh, int32_t n_tokens, int32_t n_q, int32_t n_k,
+                                         int32_t head_dim) {
+  if (bh < 1 || n_tokens < 1 || n_tokens > kMaxTokens || n_q < 1 || n_q > kMaxClusters || n_k < 1 ||
+      n_k > kMaxClusters || !dim_ok(head_dim))
+    return 0;
+  // the fp32 kernel uses the smaller row block, hence the larger item list
+  const int bm = attn_block_rows(false) < attn_block_rows(true) ? attn_block_rows(false) : attn_block_rows(true);
+  Carve c(nullptr);
+  c.take<int32_t>((size_t)bh);
+  c.take<int32_t>((size_t)bh * attn_max_items(n_tokens, n_q, bm));
+  return c.off;
+}
+
+int svg2_varblock_attn(const void* q, const void* k, const void* v, int32_t dtype, int32_t bh,
+                       int32_t n_tokens, int32_t head_dim, const int32_t* q_offsets, int32_t n_q,
+                       const int32_t* k_offsets, int32_t n_k, const int32_t* sel_count,
+                       const int32_t* sel_idx, float scale, void* out, float* lse, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  if (!dtype_ok(dtype)) return SVG2_ERR_INVALID_ARG;
+  if (bh < 1 || n_tokens < 1 || n_tokens > kMaxTokens) return SVG2_ERR_INVALID_ARG;
+  if (n_q < 1 || n_q > kMaxClusters || n_k < 1 || n_k > kMaxClusters) return SVG2_ERR_INVALID_ARG;
+  if (!dim_ok(head_dim)) return SVG2_ERR_UNSUPPORTED;
+  if (!(isfinite(scale) && scale > 0.f)) return SVG2_ERR_INVALID_ARG;
+  if (!q || !k || !v || !out || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return SVG2_ERR_INVALID_ARG;
+  if (!q_offsets || !k_offsets || !sel_count || !sel_idx || !aligned(q_offsets, 4) ||
+      !aligned(k_offsets, 4) || !aligned(sel_count, 4) || !aligned(sel_idx, 4) || (lse && !aligned(lse, 4)))
+    return SVG2_ERR_INVALID_ARG;
+  const size_t need = svg2_varblock_attn_workspace_size(bh, n_tokens, n_q, n_k, head_dim);
+  if (workspace_bytes < need || !workspace) return SVG2_ERR_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return SVG2_ERR_INVALID_ARG;
+  Carve c(workspace);
+  int32_t* item_count = c.take<int32_t>((size_t)bh);
+  const bool bf16 = dtype == SVG2_BF16;
+  int32_t* items = c.take<int32_t>((size_t)bh * attn_max_items(n_tokens, n_q, attn_block_rows(bf16)));
+  return hip_status(launch_varblock_attn(q, k, v, bf16, bh, n_tokens, head_dim, q_offsets, n_q, k_offsets,
+                                         n_k, sel_count, sel_idx, scale, out, lse, item_count, items,
+                                         stream));
+}
+
+// ------------------------------------------------------------------ unpermute
+int svg2_unpermute(const void* src, int32_t dtype, int32_t bh, int32_t n_tokens, int32_t head_dim,
+                   const int32_t* perm, void* dst, int32_t heads, int64_t dst_b_stride,
+                   int64_t dst_h_stride, int64_t dst_token_stride, hipStream_t stream) {
+  if (!dtype_ok(dtype)) return SVG2_ERR_INVALID_ARG;
+  if (bh < 1 || n_tokens < 1 || n_tokens > kMaxTokens) return SVG2_ERR_INVALID_ARG;
+  if (!dim_ok(head_dim)) return SVG2_ERR_UNSUPPORTED;
+  if (!src || !dst || !perm || !aligned(src, 16) || !aligned(dst, 16) || !aligned(perm, 4))
+    return SVG2_ERR_INVALID_ARG;
+  if (!strides_ok(heads, bh, dst_b_stride, dst_h_stride, dst_token_stride, esize(dtype)))
+    return SVG2_ERR_INVALID_ARG;
+  return hip_status(launch_scatter_rows(src, dst, esize(dtype), head_dim, bh, n_tokens, heads, dst_b_stride,
+                                        dst_h_stride, dst_token_stride, perm, stream));
+}
+
+}  // extern "C"

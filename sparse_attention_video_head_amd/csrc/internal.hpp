@@ -1,0 +1,60 @@
+// Host-side launchers of the SVG2 kernels (internal to libsvg2).
+#pragma once
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace svg2 {
+
+constexpr int kMaxClusters = 4096;
+constexpr int kSortChunk = 2048;             // tokens per counting-sort chunk
+inline int sort_chunks(int n_tokens) { return (n_tokens + kSortChunk - 1) / kSortChunk; }
+
+// ----------------------------------------------------------------- sort.hip
+// Stable counting sort of labels [bh, N] in [0, n): perm, offsets [bh, n+1],
+// counts [bh, n] (counts may be null).  hist_ws holds bh * sort_chunks(N) * n ints.
+hipError_t launch_counting_sort(const int32_t* labels, int bh, int N, int n, int32_t* hist_ws,
+                                int32_t* perm, int32_t* offsets, int32_t* counts, hipStream_t s);
+// dst[t][p][i][:] = src[t] row perm[p][i] of problem p (strided source), t < n_tensors <= 2.
+hipError_t launch_gather_rows(int n_tensors, const void* const* src, void* const* dst, int esize,
+                              int d, int bh, int N, int heads, int64_t sb, int64_t sh, int64_t st,
+                              const int32_t* perm, hipStream_t s);
+// dst row perm[p][i] of problem p (strided) = src[p][i] (contiguous).
+hipError_t launch_scatter_rows(const void* src, void* dst, int esize, int d, int bh, int N,
+                               int heads, int64_t sb, int64_t sh, int64_t st, const int32_t* perm,
+                               hipStream_t s);
+
+// --------------------------------------------------------------- kmeans.hip
+// k-means++ seeding, one work-group per problem.  state_ws: bh*N doubles (D2)
+// followed by bh*N ints (nearest pick).  Writes centroids [bh,n,d] fp32 and
+// seed_index [bh,n].
+hipError_t launch_kmeanspp(const void* x, bool bf16, int bh, int N, int d, int n, uint64_t seed,
+                           double* d2_ws, int32_t* near_ws, float* centroids, int32_t* seed_index,
+                           hipStream_t s);
+// centroid split for the matrix-core assignment: c_hi + c_lo (bf16 pair) and ||c||^2
+hipError_t launch_prep_centroids(const float* c, int bh, int n, int d, uint16_t* c_hi,
+                                 uint16_t* c_lo, float* c_norm, hipStream_t s);
+hipError_t launch_assign(const void* x, bool bf16, int bh, int N, int d, int n, const float* c,
+                         const uint16_t* c_hi, const uint16_t* c_lo, const float* c_norm,
+                         int32_t* labels, float* min_dist, hipStream_t s);
+// centroid c = mean of the rows perm[offsets[c] .. offsets[c+1]); empty keeps c.
+hipError_t launch_centroid_mean(const void* x, bool bf16, int bh, int N, int d, int n,
+                                const int32_t* perm, const int32_t* offsets, float* c,
+                                hipStream_t s);
+
+// --------------------------------------------------------------- select.hip
+hipError_t launch_select_topp(const float* cq, const int32_t* q_counts, int n_q, const float* ck,
+                              const int32_t* k_counts, int n_k, int bh, int d, double scale,
+                              double top_p, int32_t* sel_count, int32_t* sel_idx, float* probs,
+                              int64_t* row_pairs_ws, int64_t* pair_count, hipStream_t s);
+
+// ----------------------------------------------------------------- attn.hip
+int attn_block_rows(bool bf16);
+inline int attn_max_items(int N, int n_q, int bm) { return (N + bm - 1) / bm + n_q; }
+hipError_t launch_varblock_attn(const void* q, const void* k, const void* v, bool bf16, int bh,
+                                int N, int d, const int32_t* q_off, int n_q, const int32_t* k_off,
+                                int n_k, const int32_t* sel_count, const int32_t* sel_idx,
+                                float scale, void* out, float* lse, int32_t* item_count_ws,
+                                int32_t* items_ws, hipStream_t s);
+
+}  // namespace svg2

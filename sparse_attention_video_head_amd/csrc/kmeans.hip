@@ -1,0 +1,550 @@
+// k-means over the Q tokens or the K tokens of every head ("Sparse VideoGen2"
+// wiki summary, Method, stage (1); Key claims, §4.3 / Fig. 7(a)):
+//   * k-means++ seeding (Arthur & Vassilvitskii 2007) when no cached
+//     centroids are given,
+//   * Lloyd rounds: assignment to the nearest centroid, then centroid = mean of
+//     its members (the counting sort of sort.hip groups the members).
+#include <limits.h>
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace svg2 {
+
+// ======================================================================
+// k-means++ seeding
+// ======================================================================
+// Counter-based uniforms: splitmix64 (Steele, Lea & Flood, OOPSLA 2014), one
+// output of the state seed ^ (problem * 2^32 + pick), top 53 bits * 2^-53.
+__device__ __forceinline__ uint64_t splitmix64_dev(uint64_t state) {
+  uint64_t z = state + 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+__device__ __forceinline__ double seed_uniform(uint64_t seed, int problem, int pick) {
+  const uint64_t x = seed ^ (((uint64_t)(uint32_t)problem << 32) + (uint64_t)(uint32_t)pick);
+  return (double)(splitmix64_dev(x) >> 11) * 0x1.0p-53;
+}
+
+constexpr int kSeedThreads = 1024;
+constexpr int kSeedWaves = kSeedThreads / kWave;
+constexpr int kSeedMaxBlocks = 4096;     // 64-token blocks -> n_tokens <= 262144
+
+// ||x - c||^2 as the fp64 sum of fp64 squared differences: the differences of
+// bf16 or fp32 values are exact in fp64, and so are the squares of bf16
+// differences, so the result equals the plain fp64 definition up to the
+// order of the additions.  `c` holds the centre in fp64.
+template <typename T, int D> struct ExactDist;
+template <int D> struct ExactDist<uint16_t, D> {
+  static __device__ __forceinline__ double run(const uint16_t* x, const double* c) {
+    const u32x4_t* xv = reinterpret_cast<const u32x4_t*>(x);
+    double acc = 0.0;
+#pragma unroll 4
+    for (int q = 0; q < D / 8; ++q) {
+      const u32x4_t v = xv[q];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const double d0 = (double)bf16_lo(v[e]) - c[8 * q + 2 * e];
+        const double d1 = (double)bf16_hi(v[e]) - c[8 * q + 2 * e + 1];
+        acc = fma(d0, d0, acc);
+        acc = fma(d1, d1, acc);
+      }
+    }
+    return acc;
+  }
+};
+template <int D> struct ExactDist<float, D> {
+  static __device__ __forceinline__ double run(const float* x, const double* c) {
+    double acc = 0.0;
+#pragma unroll 8
+    for (int e = 0; e < D; ++e) {
+      const double df = (double)x[e] - c[e];
+      acc = fma(df, df, acc);
+    }
+    return acc;
+  }
+};
+
+// fp32 x.c for bf16 rows: every product of two bf16 values is exact in fp32
+// and each of the D fused additions errs by at most 2^-24 of the running sum,
+// so |error| <= D * 2^-24 * sum|x_i c_i| <= D * 2^-25 (||x||^2 + ||c||^2).
+// Used only to skip exact evaluations that cannot lower D^2.
+template <int D>
+__device__ __forceinline__ float dot_bf16_f32(const uint16_t* x, const float* c) {
+  const u32x4_t* xv = reinterpret_cast<const u32x4_t*>(x);
+  float acc = 0.f;
+#pragma unroll
+  for (int q = 0; q < D / 8; ++q) {
+    const u32x4_t v = xv[q];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = fmaf(bf16_lo(v[e]), c[8 * q + 2 * e], acc);
+      acc = fmaf(bf16_hi(v[e]), c[8 * q + 2 * e + 1], acc);
+    }
+  }
+  return acc;
+}
+
+// One work-group per problem runs all n picks.  Per token it keeps D2 (exact
+// fp64 squared distance to the nearest pick), the nearest pick's number and
+// ||x||^2 (fp32).  A new pick c can lower D2(x) only if
+// ||c - c_near||^2 < 4 D2(x) (triangle inequality, Elkan 2003), so other
+// tokens are skipped without reading x; the skip leaves D2 bit-identical to
+// evaluating every token.
+template <typename T, int D>
+__global__ __launch_bounds__(kSeedThreads) void k_kmeanspp(
+    const T* __restrict__ X, int N, int n, uint64_t seed, double* __restrict__ D2g,
+    int32_t* __restrict__ Ag, float* __restrict__ XNg, float* __restrict__ C0,
+    int32_t* __restrict__ seed_index) {
+  __shared__ double s_bsum[kSeedMaxBlocks];
+  __shared__ double s_cc[kMaxClusters];
+  __shared__ int32_t s_idx[kMaxClusters];
+  __shared__ float s_c[D];
+  __shared__ double s_cd[D];
+  __shared__ double s_red[17];
+  __shared__ int s_pick, s_blk, s_last;
+  __shared__ double s_resid;
+  __shared__ float s_cn;
+
+  constexpr bool kBF16 = sizeof(T) == 2;
+  const int p = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const T* Xp = X + (size_t)p * N * D;
+  double* D2 = D2g + (size_t)p * N;
+  int32_t* A = Ag + (size_t)p * N;
+  float* XN = XNg + (size_t)p * N;
+  const int nblk = (N + kWave - 1) / kWave;
+
+  if (tid == 0) s_pick = min((int)(seed_uniform(seed, p, 0) * (double)N), N - 1);
+  __syncthreads();
+
+  for (int k = 0; k < n; ++k) {
+    const int t = s_pick;
+    for (int e = tid; e < D; e += kSeedThreads) {
+      const float v = Elem<T>::get(Xp, (size_t)t * D + e);
+      s_c[e] = v;
+      s_cd[e] = (double)v;
+      C0[((size_t)p * n + k) * D + e] = v;
+    }
+    if (tid == 0) {
+      s_idx[k] = t;
+      if (seed_index) seed_index[(size_t)p * n + k] = t;
+    }
+    if (k == n - 1) break;
+    __syncthreads();
+
+    if (wave == 0) {
+      float a = 0.f;
+      for (int e = lane; e < D; e += kWave) a += s_c[e] * s_c[e];
+      a = wave_sum(a);
+      if (lane == 0) s_cn = a;
+    }
+    for (int a = tid; a < k; a += kSeedThreads)
+      s_cc[a] = ExactDist<T, D>::run(Xp + (size_t)s_idx[a] * D, s_cd);
+    __syncthreads();
+    const float cn = s_cn;
+
+    // ---- lower D2 with the new pick; 64-token block sums for sampling
+    for (int b = wave; b < nblk; b += kSeedWaves) {
+      const int tok = b * kWave + lane;
+      double d2 = 0.0;
+      if (tok < N) {
+        const T* xr = Xp + (size_t)tok * D;
+        if (k == 0) {
+          d2 = ExactDist<T, D>::run(xr, s_cd);
+          D2[tok] = d2;
+          A[tok] = 0;
+          if (kBF16) {
+            float xn = 0.f;
+            const uint32_t* xw = reinterpret_cast<const uint32_t*>(xr);
+            for (int w = 0; w < D / 2; ++w) {
+              const float a0 = bf16_lo(xw[w]), a1 = bf16_hi(xw[w]);
+              xn = fmaf(a0, a0, fmaf(a1, a1, xn));
+            }
+            XN[tok] = xn;
+          }
+        } else {
+          d2 = D2[tok];
+          const int a = A[tok];
+          if (!(s_cc[a] >= 4.0 * d2 * (1.0 + 0x1p-20))) {
+            bool need = true;
+            if (kBF16) {
+              const float xn = XN[tok];
+              // |approx - ||x - c||^2| <= D 2^-24 (xn + cn) plus the rounding
+              // of xn, cn and the two additions: below 2e-5 (xn + cn) at D = 128
+              const float approx =
+                  xn + cn - 2.f * dot_bf16_f32<D>(reinterpret_cast<const uint16_t*>(xr), s_c);
+              need = approx <= (float)d2 + 5e-5f * (xn + cn) + 1e-30f;
+            }
+            if (need) {
+              const double nd = ExactDist<T, D>::run(xr, s_cd);
+              if (nd < d2) {
+                d2 = nd;
+                D2[tok] = nd;
+                A[tok] = k;
+              }
+            }
+          }
+        }
+      }
+      const double inc = wave_inclusive_scan(d2);
+      if (lane == kWave - 1) s_bsum[b] = inc;
+    }
+    if (tid == 0) {
+      s_blk = INT_MAX;
+      s_last = -1;
+    }
+    __syncthreads();
+
+    // ---- sample pick k+1: smallest token whose running D2 sum exceeds u*total
+    const int per = (nblk + kSeedThreads - 1) / kSeedThreads;
+    const int b0 = min(tid * per, nblk), b1 = min(b0 + per, nblk);
+    double loc = 0.0;
+    for (int b = b0; b < b1; ++b) loc += s_bsum[b];
+    double total;
+    const double excl = block_exclusive_scan(loc, s_red, &total);
+    const double u = seed_uniform(seed, p, k + 1);
+    const double target = u * total;
+    int found = INT_MAX;
+    double resid = 0.0;
+    if (total > 0.0) {
+      double run = excl;
+      for (int b = b0; b < b1; ++b) {
+        const double nxt = run + s_bsum[b];
+        if (found == INT_MAX && run <= target && target < nxt) {
+          found = b;
+          resid = target - run;
+        }
+        run = nxt;
+      }
+      if (found != INT_MAX) atomicMin(&s_blk, found);
+      // last block with mass (fallback when rounding leaves no block above target)
+      for (int b = b1 - 1; b >= b0; --b)
+        if (s_bsum[b] > 0.0) {
+          atomicMax(&s_last, b);
+          break;
+        }
+    }
+    __syncthreads();
+    if (found != INT_MAX && found == s_blk) s_resid = resid;
+    __syncthreads();
+    if (wave == 0) {
+      int pick;
+      if (!(total > 0.0)) {
+        pick = min((int)(u * (double)N), N - 1);
+      } else {
+        int b = s_blk;
+        bool exact = true;
+        if (b == INT_MAX) {
+          b = s_last;
+          exact = false;
+        }
+        b = clampi(b, 0, nblk - 1);
+        const int tok = b * kWave + lane;
+        const double v = tok < N ? D2[tok] : 0.0;
+        const double inc = wave_inclusive_scan(v);
+        const uint64_t above = exact ? __ballot(inc > s_resid) : 0ull;
+        if (above) {
+          pick = b * kWave + __ffsll((unsigned long long)above) - 1;
+        } else {
+          const uint64_t pos = __ballot(v > 0.0);
+          pick = b * kWave + (63 - __clzll((long long)pos));
+        }
+      }
+      if (lane == 0) s_pick = clampi(pick, 0, N - 1);
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_kmeanspp(const void* x, bool bf16, int bh, int N, int d, int n, uint64_t seed,
+                           double* d2_ws, int32_t* near_ws, float* centroids, int32_t* seed_index,
+                           hipStream_t s) {
+  float* xn_ws = reinterpret_cast<float*>(near_ws + (size_t)bh * N);
+#define SVG2_SEED(T, D)                                                                         \
+  hipLaunchKernelGGL((k_kmeanspp<T, D>), dim3(bh), dim3(kSeedThreads), 0, s,                  \
+                     static_cast<const T*>(x), N, n, seed, d2_ws, near_ws, xn_ws, centroids, \
+                     seed_index)
+  if (bf16) {
+    if (d == 128) SVG2_SEED(uint16_t, 128); else SVG2_SEED(uint16_t, 64);
+  } else {
+    if (d == 128) SVG2_SEED(float, 128); else SVG2_SEED(float, 64);
+  }
+#undef SVG2_SEED
+  return hipGetLastError();
+}
+
+// ======================================================================
+// Lloyd assignment
+// ======================================================================
+// c = c_hi + c_lo with both halves bf16 (|c - c_hi - c_lo| <= 2^-18 |c|), and
+// ||c||^2 in fp32, for the bf16 matrix-core distance contraction.
+__global__ __launch_bounds__(256) void k_prep_centroids(const float* __restrict__ c, int rows, int d,
+                                                        uint16_t* __restrict__ hi,
+                                                        uint16_t* __restrict__ lo,
+                                                        float* __restrict__ cn) {
+  const int row = blockIdx.x * 4 + threadIdx.x / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
+  if (row >= rows) return;
+  float acc = 0.f;
+  for (int e = lane; e < d; e += kWave) {
+    const float v = c[(size_t)row * d + e];
+    const uint16_t h = f32_to_bf16(v);
+    const uint16_t l = f32_to_bf16(v - bf16_to_f32(h));
+    hi[(size_t)row * d + e] = h;
+    lo[(size_t)row * d + e] = l;
+    acc = fmaf(v, v, acc);
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) cn[row] = acc;
+}
+
+hipError_t launch_prep_centroids(const float* c, int bh, int n, int d, uint16_t* c_hi,
+                                 uint16_t* c_lo, float* c_norm, hipStream_t s) {
+  const int rows = bh * n;
+  hipLaunchKernelGGL(k_prep_centroids, dim3((rows + 3) / 4), dim3(256), 0, s, c, rows, d, c_hi, c_lo,
+                     c_norm);
+  return hipGetLastError();
+}
+
+// bf16 inputs: argmin_c ||c||^2 - 2 x.c on matrix cores.  The MFMA computes
+// S^T = C x X^T (centroids as rows, tokens as columns) so that each lane holds
+// 16 centroid distances of ONE token and the argmin is mostly in-lane.
+// A work-group holds 512 tokens (4 waves x 4 blocks of 32) in registers and
+// streams the centroids through LDS in chunks of 64.
+constexpr int kAsgTB = 4;        // 32-token blocks per wave
+constexpr int kAsgCB = 64;       // centroids per LDS chunk
+
+template <int D>
+__global__ __launch_bounds__(256) void k_assign_bf16(const uint16_t* __restrict__ X, int N, int n,
+                                                     const uint16_t* __restrict__ Chi,
+                                                     const uint16_t* __restrict__ Clo,
+                                                     const float* __restrict__ Cn,
+                                                     int32_t* __restrict__ labels,
+                                                     float* __restrict__ min_dist) {
+  constexpr int KS = D / 16;
+  constexpr int LDR = D + 8;                  // padded LDS row, elements
+  __shared__ __attribute__((aligned(16))) uint16_t sh_hi[kAsgCB * LDR];
+  __shared__ __attribute__((aligned(16))) uint16_t sh_lo[kAsgCB * LDR];
+  __shared__ float sh_cn[kAsgCB];
+
+  const int p = blockIdx.y;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int col = lane & 31, half = lane >> 5;
+  const int tok0 = blockIdx.x * (4 * kAsgTB * 32) + wave * (kAsgTB * 32);
+  const uint16_t* Xp = X + (size_t)p * N * D;
+
+  bf16x8_t xb[kAsgTB][KS];
+  float xn[kAsgTB];
+#pragma unroll
+  for (int tb = 0; tb < kAsgTB; ++tb) {
+    const int t = tok0 + tb * 32 + col;
+    float acc = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (t < N) v = *reinterpret_cast<const u32x4_t*>(Xp + (size_t)t * D + ks * 16 + half * 8);
+      xb[tb][ks] = __builtin_bit_cast(bf16x8_t, v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a0 = bf16_lo(v[e]), a1 = bf16_hi(v[e]);
+        acc = fmaf(a0, a0, fmaf(a1, a1, acc));
+      }
+    }
+    xn[tb] = acc + __shfl_xor(acc, 32);
+  }
+
+  float best[kAsgTB];
+  int bidx[kAsgTB];
+#pragma unroll
+  for (int tb = 0; tb < kAsgTB; ++tb) {
+    best[tb] = __builtin_inff();
+    bidx[tb] = 0;
+  }
+
+  const uint16_t* Hp = Chi + (size_t)p * n * D;
+  const uint16_t* Lp = Clo + (size_t)p * n * D;
+  for (int c0 = 0; c0 < n; c0 += kAsgCB) {
+    __syncthreads();
+    for (int v = threadIdx.x; v < kAsgCB * D / 8; v += 256) {
+      const int r = v / (D / 8), cv = v % (D / 8);
+      u32x4_t h = {0u, 0u, 0u, 0u}, l = {0u, 0u, 0u, 0u};
+      if (c0 + r < n) {
+        h = *reinterpret_cast<const u32x4_t*>(Hp + (size_t)(c0 + r) * D + cv * 8);
+        l = *reinterpret_cast<const u32x4_t*>(Lp + (size_t)(c0 + r) * D + cv * 8);
+      }
+      *reinterpret_cast<u32x4_t*>(&sh_hi[r * LDR + cv * 8]) = h;
+      *reinterpret_cast<u32x4_t*>(&sh_lo[r * LDR + cv * 8]) = l;
+    }
+    for (int r = threadIdx.x; r < kAsgCB; r += 256)
+      sh_cn[r] = (c0 + r < n) ? Cn[(size_t)p * n + c0 + r] : __builtin_inff();
+    __syncthreads();
+#pragma unroll
+    for (int mb = 0; mb < kAsgCB / 32; ++mb) {
+      f32x16_t acc[kAsgTB];
+#pragma unroll
+      for (int tb = 0; tb < kAsgTB; ++tb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[tb][i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int off = (mb * 32 + col) * LDR + ks * 16 + half * 8;
+        const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&sh_hi[off]);
+        const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&sh_lo[off]);
+#pragma unroll
+        for (int tb = 0; tb < kAsgTB; ++tb) {
+          acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xb[tb][ks], acc[tb], 0, 0, 0);
+          acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xb[tb][ks], acc[tb], 0, 0, 0);
+        }
+      }
+      // lane (col, half) holds centroid rows (i/4)*8 + half*4 + i%4 of this block
+#pragma unroll
+      for (int tb = 0; tb < kAsgTB; ++tb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = mb * 32 + (i / 4) * 8 + half * 4 + (i % 4);
+          const float dist = sh_cn[r] - 2.f * acc[tb][i];
+          if (dist < best[tb]) {
+            best[tb] = dist;
+            bidx[tb] = c0 + r;
+          }
+        }
+    }
+  }
+
+#pragma unroll
+  for (int tb = 0; tb < kAsgTB; ++tb) {
+    const float ob = __shfl_xor(best[tb], 32);
+    const int oi = __shfl_xor(bidx[tb], 32);
+    if (ob < best[tb] || (ob == best[tb] && oi < bidx[tb])) {
+      best[tb] = ob;
+      bidx[tb] = oi;
+    }
+    const int t = tok0 + tb * 32 + col;
+    if (half == 0 && t < N) {
+      labels[(size_t)p * N + t] = bidx[tb];
+      if (min_dist) min_dist[(size_t)p * N + t] = fmaxf(xn[tb] + best[tb], 0.f);
+    }
+  }
+}
+
+// fp32 inputs: exact-difference distances in fp64 on the vector ALUs.
+template <int D>
+__global__ __launch_bounds__(256) void k_assign_f32(const float* __restrict__ X, int N, int n,
+                                                    const float* __restrict__ C,
+                                                    int32_t* __restrict__ labels,
+                                                    float* __restrict__ min_dist) {
+  constexpr int CB = 32;
+  __shared__ float sh_c[CB * D];
+  const int p = blockIdx.y;
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const float* xr = X + ((size_t)p * N + min(t, N - 1)) * D;
+  float x[D];
+#pragma unroll
+  for (int e = 0; e < D; ++e) x[e] = xr[e];
+  double best = __builtin_inf();
+  int bidx = 0;
+  const float* Cp = C + (size_t)p * n * D;
+  for (int c0 = 0; c0 < n; c0 += CB) {
+    __syncthreads();
+    for (int v = threadIdx.x; v < CB * D; v += 256) sh_c[v] = (c0 + v / D < n) ? Cp[(size_t)c0 * D + v] : 0.f;
+    __syncthreads();
+    const int cend = min(CB, n - c0);
+    for (int r = 0; r < cend; ++r) {
+      double acc = 0.0;
+#pragma unroll
+      for (int e = 0; e < D; ++e) {
+        const double df = (double)x[e] - (double)sh_c[r * D + e];
+        acc += df * df;
+      }
+      if (acc < best) {
+        best = acc;
+        bidx = c0 + r;
+      }
+    }
+  }
+  if (t < N) {
+    labels[(size_t)p * N + t] = bidx;
+    if (min_dist) min_dist[(size_t)p * N + t] = (float)best;
+  }
+}
+
+hipError_t launch_assign(const void* x, bool bf16, int bh, int N, int d, int n, const float* c,
+                         const uint16_t* c_hi, const uint16_t* c_lo, const float* c_norm,
+                         int32_t* labels, float* min_dist, hipStream_t s) {
+  if (bf16) {
+    const dim3 grid((N + 4 * kAsgTB * 32 - 1) / (4 * kAsgTB * 32), bh);
+    if (d == 128)
+      hipLaunchKernelGGL(k_assign_bf16<128>, grid, dim3(256), 0, s, static_cast<const uint16_t*>(x), N, n,
+                         c_hi, c_lo, c_norm, labels, min_dist);
+    else
+      hipLaunchKernelGGL(k_assign_bf16<64>, grid, dim3(256), 0, s, static_cast<const uint16_t*>(x), N, n,
+                         c_hi, c_lo, c_norm, labels, min_dist);
+  } else {
+    const dim3 grid((N + 255) / 256, bh);
+    if (d == 128)
+      hipLaunchKernelGGL(k_assign_f32<128>, grid, dim3(256), 0, s, static_cast<const float*>(x), N, n, c,
+                         labels, min_dist);
+    else
+      hipLaunchKernelGGL(k_assign_f32<64>, grid, dim3(256), 0, s, static_cast<const float*>(x), N, n, c,
+                         labels, min_dist);
+  }
+  return hipGetLastError();
+}
+
+// ======================================================================
+// Lloyd update: centroid = mean of members (segmented over the sorted order)
+// ======================================================================
+// One work-group per (cluster, problem).  Thread (row lane rl, column pair cp)
+// sums rows offsets[c] + rl, + RL, ... of two columns in fp64; the RL partial
+// sums are combined in a fixed order, so the result is deterministic.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_centroid_mean(const T* __restrict__ X, int N, int n,
+                                                       const int32_t* __restrict__ perm,
+                                                       const int32_t* __restrict__ offsets,
+                                                       float* __restrict__ C) {
+  constexpr int CP = D / 2;
+  constexpr int RL = 256 / CP;
+  __shared__ double red[RL][D];
+  const int c = blockIdx.x, p = blockIdx.y;
+  const int a = offsets[(size_t)p * (n + 1) + c];
+  const int b = offsets[(size_t)p * (n + 1) + c + 1];
+  if (b <= a) return;                        // empty cluster keeps its centroid
+  const int cp = threadIdx.x % CP, rl = threadIdx.x / CP;
+  const T* Xp = X + (size_t)p * N * D;
+  const int32_t* pp = perm + (size_t)p * N;
+  double s0 = 0.0, s1 = 0.0;
+  for (int i = a + rl; i < b; i += RL) {
+    const int t = pp[i];
+    s0 += (double)Elem<T>::get(Xp, (size_t)t * D + 2 * cp);
+    s1 += (double)Elem<T>::get(Xp, (size_t)t * D + 2 * cp + 1);
+  }
+  red[rl][2 * cp] = s0;
+  red[rl][2 * cp + 1] = s1;
+  __syncthreads();
+  if (threadIdx.x < D) {
+    double s = 0.0;
+#pragma unroll
+    for (int r = 0; r < RL; ++r) s += red[r][threadIdx.x];
+    C[((size_t)p * n + c) * D + threadIdx.x] = (float)(s / (double)(b - a));
+  }
+}
+
+hipError_t launch_centroid_mean(const void* x, bool bf16, int bh, int N, int d, int n,
+                                const int32_t* perm, const int32_t* offsets, float* c,
+                                hipStream_t s) {
+  const dim3 grid(n, bh);
+#define SVG2_MEAN(T, D)                                                                           \
+  hipLaunchKernelGGL((k_centroid_mean<T, D>), grid, dim3(256), 0, s, static_cast<const T*>(x), N, n, \
+                     perm, offsets, c)
+  if (bf16) {
+    if (d == 128) SVG2_MEAN(uint16_t, 128); else SVG2_MEAN(uint16_t, 64);
+  } else {
+    if (d == 128) SVG2_MEAN(float, 128); else SVG2_MEAN(float, 64);
+  }
+#undef SVG2_MEAN
+  return hipGetLastError();
+}
+
+}  // namespace svg2

@@ -1,0 +1,116 @@
+"""One SVG2 sparse-attention layer on the GPU: the five library calls chained
+("Sparse VideoGen2" wiki summary, Method, stages (1)-(4)):
+
+    k-means(Q), k-means(K)  ->  permute Q by P_Q, K and V by P_K
+    ->  centroid scores + top-p  ->  variable-block attention  ->  un-permute
+
+Buffers (outputs and workspaces) are allocated once per shape, so repeated
+calls launch kernels only.  The Q-side and K-side k-means may run on two
+streams.  The centroid cache of the method is the ``centroids_q`` /
+``centroids_k`` state: ``run(..., warm=True)`` warm-starts from it.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import torch
+
+from . import binding as B
+
+
+class SVG2Layer:
+    def __init__(self, bh: int, n_tokens: int, head_dim: int, dtype: torch.dtype, n_q: int, n_k: int,
+                 device="cuda", two_streams: bool = True):
+        self.bh, self.N, self.d, self.dtype = bh, n_tokens, head_dim, dtype
+        self.n_q, self.n_k = n_q, n_k
+        self.scale = 1.0 / math.sqrt(head_dim)
+        dev = torch.device(device)
+        self.dev = dev
+        L = B.lib()
+        e = lambda *s, dt=torch.int32: torch.empty(*s, dtype=dt, device=dev)
+        self.cq = e(bh, n_q, head_dim, dt=torch.float32)
+        self.ck = e(bh, n_k, head_dim, dt=torch.float32)
+        self.labels_q, self.labels_k = e(bh, n_tokens), e(bh, n_tokens)
+        self.counts_q, self.counts_k = e(bh, n_q), e(bh, n_k)
+        self.qp = e(bh, n_tokens, head_dim, dt=dtype)
+        self.kp = e(bh, n_tokens, head_dim, dt=dtype)
+        self.vp = e(bh, n_tokens, head_dim, dt=dtype)
+        self.op = e(bh, n_tokens, head_dim, dt=dtype)
+        self.out = e(bh, n_tokens, head_dim, dt=dtype)
+        self.perm_q, self.perm_k = e(bh, n_tokens), e(bh, n_tokens)
+        self.off_q, self.off_k = e(bh, n_q + 1), e(bh, n_k + 1)
+        self.sel_count, self.sel_idx = e(bh, n_q), e(bh, n_q, n_k)
+        self.pairs = e(bh, dt=torch.int64)
+        u8 = lambda n: torch.empty(max(int(n), 1), dtype=torch.uint8, device=dev)
+        self.ws_kq = u8(L.svg2_kmeans_workspace_size(bh, n_tokens, head_dim, n_q))
+        self.ws_kk = u8(L.svg2_kmeans_workspace_size(bh, n_tokens, head_dim, n_k))
+        self.ws_pq = u8(L.svg2_permute_workspace_size(bh, n_tokens, n_q))
+        self.ws_pk = u8(L.svg2_permute_workspace_size(bh, n_tokens, n_k))
+        self.ws_sel = u8(L.svg2_select_topp_workspace_size(bh, n_q, n_k))
+        self.ws_attn = u8(L.svg2_varblock_attn_workspace_size(bh, n_tokens, n_q, n_k, head_dim))
+        # dense baseline: one cluster holding every token, selecting itself
+        self.dense_off = torch.tensor([0, n_tokens], dtype=torch.int32, device=dev).repeat(bh, 1).contiguous()
+        self.dense_cnt = torch.ones(bh, 1, dtype=torch.int32, device=dev)
+        self.dense_sel = torch.zeros(bh, 1, 1, dtype=torch.int32, device=dev)
+        self.ws_dense = u8(L.svg2_varblock_attn_workspace_size(bh, n_tokens, 1, 1, head_dim))
+        self.side = torch.cuda.Stream(device=dev) if two_streams else None
+
+    # ------------------------------------------------------------ steps
+    def kmeans(self, q, k, iters: int, warm: bool, seed_q: int, seed_k: int):
+        def side_q():
+            B.kmeans(q, self.n_q, iters, init=self.cq if warm else None, seed=seed_q, centroids=self.cq,
+                     labels=self.labels_q, counts=self.counts_q, workspace=self.ws_kq)
+
+        def side_k():
+            B.kmeans(k, self.n_k, iters, init=self.ck if warm else None, seed=seed_k, centroids=self.ck,
+                     labels=self.labels_k, counts=self.counts_k, workspace=self.ws_kk)
+
+        if self.side is None:
+            side_q()
+            side_k()
+            return
+        main = torch.cuda.current_stream(self.dev)
+        self.side.wait_stream(main)
+        with torch.cuda.stream(self.side):
+            side_k()
+        side_q()
+        main.wait_stream(self.side)
+
+    def permute(self, q, k, v):
+        B.permute(self.labels_q, self.n_q, q, outs=[self.qp], perm=self.perm_q, offsets=self.off_q,
+                  workspace=self.ws_pq)
+        B.permute(self.labels_k, self.n_k, k, v, outs=[self.kp, self.vp], perm=self.perm_k,
+                  offsets=self.off_k, workspace=self.ws_pk)
+
+    def select(self, top_p: float):
+        B.select_topp(self.cq, self.counts_q, self.ck, self.counts_k, top_p, scale=self.scale,
+                      sel_count=self.sel_count, sel_idx=self.sel_idx, pair_count=self.pairs,
+                      workspace=self.ws_sel)
+
+    def attend(self):
+        B.varblock_attn(self.qp, self.kp, self.vp, self.off_q, self.off_k, self.sel_count, self.sel_idx,
+                        scale=self.scale, out=self.op, workspace=self.ws_attn)
+
+    def unpermute(self, out: Optional[torch.Tensor] = None):
+        return B.unpermute(self.op, self.perm_q, out=self.out if out is None else out)
+
+    # ------------------------------------------------------------ layer
+    def run(self, q, k, v, top_p: float, iters: int = 5, warm: bool = False, seed_q: int = 0,
+            seed_k: int = 1, out: Optional[torch.Tensor] = None):
+        """Whole layer; returns the output in the original token order."""
+        self.kmeans(q, k, iters, warm, seed_q, seed_k)
+        self.permute(q, k, v)
+        self.select(top_p)
+        self.attend()
+        return self.unpermute(out)
+
+    def dense(self, q, k, v, out: Optional[torch.Tensor] = None):
+        """This library's own dense attention (one block, every key selected)."""
+        o = out if out is not None else torch.empty_like(q)
+        B.varblock_attn(q, k, v, self.dense_off, self.dense_off, self.dense_cnt, self.dense_sel,
+                        scale=self.scale, out=o, workspace=self.ws_dense)
+        return o
+
+    def density(self) -> float:
+        return float(self.pairs.sum().item()) / (self.bh * float(self.N) ** 2)

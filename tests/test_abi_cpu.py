@@ -1,0 +1,146 @@
+"""The C ABI without a GPU: the library loads, exports every function that
+include/svg2.h declares, and rejects bad arguments on the host before any
+HIP call (so these calls never touch a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_attention_video_head_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HDR = os.path.join(ROOT, "include", "svg2.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = 0x10000        # 16-byte aligned non-null address; never dereferenced
+MISALIGNED = 0x10004
+
+
+def _declared():
+    src = open(HDR).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(svg2_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_five_calls():
+    names = _declared()
+    for call in ("svg2_kmeans", "svg2_permute", "svg2_select_topp", "svg2_varblock_attn", "svg2_unpermute"):
+        assert call in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = B.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    assert sorted(_declared()) == sorted(B.EXPORTED)
+    assert "gfx950" in B.version()
+
+
+def test_status_strings():
+    L = B.lib()
+    for s in range(5):
+        assert L.svg2_status_string(s)
+    assert L.svg2_status_string(99) == b"unknown status"
+
+
+def _km(**kw):
+    a = dict(x=FAKE, dtype=1, bh=2, N=1000, d=128, n=16, iters=3, init=None, seed=0, cent=FAKE, lab=FAKE,
+             cnt=FAKE, md=None, si=None, ws=FAKE, wsn=1 << 40)
+    a.update(kw)
+    return B.lib().svg2_kmeans(a["x"], a["dtype"], a["bh"], a["N"], a["d"], a["n"], a["iters"], a["init"],
+                               a["seed"], a["cent"], a["lab"], a["cnt"], a["md"], a["si"], a["ws"], a["wsn"],
+                               None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), INVALID), (dict(x=MISALIGNED), INVALID), (dict(dtype=7), INVALID),
+    (dict(bh=0), INVALID), (dict(N=0), INVALID), (dict(n=0), INVALID), (dict(n=1001), INVALID),
+    (dict(n=4097, N=10000), INVALID), (dict(d=96), UNSUPPORTED), (dict(iters=-1), INVALID),
+    (dict(iters=101), INVALID), (dict(cent=None), INVALID), (dict(lab=None), INVALID),
+    (dict(cnt=None), INVALID), (dict(N=300000), UNSUPPORTED), (dict(wsn=10), WORKSPACE),
+    (dict(ws=None), WORKSPACE), (dict(init=MISALIGNED), INVALID), (dict(lab=FAKE + 2), INVALID),
+])
+def test_kmeans_validation(kw, code):
+    assert _km(**kw) == code
+
+
+def test_kmeans_size_queries():
+    L = B.lib()
+    assert L.svg2_kmeans_workspace_size(1, 10, 96, 4) == 0
+    assert L.svg2_kmeans_workspace_size(1, 10, 128, 11) == 0
+    assert L.svg2_kmeans_workspace_size(24, 118800, 128, 1000) > 24 * 118800 * 8
+
+
+def _perm(**kw):
+    a = dict(lab=FAKE, bh=4, N=500, n=8, nt=1, src=[FAKE], heads=1, sb=500 * 128, sh=0, st=128, dst=[FAKE],
+             dtype=1, d=128, perm=FAKE, off=FAKE, ws=FAKE, wsn=1 << 30)
+    a.update(kw)
+    src = (ctypes.c_void_p * 2)(*a["src"], *([0] * (2 - len(a["src"]))))
+    dst = (ctypes.c_void_p * 2)(*a["dst"], *([0] * (2 - len(a["dst"]))))
+    return B.lib().svg2_permute(a["lab"], a["bh"], a["N"], a["n"], a["nt"], src, a["heads"], a["sb"], a["sh"],
+                                a["st"], dst, a["dtype"], a["d"], a["perm"], a["off"], a["ws"], a["wsn"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(nt=0), INVALID), (dict(nt=3), INVALID), (dict(src=[0]), INVALID), (dict(dst=[MISALIGNED]), INVALID),
+    (dict(nt=2, src=[FAKE]), INVALID), (dict(heads=3), INVALID), (dict(st=12), INVALID), (dict(sb=-128), INVALID),
+    (dict(lab=None), INVALID), (dict(perm=None), INVALID), (dict(off=None), INVALID), (dict(d=32), UNSUPPORTED),
+    (dict(wsn=4), WORKSPACE), (dict(n=501), INVALID),
+])
+def test_permute_validation(kw, code):
+    assert _perm(**kw) == code
+
+
+def _sel(**kw):
+    a = dict(cq=FAKE, qc=FAKE, nq=10, ck=FAKE, kc=FAKE, nk=20, bh=2, d=128, scale=0.088, p=0.9, sc=FAKE,
+             si=FAKE, pr=None, pc=None, ws=FAKE, wsn=1 << 20)
+    a.update(kw)
+    return B.lib().svg2_select_topp(a["cq"], a["qc"], a["nq"], a["ck"], a["kc"], a["nk"], a["bh"], a["d"],
+                                    ctypes.c_float(a["scale"]), ctypes.c_float(a["p"]), a["sc"], a["si"],
+                                    a["pr"], a["pc"], a["ws"], a["wsn"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(p=0.0), INVALID), (dict(p=1.5), INVALID), (dict(p=float("nan")), INVALID),
+    (dict(scale=0.0), INVALID), (dict(scale=float("inf")), INVALID), (dict(nk=4097), INVALID),
+    (dict(nq=0), INVALID), (dict(cq=None), INVALID), (dict(si=None), INVALID), (dict(d=80), UNSUPPORTED),
+    (dict(pc=FAKE + 4), INVALID), (dict(wsn=0), WORKSPACE),
+])
+def test_select_validation(kw, code):
+    assert _sel(**kw) == code
+
+
+def _attn(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=1, bh=2, N=1000, d=128, qo=FAKE, nq=8, ko=FAKE, nk=9, sc=FAKE,
+             si=FAKE, scale=0.088, out=FAKE, lse=None, ws=FAKE, wsn=1 << 30)
+    a.update(kw)
+    return B.lib().svg2_varblock_attn(a["q"], a["k"], a["v"], a["dtype"], a["bh"], a["N"], a["d"], a["qo"],
+                                      a["nq"], a["ko"], a["nk"], a["sc"], a["si"], ctypes.c_float(a["scale"]),
+                                      a["out"], a["lse"], a["ws"], a["wsn"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(v=MISALIGNED), INVALID), (dict(out=None), INVALID), (dict(dtype=2), INVALID),
+    (dict(N=1 << 25), INVALID), (dict(nq=5000), INVALID), (dict(scale=-1.0), INVALID), (dict(d=256), UNSUPPORTED),
+    (dict(si=None), INVALID), (dict(lse=FAKE + 2), INVALID), (dict(wsn=16), WORKSPACE),
+])
+def test_attn_validation(kw, code):
+    assert _attn(**kw) == code
+
+
+def test_unpermute_validation():
+    L = B.lib()
+    assert L.svg2_unpermute(None, 1, 1, 10, 128, FAKE, FAKE, 1, 1280, 0, 128, None) == INVALID
+    assert L.svg2_unpermute(FAKE, 1, 1, 10, 100, FAKE, FAKE, 1, 1280, 0, 128, None) == UNSUPPORTED
+    assert L.svg2_unpermute(FAKE, 1, 2, 10, 128, FAKE, FAKE, 3, 1280, 0, 128, None) == INVALID
+    assert L.svg2_unpermute(FAKE, 0, 1, 10, 128, FAKE, FAKE, 1, 1280, 0, 130, None) == INVALID
+    assert L.svg2_unpermute(FAKE, 1, 1, 10, 128, None, FAKE, 1, 1280, 0, 128, None) == INVALID
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(B.Svg2Error):
+        B.kmeans(torch.zeros(1, 8, 64), 2, 1)
+    with pytest.raises(B.Svg2Error):
+        B.unpermute(torch.zeros(1, 8, 64), torch.zeros(1, 8, dtype=torch.int32))

@@ -1,0 +1,297 @@
+"""GPU parity: every HIP entry point against the fp64 oracle on the same
+seeded inputs.  Inputs come from the generator and, for later stages, from
+the oracle's own earlier stages; nothing computed on the GPU is fed back to
+the oracle.
+
+Bars (the tolerances are fixed by the method's statement of the path):
+  * integer / index outputs (labels, offsets, permutation, selections,
+    k-means++ picks): bit-exact, except tokens / rows inside the stated
+    tie bands, which must be rare;
+  * bf16 attention: max-abs 2e-2 and relative-L2 1e-2; fp32: 1e-4 / 1e-4;
+  * centroids: within 1e-5 * max(1, |c|).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_attention_video_head_amd import binding as B
+from sparse_attention_video_head_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def np64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64) if t.dtype != torch.float64 else t.cpu().numpy()
+
+
+def dtype_of(name):
+    return torch.float32 if name == "f32" else torch.bfloat16
+
+
+def rel_l2(a, b):
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
+
+
+def mixture(bh, N, d, comps, seed, dtype):
+    """Clustered [bh, N, d] Q, K and N(0,1) V (seeded, numpy -> rounded)."""
+    rng = np.random.default_rng(seed)
+    qs, ks, vs = [], [], []
+    for _ in range(bh):
+        mu = rng.standard_normal((comps, d))
+        z = rng.integers(0, comps, N)
+        qs.append(mu[z] + 0.3 * rng.standard_normal((N, d)))
+        ks.append(mu[z] + 0.3 * rng.standard_normal((N, d)))
+        vs.append(rng.standard_normal((N, d)))
+    f = lambda a: torch.from_numpy(np.stack(a)).to(dtype)
+    return f(qs), f(ks), f(vs)
+
+
+# ====================================================================== permute
+@pytest.mark.parametrize("dt,d,N,n,skew,nt", [
+    ("bf16", 128, 5000, 37, 0.0, 1), ("bf16", 128, 4097, 300, 1.2, 2), ("f32", 64, 2048, 5, 0.0, 2),
+    ("bf16", 64, 1, 1, 0.0, 1), ("f32", 128, 777, 777, 0.0, 1), ("bf16", 128, 20000, 4096, 0.8, 2),
+])
+def test_permute_bit_exact(dt, d, N, n, skew, nt):
+    bh = 3
+    dtype = dtype_of(dt)
+    labels = np.stack([synth.random_labels(N, n, seed=10 + h, skew=skew) for h in range(bh)])
+    xs = [synth.uniform_rows(bh * N, d, seed=20 + t, dtype=dtype).reshape(bh, N, d) for t in range(nt)]
+    outs, perm, off = B.permute(torch.from_numpy(labels).to(DEV), n, *[x.to(DEV) for x in xs])
+    torch.cuda.synchronize()
+    for h in range(bh):
+        p_ref, o_ref, _ = oracle.counting_sort(labels[h], n)
+        np.testing.assert_array_equal(perm[h].cpu().numpy(), p_ref)
+        np.testing.assert_array_equal(off[h].cpu().numpy(), o_ref)
+        for t in range(nt):
+            assert torch.equal(outs[t][h].cpu(), xs[t][h][torch.from_numpy(p_ref)])
+
+
+def test_permute_strided_bnhd_layout_and_unpermute():
+    """A [B, N, H, d] source (model layout) gathered through strides; the
+    un-permute scatters back into the same strided layout exactly."""
+    Bsz, H, N, d, n = 2, 3, 1500, 128, 20
+    x = synth.uniform_rows(Bsz * N * H, d, seed=5, dtype=torch.bfloat16).reshape(Bsz, N, H, d)
+    labels = np.stack([synth.random_labels(N, n, seed=30 + p) for p in range(Bsz * H)])
+    xv = x.to(DEV).transpose(1, 2)                      # [B, H, N, d] view, strided
+    (xp,), perm, off = B.permute(torch.from_numpy(labels).to(DEV), n, xv)
+    back = torch.zeros_like(x, device=DEV)
+    B.unpermute(xp, perm, out=back.transpose(1, 2))
+    torch.cuda.synchronize()
+    xh = x.transpose(1, 2).reshape(Bsz * H, N, d)
+    for p in range(Bsz * H):
+        pr, _, _ = oracle.counting_sort(labels[p], n)
+        assert torch.equal(xp[p].cpu(), xh[p][torch.from_numpy(pr)])
+    assert torch.equal(back.cpu(), x)
+
+
+@pytest.mark.parametrize("dt,d", [("bf16", 128), ("f32", 64), ("bf16", 64)])
+def test_unpermute_bit_exact(dt, d):
+    bh, N = 2, 3001
+    src = synth.uniform_rows(bh * N, d, seed=7, dtype=dtype_of(dt)).reshape(bh, N, d)
+    rng = np.random.default_rng(3)
+    perm = np.stack([rng.permutation(N) for _ in range(bh)]).astype(np.int32)
+    out = B.unpermute(src.to(DEV), torch.from_numpy(perm).to(DEV))
+    torch.cuda.synchronize()
+    for h in range(bh):
+        ref = oracle.unpermute_rows(np64(src[h]), perm[h])
+        np.testing.assert_array_equal(np64(out[h]), ref)
+
+
+# ====================================================================== select
+@pytest.mark.parametrize("n_q,n_k,d,top_p,spread", [
+    (40, 250, 128, 0.9, 1.0), (17, 1000, 128, 0.8, 0.5), (8, 64, 64, 0.95, 1.5), (5, 1, 64, 0.5, 1.0),
+    (12, 4096, 128, 0.9, 0.7), (9, 300, 128, 1.0, 1.0), (9, 300, 128, 1e-6, 1.0),
+])
+def test_select_topp_exact(n_q, n_k, d, top_p, spread):
+    bh = 2
+    cq = np.stack([synth.gaussian_centroids(n_q, d, seed=40 + h, spread=spread) for h in range(bh)])
+    ck = np.stack([synth.gaussian_centroids(n_k, d, seed=50 + h, spread=spread) for h in range(bh)])
+    rng = np.random.default_rng(6)
+    kc = rng.integers(0, 200, (bh, n_k)).astype(np.int32)
+    kc[:, 0] = np.maximum(kc[:, 0], 1)
+    if n_k > 3:
+        kc[:, 1] = 0                                       # an empty cluster
+    qc = rng.integers(0, 300, (bh, n_q)).astype(np.int32)
+    scale = 1.0 / math.sqrt(d)
+    r = B.select_topp(torch.from_numpy(cq).to(DEV), torch.from_numpy(qc).to(DEV), torch.from_numpy(ck).to(DEV),
+                      torch.from_numpy(kc).to(DEV), top_p, scale=scale, probs=True)
+    torch.cuda.synchronize()
+    p32 = float(np.float32(top_p))
+    s32 = float(np.float32(scale))
+    n_amb = 0
+    for h in range(bh):
+        P = oracle.centroid_probs(cq[h].astype(np.float64), ck[h].astype(np.float64), kc[h], s32)
+        sel = oracle.select_topp(P, kc[h], p32, band=1e-10)
+        np.testing.assert_allclose(r["probs"][h].cpu().numpy(), P, rtol=1e-6, atol=1e-30)
+        cnt = r["sel_count"][h].cpu().numpy()
+        idx = r["sel_idx"][h].cpu().numpy()
+        pairs = 0
+        for i in range(n_q):
+            got = idx[i, :cnt[i]]
+            pairs += int(qc[h, i]) * int(kc[h, got].sum())
+            if sel.ambiguous[i]:
+                n_amb += 1
+                continue
+            np.testing.assert_array_equal(got, sel.lists[i], err_msg=f"head {h} row {i}")
+        assert int(r["pair_count"][h]) == pairs
+    assert n_amb <= max(1, bh * n_q // 1000)
+
+
+# ====================================================================== attention
+def _attn_case(dt, d, bh, N, n_q, n_k, top_p, seed, empty_rows=False):
+    dtype = dtype_of(dt)
+    q, k, v = mixture(bh, N, d, comps=max(4, n_k // 3), seed=seed, dtype=dtype)
+    qo, ko, cnt, idx, lists = [], [], [], [], []
+    for h in range(bh):
+        lq = synth.random_labels(N, n_q, seed=seed * 7 + h, skew=0.7)
+        lk = synth.random_labels(N, n_k, seed=seed * 11 + h, skew=0.9)
+        _, oq, cq_ = oracle.counting_sort(lq, n_q)
+        _, okk, ck_ = oracle.counting_sort(lk, n_k)
+        P = oracle.centroid_probs(synth.gaussian_centroids(n_q, d, seed + h), synth.gaussian_centroids(n_k, d, seed + 99 + h),
+                                  ck_, 1 / math.sqrt(d))
+        sel = oracle.select_topp(P, ck_, top_p)
+        ls = [l.copy() for l in sel.lists]
+        if empty_rows:
+            ls[0] = np.zeros(0, np.int64)
+        row_idx = np.zeros((n_q, n_k), np.int32)
+        for i, l in enumerate(ls):
+            row_idx[i, :len(l)] = l
+        qo.append(oq); ko.append(okk); idx.append(row_idx); lists.append(ls)
+        cnt.append([len(l) for l in ls])
+    t = lambda a: torch.from_numpy(np.asarray(a, dtype=np.int32)).to(DEV)
+    return q, k, v, t(qo), t(ko), t(cnt), t(idx), lists, np.array(qo), np.array(ko)
+
+
+@pytest.mark.parametrize("dt,d,N,n_q,n_k,top_p", [
+    ("bf16", 128, 3000, 20, 50, 0.9), ("bf16", 128, 4099, 7, 130, 0.6), ("bf16", 64, 2500, 30, 40, 0.95),
+    ("f32", 64, 2000, 16, 32, 0.9), ("f32", 128, 1500, 9, 25, 0.7), ("bf16", 128, 700, 1, 1, 1.0),
+])
+def test_varblock_attn_vs_oracle(dt, d, N, n_q, n_k, top_p):
+    bh = 2
+    q, k, v, qo, ko, cnt, idx, lists, qo_np, ko_np = _attn_case(dt, d, bh, N, n_q, n_k, top_p, seed=N + n_q,
+                                                               empty_rows=(dt == "bf16" and n_q > 1))
+    out, lse = B.varblock_attn(q.to(DEV), k.to(DEV), v.to(DEV), qo, ko, cnt, idx, lse=True)
+    torch.cuda.synchronize()
+    tol = (2e-2, 1e-2) if dt == "bf16" else (1e-4, 1e-4)
+    s = 1 / math.sqrt(d)
+    for h in range(bh):
+        ref, ref_lse = oracle.block_attention(np64(q[h]), np64(k[h]), np64(v[h]), qo_np[h], ko_np[h], lists[h], s)
+        got = np64(out[h])
+        assert np.max(np.abs(got - ref)) <= tol[0]
+        assert rel_l2(got, ref) <= tol[1]
+        gl = lse[h].cpu().numpy().astype(np.float64)
+        fin = np.isfinite(ref_lse)
+        np.testing.assert_allclose(gl[fin], ref_lse[fin], rtol=0, atol=1e-3 if dt == "bf16" else 1e-4)
+        assert np.all(gl[~fin] == -np.inf) and np.all(got[~fin] == 0)
+
+
+def test_varblock_attn_dense_equals_softmax_attention():
+    """n_q = n_k = 1 with every key selected is plain softmax attention."""
+    bh, N, d = 2, 1100, 128
+    q, k, v = mixture(bh, N, d, 10, seed=3, dtype=torch.bfloat16)
+    off = torch.tensor([[0, N]] * bh, dtype=torch.int32, device=DEV)
+    out, _ = B.varblock_attn(q.to(DEV), k.to(DEV), v.to(DEV), off, off,
+                             torch.ones(bh, 1, dtype=torch.int32, device=DEV),
+                             torch.zeros(bh, 1, 1, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    for h in range(bh):
+        ref, _ = oracle.softmax_attention_rows(np64(q[h]), np64(k[h]), np64(v[h]), 1 / math.sqrt(d))
+        assert np.max(np.abs(np64(out[h]) - ref)) <= 2e-2
+        assert rel_l2(np64(out[h]), ref) <= 1e-2
+
+
+def test_varblock_attn_deterministic():
+    q, k, v, qo, ko, cnt, idx, *_ = _attn_case("bf16", 128, 2, 3000, 20, 50, 0.9, seed=77)
+    a, _ = B.varblock_attn(q.to(DEV), k.to(DEV), v.to(DEV), qo, ko, cnt, idx)
+    b, _ = B.varblock_attn(q.to(DEV), k.to(DEV), v.to(DEV), qo, ko, cnt, idx)
+    assert torch.equal(a, b)
+
+
+# ====================================================================== k-means
+@pytest.mark.parametrize("dt,d,N,n", [("bf16", 128, 6000, 50), ("bf16", 64, 3000, 17), ("f32", 64, 4096, 64),
+                                      ("bf16", 128, 2000, 1)])
+def test_kmeans_one_round_vs_oracle(dt, d, N, n):
+    """One Lloyd round from the same initial centroids: labels outside the
+    tie band, counts and centroids."""
+    bh = 2
+    q, _, _ = mixture(bh, N, d, comps=max(2, n // 2), seed=N + n, dtype=dtype_of(dt))
+    init = np.stack([np64(q[h])[np.random.default_rng(h).choice(N, n, replace=False)] for h in range(bh)])
+    init = init + 0.01 * np.random.default_rng(9).standard_normal(init.shape)
+    init32 = init.astype(np.float32)
+    r = B.kmeans(q.to(DEV), n, 1, init=torch.from_numpy(init32).to(DEV), min_dist=True)
+    torch.cuda.synchronize()
+    for h in range(bh):
+        X = np64(q[h])
+        a = oracle.assign(X, init32[h].astype(np.float64))
+        lab = r["labels"][h].cpu().numpy()
+        clear = a.margin >= 1e-5
+        assert np.mean(~clear) <= 1e-3 + 1.0 / N
+        np.testing.assert_array_equal(lab[clear], a.labels[clear])
+        np.testing.assert_array_equal(r["counts"][h].cpu().numpy(), np.bincount(lab, minlength=n))
+        np.testing.assert_allclose(r["min_dist"][h].cpu().numpy(), a.min_dist, rtol=1e-4, atol=1e-3)
+        if np.all(lab == a.labels):
+            C, _ = oracle.update(X, a.labels, init32[h].astype(np.float64))
+            got = r["centroids"][h].cpu().numpy().astype(np.float64)
+            assert np.all(np.abs(got - C) <= 1e-5 * np.maximum(1.0, np.abs(C)))
+
+
+def test_kmeans_chained_rounds_equal_one_call():
+    """T chained one-round calls equal one T-round call, bit for bit."""
+    bh, N, d, n = 2, 5000, 128, 40
+    q, _, _ = mixture(bh, N, d, comps=30, seed=5, dtype=torch.bfloat16)
+    qd = q.to(DEV)
+    one = B.kmeans(qd, n, 3, seed=11)
+    c = B.kmeans(qd, n, 0, seed=11)["centroids"].clone()
+    for _ in range(3):
+        step = B.kmeans(qd, n, 1, init=c)
+        c = step["centroids"].clone()
+    torch.cuda.synchronize()
+    assert torch.equal(one["centroids"], c)
+    assert torch.equal(one["labels"], step["labels"])
+    assert torch.equal(one["counts"], step["counts"])
+
+
+@pytest.mark.parametrize("dt,d,N,n,heads", [("f32", 64, 4096, 64, 1), ("bf16", 128, 16384, 250, 2),
+                                           ("bf16", 128, 3000, 100, 2), ("bf16", 64, 700, 700, 1)])
+def test_kmeanspp_picks_match_oracle(dt, d, N, n, heads):
+    q, _, _ = mixture(heads, N, d, comps=max(8, n // 2), seed=n, dtype=dtype_of(dt))
+    seed = 0xABCDEF12345 + n
+    r = B.kmeans(q.to(DEV), n, 0, seed=seed, seed_index=True)
+    torch.cuda.synchronize()
+    for h in range(heads):
+        X = np64(q[h])
+        ref = oracle.kmeanspp(X, n, seed, problem=h)
+        got = r["seed_index"][h].cpu().numpy()
+        amb = np.nonzero(ref.margin < 1e-10)[0]
+        upto = int(amb[0]) if len(amb) else n
+        np.testing.assert_array_equal(got[:upto], ref.index[:upto])
+        assert upto >= n // 2
+        np.testing.assert_array_equal(r["centroids"][h].cpu().numpy()[:upto].astype(np.float64), X[got[:upto]])
+
+
+# ====================================================================== whole layer
+def test_layer_tiny_config_end_to_end():
+    """The tiny fp32 config: the whole GPU layer (cold k-means++, 5 rounds,
+    permute, top-p 0.9, attention, un-permute) against the oracle layer."""
+    from sparse_attention_video_head_amd.pipeline import SVG2Layer
+    cfg = synth.CONFIGS["tiny"]
+    data = synth.make_layer(cfg)
+    layer = SVG2Layer(cfg.bh, cfg.n_tokens, cfg.head_dim, cfg.torch_dtype, cfg.n_q, cfg.n_k)
+    top_p = cfg.top_p[0]
+    out = layer.run(data["q"].to(DEV), data["k"].to(DEV), data["v"].to(DEV), top_p, iters=cfg.iters,
+                    seed_q=100, seed_k=200)
+    torch.cuda.synchronize()
+    q, k, v = (np64(data[x][0]) for x in "qkv")
+    ref = oracle.layer(q, k, v, cfg.n_q, cfg.n_k, cfg.iters, float(np.float32(top_p)), seed_q=100, seed_k=200)
+    agree_q = np.mean(layer.labels_q[0].cpu().numpy() == ref.km_q.labels)
+    agree_k = np.mean(layer.labels_k[0].cpu().numpy() == ref.km_k.labels)
+    assert agree_q >= 0.999 and agree_k >= 0.999
+    got = np64(out[0])
+    assert rel_l2(got, ref.out) <= 1e-4
+    assert np.max(np.abs(got - ref.out)) <= 1e-3
+    assert int(layer.pairs[0]) == ref.pairs
