@@ -94,7 +94,6 @@ int svg2_last_hip_error(void);
  *                   T-th assignment.
  *   seed_index      out [bh, n_clusters] int32 or NULL: token index of each
  *                   k-means++ pick (cold start only).
- * Limits: k-means++ (init_centroids NULL) needs n_tokens <= 262144.
  * ---------------------------------------------------------------------- */
 size_t svg2_kmeans_workspace_size(int32_t bh, int32_t n_tokens, int32_t head_dim,
                                   int32_t n_clusters);

@@ -15,7 +15,6 @@ namespace {
 thread_local int g_last_hip_error = 0;
 
 constexpr int kMaxTokens = 1 << 24;
-constexpr int kMaxSeedTokens = 262144;     // k-means++ keeps 64-token block sums in LDS
 constexpr size_t kAlign = 256;
 
 int hip_status(hipError_t e) {
@@ -47,7 +46,9 @@ struct Carve {
 struct KmeansWs {
   double* d2;
   int32_t* near;      // 2 * bh * N ints: nearest pick, then ||x||^2 as float
-  int32_t* seed_idx;
+  int32_t* picks;
+  double* cc;
+  double* bsum;
   uint16_t* c_hi;
   uint16_t* c_lo;
   float* c_norm;
@@ -61,7 +62,9 @@ KmeansWs carve_kmeans(Carve& c, int bh, int N, int d, int n) {
   const size_t bN = (size_t)bh * N;
   w.d2 = c.take<double>(bN);
   w.near = c.take<int32_t>(2 * bN);
-  w.seed_idx = c.take<int32_t>((size_t)bh * n);
+  w.picks = c.take<int32_t>((size_t)bh * n);
+  w.cc = c.take<double>((size_t)bh * n);
+  w.bsum = c.take<double>((size_t)bh * ((N + 255) / 256));
   w.c_hi = c.take<uint16_t>((size_t)bh * n * d);
   w.c_lo = c.take<uint16_t>((size_t)bh * n * d);
   w.c_norm = c.take<float>((size_t)bh * n);
@@ -123,7 +126,6 @@ int svg2_kmeans(const void* x, int32_t dtype, int32_t bh, int32_t n_tokens, int3
   if ((labels && !aligned(labels, 4)) || (counts && !aligned(counts, 4)) ||
       (min_dist && !aligned(min_dist, 4)) || (seed_index && !aligned(seed_index, 4)))
     return SVG2_ERR_INVALID_ARG;
-  if (!init_centroids && n_tokens > kMaxSeedTokens) return SVG2_ERR_UNSUPPORTED;
   const size_t need = svg2_kmeans_workspace_size(bh, n_tokens, head_dim, n_clusters);
   if (workspace_bytes < need || (need && !workspace)) return SVG2_ERR_WORKSPACE;
   if (!aligned(workspace, kAlign)) return SVG2_ERR_INVALID_ARG;
@@ -134,8 +136,8 @@ int svg2_kmeans(const void* x, int32_t dtype, int32_t bh, int32_t n_tokens, int3
   const int N = n_tokens, n = n_clusters, d = head_dim;
   int st;
   if (!init_centroids) {
-    st = hip_status(launch_kmeanspp(x, bf16, bh, N, d, n, seed, w.d2, w.near, centroids,
-                                    seed_index ? seed_index : w.seed_idx, stream));
+    st = hip_status(launch_kmeanspp(x, bf16, bh, N, d, n, seed, w.d2, w.near, centroids, seed_index,
+                                    w.picks, w.cc, w.bsum, stream));
     if (st) return st;
   } else if (init_centroids != centroids) {
     st = hip_status(hipMemcpyAsync(centroids, init_centroids, (size_t)bh * n * d * sizeof(float),

@@ -104,8 +104,19 @@ struct KeyCursor {
 };
 
 // ---------------------------------------------------------------- bf16
+// Lazy rescaling: the exponentials use a reference max m_ref that only moves
+// when a tile's max exceeds it by more than kLazyTau (log2 units), so P stays
+// <= 2^kLazyTau and O / l are rescaled rarely.  The result is the same
+// softmax; only the intermediate scaling differs.
+constexpr float kLazyTau = 8.f;
+
 template <int D>
-__global__ __launch_bounds__(256) void k_attn_bf16(
+struct AttnTileRegs {
+  u32x4_t r[8];
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void k_attn_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     int N, const int32_t* __restrict__ q_off, int n_q, const int32_t* __restrict__ k_off, int n_k,
     const int32_t* __restrict__ sel_count, const int32_t* __restrict__ sel_idx, float scale_log2,
@@ -162,6 +173,7 @@ __global__ __launch_bounds__(256) void k_attn_bf16(
       slot_of[e] = -1;
     }
   }
+  const uint16_t* src = is_v ? V + base + vc * 8 : K + base;
 
   KeyCursor cur;
   {
@@ -170,34 +182,26 @@ __global__ __launch_bounds__(256) void k_attn_bf16(
     cur.init(sel_idx + ((size_t)p * n_q + ci) * n_k, k_off + (size_t)p * (n_k + 1), ns, n_k, N);
   }
 
-  float m_run = -__builtin_inff();
-  float l_run = 0.f;
-  f32x16_t o[DT];
+  // global -> registers for the tile whose keys are `key`
+  auto load_tile = [&](const int (&key)[8], AttnTileRegs<D>& t) {
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
-
-  for (;;) {
-    int key[8];
-    const int filled = cur.fill<8>(BN, slot_of, key);
-    if (filled == 0) break;
-    __syncthreads();                                   // previous tile consumed
-    if (is_v) {
-      u32x4_t r[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        r[e] = u32x4_t{0u, 0u, 0u, 0u};
-        if (key[e] >= 0) r[e] = *reinterpret_cast<const u32x4_t*>(V + base + (size_t)key[e] * D + vc * 8);
+    for (int e = 0; e < 8; ++e) {
+      t.r[e] = u32x4_t{0u, 0u, 0u, 0u};
+      if (key[e] >= 0) {
+        const size_t off = is_v ? (size_t)key[e] * D : (size_t)key[e] * D + ((ku + KUNITS * e) % VPR) * 8;
+        if (is_v || is_k) t.r[e] = *reinterpret_cast<const u32x4_t*>(src + off);
       }
-      // transpose the 8 keys x 8 columns block: output row (column vc*8+x)
-      // holds the 8 keys in slot order
+    }
+  };
+  // registers -> LDS (V transposed into the permuted key order)
+  auto store_tile = [&](const AttnTileRegs<D>& t) {
+    if (is_v) {
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
         const uint32_t sel = (x & 1) ? 0x07060302u : 0x05040100u;
         u32x4_t w;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) w[q] = __builtin_amdgcn_perm(r[2 * q + 1][x >> 1], r[2 * q][x >> 1], sel);
+        for (int q = 0; q < 4; ++q) w[q] = __builtin_amdgcn_perm(t.r[2 * q + 1][x >> 1], t.r[2 * q][x >> 1], sel);
         const int d = vc * 8 + x;
         const int blk = vg ^ ((d >> 3) & 7);
         *reinterpret_cast<u32x4_t*>(&sV[d * VLD + blk * 8]) = w;
@@ -206,12 +210,32 @@ __global__ __launch_bounds__(256) void k_attn_bf16(
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int v = ku + KUNITS * e;
-        u32x4_t w = {0u, 0u, 0u, 0u};
-        if (key[e] >= 0) w = *reinterpret_cast<const u32x4_t*>(K + base + (size_t)key[e] * D + (v % VPR) * 8);
-        *reinterpret_cast<u32x4_t*>(&sK[(v / VPR) * KLD + (v % VPR) * 8]) = w;
+        *reinterpret_cast<u32x4_t*>(&sK[(v / VPR) * KLD + (v % VPR) * 8]) = t.r[e];
       }
     }
-    __syncthreads();
+  };
+
+  float m_ref = -__builtin_inff();
+  float l_run = 0.f;
+  f32x16_t o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
+
+  AttnTileRegs<D> regs;
+  int key[8];
+  int filled = cur.fill<8>(BN, slot_of, key);
+  if (filled > 0) {
+    load_tile(key, regs);
+    store_tile(regs);
+  }
+  __syncthreads();
+
+  while (filled > 0) {
+    // prefetch the next tile while this one is computed
+    const int next_filled = cur.fill<8>(BN, slot_of, key);
+    if (next_filled > 0) load_tile(key, regs);
 
     // ---- S^T = K Q^T for 2 sub-tiles of 32 keys
     f32x16_t s[2];
@@ -226,35 +250,41 @@ __global__ __launch_bounds__(256) void k_attn_bf16(
       }
     }
     // ---- online softmax; lane holds keys st*32 + (i/4)*8 + half*4 + i%4
-    float mx = -__builtin_inff();
+    if (filled < BN) {
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int ks = st * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+          if (ks >= filled) s[st][i] = -__builtin_inff();
+        }
+    }
+    float mx = s[0][0];
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int ks = st * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-        const float x = ks < filled ? s[st][i] * scale_log2 : -__builtin_inff();
-        s[st][i] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[st][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+    if (mx > m_ref + kLazyTau) {
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - mx);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+      m_ref = mx;
+    }
+    const float neg = -m_ref;
     float rs = 0.f;
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float e = __builtin_amdgcn_exp2f(s[st][i] - m_use);
+        const float e = __builtin_amdgcn_exp2f(fmaf(s[st][i], scale_log2, neg));
         s[st][i] = e;
         rs += e;
       }
-    l_run = l_run * alpha + rs;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
-    m_run = m_new;
+    l_run += rs;
 
     // ---- O^T += V^T P^T, 4 k-steps of 16 keys
 #pragma unroll
@@ -272,6 +302,12 @@ __global__ __launch_bounds__(256) void k_attn_bf16(
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[dt], 0, 0, 0);
       }
     }
+    __syncthreads();                       // every wave is done with this tile
+    if (next_filled > 0) {
+      store_tile(regs);
+      __syncthreads();
+    }
+    filled = next_filled;
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -288,7 +324,7 @@ __global__ __launch_bounds__(256) void k_attn_bf16(
         *reinterpret_cast<uint2*>(orow + dt * 32 + g * 8 + half * 4) = w;
       }
     if (lse && half == 0)
-      lse[(size_t)p * N + row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f
+      lse[(size_t)p * N + row] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * 0.69314718055994531f
                                             : -__builtin_inff();
   }
 }

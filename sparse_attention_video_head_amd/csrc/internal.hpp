@@ -25,12 +25,13 @@ hipError_t launch_scatter_rows(const void* src, void* dst, int esize, int d, int
                                hipStream_t s);
 
 // --------------------------------------------------------------- kmeans.hip
-// k-means++ seeding, one work-group per problem.  state_ws: bh*N doubles (D2)
-// followed by bh*N ints (nearest pick).  Writes centroids [bh,n,d] fp32 and
-// seed_index [bh,n].
+// k-means++ seeding (two kernels per pick).  d2_ws: bh*N doubles; near_ws:
+// 2*bh*N ints (nearest pick, then ||x||^2 as float); picks_ws: bh*n ints;
+// cc_ws: bh*n doubles; bsum_ws: bh*ceil(N/256) doubles.  Writes centroids
+// [bh,n,d] fp32 and seed_index [bh,n] (may be null).
 hipError_t launch_kmeanspp(const void* x, bool bf16, int bh, int N, int d, int n, uint64_t seed,
                            double* d2_ws, int32_t* near_ws, float* centroids, int32_t* seed_index,
-                           hipStream_t s);
+                           int32_t* picks_ws, double* cc_ws, double* bsum_ws, hipStream_t s);
 // centroid split for the matrix-core assignment: c_hi + c_lo (bf16 pair) and ||c||^2
 hipError_t launch_prep_centroids(const float* c, int bh, int n, int d, uint16_t* c_hi,
                                  uint16_t* c_lo, float* c_norm, hipStream_t s);

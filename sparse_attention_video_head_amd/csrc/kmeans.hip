@@ -27,9 +27,6 @@ __device__ __forceinline__ double seed_uniform(uint64_t seed, int problem, int p
   return (double)(splitmix64_dev(x) >> 11) * 0x1.0p-53;
 }
 
-constexpr int kSeedThreads = 1024;
-constexpr int kSeedWaves = kSeedThreads / kWave;
-constexpr int kSeedMaxBlocks = 4096;     // 64-token blocks -> n_tokens <= 262144
 
 // ||x - c||^2 as the fp64 sum of fp64 squared differences: the differences of
 // bf16 or fp32 values are exact in fp64, and so are the squares of bf16
@@ -74,7 +71,7 @@ template <int D>
 __device__ __forceinline__ float dot_bf16_f32(const uint16_t* x, const float* c) {
   const u32x4_t* xv = reinterpret_cast<const u32x4_t*>(x);
   float acc = 0.f;
-#pragma unroll
+#pragma unroll 4
   for (int q = 0; q < D / 8; ++q) {
     const u32x4_t v = xv[q];
 #pragma unroll
@@ -86,190 +83,276 @@ __device__ __forceinline__ float dot_bf16_f32(const uint16_t* x, const float* c)
   return acc;
 }
 
-// One work-group per problem runs all n picks.  Per token it keeps D2 (exact
-// fp64 squared distance to the nearest pick), the nearest pick's number and
-// ||x||^2 (fp32).  A new pick c can lower D2(x) only if
-// ||c - c_near||^2 < 4 D2(x) (triangle inequality, Elkan 2003), so other
-// tokens are skipped without reading x; the skip leaves D2 bit-identical to
-// evaluating every token.
+// k-means++ runs as two kernels per pick so that every problem's tokens are
+// spread over the whole chip and the kernel boundaries order the picks:
+//   k_seed_update(k)  all tokens: D2 = min(D2, ||x - c_k||^2), then 256-token
+//                     block sums of D2 (4 consecutive tokens per lane);
+//   k_seed_sample(k)  one work-group per problem: pick k+1 by inverse-CDF
+//                     sampling over the block sums, then the distances from
+//                     pick k+1 to every earlier pick for the next update.
+// Per token the state is D2 (exact fp64), the nearest pick's number and
+// ||x||^2 (fp32).  A pick c can lower D2(x) only if ||c - c_near||^2 < 4 D2(x)
+// (triangle inequality, Elkan 2003), so other tokens are skipped without
+// reading x; the skip leaves D2 bit-identical to evaluating every token.
+constexpr int kSeedTPL = 4;
+constexpr int kSeedBlk = kWave * kSeedTPL;        // 256 tokens per sampling block
+constexpr int kSeedWavesPerWG = 4;
+
 template <typename T, int D>
-__global__ __launch_bounds__(kSeedThreads) void k_kmeanspp(
-    const T* __restrict__ X, int N, int n, uint64_t seed, double* __restrict__ D2g,
-    int32_t* __restrict__ Ag, float* __restrict__ XNg, float* __restrict__ C0,
+__device__ __forceinline__ bool seed_lowers(const T* xr, const double* cd, const float* cf, float cn,
+                                            float xn, double cc_near, double& d2) {
+  if (cc_near >= 4.0 * d2 * (1.0 + 0x1p-20)) return false;
+  if (sizeof(T) == 2) {
+    // |approx - ||x - c||^2| <= D 2^-24 (xn + cn) plus the rounding of xn, cn
+    // and the two additions: below 2e-5 (xn + cn) at D = 128
+    const float approx = xn + cn - 2.f * dot_bf16_f32<D>(reinterpret_cast<const uint16_t*>(xr), cf);
+    if (!(approx <= (float)d2 + 5e-5f * (xn + cn) + 1e-30f)) return false;
+  }
+  const double nd = ExactDist<T, D>::run(xr, cd);
+  if (nd < d2) {
+    d2 = nd;
+    return true;
+  }
+  return false;
+}
+
+__device__ __forceinline__ int first_pick(uint64_t seed, int p, int N) {
+  return min((int)(seed_uniform(seed, p, 0) * (double)N), N - 1);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_seed_update(
+    const T* __restrict__ X, int N, int n, int k, uint64_t seed, double* __restrict__ D2g,
+    int32_t* __restrict__ Ag, float* __restrict__ XNg, int32_t* __restrict__ picks,
+    const double* __restrict__ ccg, double* __restrict__ bsum, float* __restrict__ C0,
     int32_t* __restrict__ seed_index) {
-  __shared__ double s_bsum[kSeedMaxBlocks];
-  __shared__ double s_cc[kMaxClusters];
-  __shared__ int32_t s_idx[kMaxClusters];
   __shared__ float s_c[D];
   __shared__ double s_cd[D];
-  __shared__ double s_red[17];
-  __shared__ int s_pick, s_blk, s_last;
-  __shared__ double s_resid;
-  __shared__ float s_cn;
-
   constexpr bool kBF16 = sizeof(T) == 2;
-  const int p = blockIdx.x;
+  const int p = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const T* Xp = X + (size_t)p * N * D;
   double* D2 = D2g + (size_t)p * N;
   int32_t* A = Ag + (size_t)p * N;
   float* XN = XNg + (size_t)p * N;
-  const int nblk = (N + kWave - 1) / kWave;
-
-  if (tid == 0) s_pick = min((int)(seed_uniform(seed, p, 0) * (double)N), N - 1);
+  const int nblk = (N + kSeedBlk - 1) / kSeedBlk;
+  const int t = k == 0 ? first_pick(seed, p, N) : picks[(size_t)p * n + k];
+  for (int e = tid; e < D; e += 256) {
+    const float v = Elem<T>::get(Xp, (size_t)t * D + e);
+    s_c[e] = v;
+    s_cd[e] = (double)v;
+    if (k == 0 && blockIdx.x == 0) C0[(size_t)p * n * D + e] = v;
+  }
+  if (k == 0 && blockIdx.x == 0 && tid == 0) {
+    picks[(size_t)p * n] = t;
+    if (seed_index) seed_index[(size_t)p * n] = t;
+  }
   __syncthreads();
+  float cn = 0.f;
+  for (int e = lane; e < D; e += kWave) cn = fmaf(s_c[e], s_c[e], cn);
+  cn = wave_sum(cn);
 
-  for (int k = 0; k < n; ++k) {
-    const int t = s_pick;
-    for (int e = tid; e < D; e += kSeedThreads) {
-      const float v = Elem<T>::get(Xp, (size_t)t * D + e);
-      s_c[e] = v;
-      s_cd[e] = (double)v;
-      C0[((size_t)p * n + k) * D + e] = v;
-    }
-    if (tid == 0) {
-      s_idx[k] = t;
-      if (seed_index) seed_index[(size_t)p * n + k] = t;
-    }
-    if (k == n - 1) break;
-    __syncthreads();
-
-    if (wave == 0) {
-      float a = 0.f;
-      for (int e = lane; e < D; e += kWave) a += s_c[e] * s_c[e];
-      a = wave_sum(a);
-      if (lane == 0) s_cn = a;
-    }
-    for (int a = tid; a < k; a += kSeedThreads)
-      s_cc[a] = ExactDist<T, D>::run(Xp + (size_t)s_idx[a] * D, s_cd);
-    __syncthreads();
-    const float cn = s_cn;
-
-    // ---- lower D2 with the new pick; 64-token block sums for sampling
-    for (int b = wave; b < nblk; b += kSeedWaves) {
-      const int tok = b * kWave + lane;
-      double d2 = 0.0;
+  const int b = blockIdx.x * kSeedWavesPerWG + wave;
+  if (b >= nblk) return;
+  const int t0 = b * kSeedBlk + kSeedTPL * lane;
+  double d2[kSeedTPL];
+  if (k == 0) {
+#pragma unroll 1
+    for (int i = 0; i < kSeedTPL; ++i) {
+      d2[i] = 0.0;
+      const int tok = t0 + i;
       if (tok < N) {
         const T* xr = Xp + (size_t)tok * D;
-        if (k == 0) {
-          d2 = ExactDist<T, D>::run(xr, s_cd);
-          D2[tok] = d2;
-          A[tok] = 0;
-          if (kBF16) {
-            float xn = 0.f;
-            const uint32_t* xw = reinterpret_cast<const uint32_t*>(xr);
-            for (int w = 0; w < D / 2; ++w) {
-              const float a0 = bf16_lo(xw[w]), a1 = bf16_hi(xw[w]);
+        d2[i] = ExactDist<T, D>::run(xr, s_cd);
+        D2[tok] = d2[i];
+        A[tok] = 0;
+        if (kBF16) {
+          const u32x4_t* xv = reinterpret_cast<const u32x4_t*>(xr);
+          float xn = 0.f;
+#pragma unroll 4
+          for (int q = 0; q < D / 8; ++q) {
+            const u32x4_t v = xv[q];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float a0 = bf16_lo(v[e]), a1 = bf16_hi(v[e]);
               xn = fmaf(a0, a0, fmaf(a1, a1, xn));
             }
-            XN[tok] = xn;
           }
-        } else {
-          d2 = D2[tok];
-          const int a = A[tok];
-          if (!(s_cc[a] >= 4.0 * d2 * (1.0 + 0x1p-20))) {
-            bool need = true;
-            if (kBF16) {
-              const float xn = XN[tok];
-              // |approx - ||x - c||^2| <= D 2^-24 (xn + cn) plus the rounding
-              // of xn, cn and the two additions: below 2e-5 (xn + cn) at D = 128
-              const float approx =
-                  xn + cn - 2.f * dot_bf16_f32<D>(reinterpret_cast<const uint16_t*>(xr), s_c);
-              need = approx <= (float)d2 + 5e-5f * (xn + cn) + 1e-30f;
-            }
-            if (need) {
-              const double nd = ExactDist<T, D>::run(xr, s_cd);
-              if (nd < d2) {
-                d2 = nd;
-                D2[tok] = nd;
-                A[tok] = k;
-              }
-            }
-          }
+          XN[tok] = xn;
         }
       }
-      const double inc = wave_inclusive_scan(d2);
-      if (lane == kWave - 1) s_bsum[b] = inc;
     }
-    if (tid == 0) {
-      s_blk = INT_MAX;
-      s_last = -1;
-    }
-    __syncthreads();
-
-    // ---- sample pick k+1: smallest token whose running D2 sum exceeds u*total
-    const int per = (nblk + kSeedThreads - 1) / kSeedThreads;
-    const int b0 = min(tid * per, nblk), b1 = min(b0 + per, nblk);
-    double loc = 0.0;
-    for (int b = b0; b < b1; ++b) loc += s_bsum[b];
-    double total;
-    const double excl = block_exclusive_scan(loc, s_red, &total);
-    const double u = seed_uniform(seed, p, k + 1);
-    const double target = u * total;
-    int found = INT_MAX;
-    double resid = 0.0;
-    if (total > 0.0) {
-      double run = excl;
-      for (int b = b0; b < b1; ++b) {
-        const double nxt = run + s_bsum[b];
-        if (found == INT_MAX && run <= target && target < nxt) {
-          found = b;
-          resid = target - run;
-        }
-        run = nxt;
-      }
-      if (found != INT_MAX) atomicMin(&s_blk, found);
-      // last block with mass (fallback when rounding leaves no block above target)
-      for (int b = b1 - 1; b >= b0; --b)
-        if (s_bsum[b] > 0.0) {
-          atomicMax(&s_last, b);
-          break;
-        }
-    }
-    __syncthreads();
-    if (found != INT_MAX && found == s_blk) s_resid = resid;
-    __syncthreads();
-    if (wave == 0) {
-      int pick;
-      if (!(total > 0.0)) {
-        pick = min((int)(u * (double)N), N - 1);
+  } else {
+    const double* cc = ccg + (size_t)p * n;
+    int a[kSeedTPL];
+    float xn[kSeedTPL];
+    // 16-byte state loads need every problem's arrays 16-byte aligned
+    if ((N % kSeedTPL) == 0 && t0 + kSeedTPL <= N) {
+      const double2 d01 = *reinterpret_cast<const double2*>(D2 + t0);
+      const double2 d23 = *reinterpret_cast<const double2*>(D2 + t0 + 2);
+      const int4 av = *reinterpret_cast<const int4*>(A + t0);
+      d2[0] = d01.x; d2[1] = d01.y; d2[2] = d23.x; d2[3] = d23.y;
+      a[0] = av.x; a[1] = av.y; a[2] = av.z; a[3] = av.w;
+      if (kBF16) {
+        const float4 xv = *reinterpret_cast<const float4*>(XN + t0);
+        xn[0] = xv.x; xn[1] = xv.y; xn[2] = xv.z; xn[3] = xv.w;
       } else {
-        int b = s_blk;
-        bool exact = true;
-        if (b == INT_MAX) {
-          b = s_last;
-          exact = false;
-        }
-        b = clampi(b, 0, nblk - 1);
-        const int tok = b * kWave + lane;
-        const double v = tok < N ? D2[tok] : 0.0;
-        const double inc = wave_inclusive_scan(v);
-        const uint64_t above = exact ? __ballot(inc > s_resid) : 0ull;
-        if (above) {
-          pick = b * kWave + __ffsll((unsigned long long)above) - 1;
-        } else {
-          const uint64_t pos = __ballot(v > 0.0);
-          pick = b * kWave + (63 - __clzll((long long)pos));
-        }
+        xn[0] = xn[1] = xn[2] = xn[3] = 0.f;
       }
-      if (lane == 0) s_pick = clampi(pick, 0, N - 1);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kSeedTPL; ++i) {
+        const bool ok = t0 + i < N;
+        d2[i] = ok ? D2[t0 + i] : 0.0;
+        a[i] = ok ? clampi(A[t0 + i], 0, k - 1) : 0;
+        xn[i] = (ok && kBF16) ? XN[t0 + i] : 0.f;
+      }
     }
-    __syncthreads();
+#pragma unroll 1
+    for (int i = 0; i < kSeedTPL; ++i) {
+      const int tok = t0 + i;
+      if (tok < N &&
+          seed_lowers<T, D>(Xp + (size_t)tok * D, s_cd, s_c, cn, xn[i], cc[clampi(a[i], 0, k - 1)], d2[i])) {
+        D2[tok] = d2[i];
+        A[tok] = k;
+      }
+    }
+  }
+  const double lsum = ((d2[0] + d2[1]) + d2[2]) + d2[3];
+  const double inc = wave_inclusive_scan(lsum);
+  if (lane == kWave - 1) bsum[(size_t)p * nblk + b] = inc;
+}
+
+// Pick k+1 of problem blockIdx.x: the smallest token whose running D2 sum
+// exceeds u_{k+1} * sum D2 (block sums, then the 256 tokens of the block).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_seed_sample(const T* __restrict__ X, int N, int n, int k,
+                                                     uint64_t seed, const double* __restrict__ D2g,
+                                                     const double* __restrict__ bsum,
+                                                     int32_t* __restrict__ picks, double* __restrict__ ccg,
+                                                     float* __restrict__ C0, int32_t* __restrict__ seed_index) {
+  __shared__ double s_red[17];
+  __shared__ double s_cd[D];
+  __shared__ int s_blk, s_last, s_pick;
+  __shared__ double s_resid;
+  const int p = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const T* Xp = X + (size_t)p * N * D;
+  const double* D2 = D2g + (size_t)p * N;
+  const double* bs = bsum + (size_t)p * ((N + kSeedBlk - 1) / kSeedBlk);
+  const int nblk = (N + kSeedBlk - 1) / kSeedBlk;
+  if (tid == 0) {
+    s_blk = INT_MAX;
+    s_last = -1;
+  }
+  const int per = (nblk + 255) / 256;
+  const int b0 = min(tid * per, nblk), b1 = min(b0 + per, nblk);
+  double loc = 0.0;
+  for (int b = b0; b < b1; ++b) loc += bs[b];
+  double total;
+  const double excl = block_exclusive_scan(loc, s_red, &total);
+  const double u = seed_uniform(seed, p, k + 1);
+  const double target = u * total;
+  int found = INT_MAX;
+  double resid = 0.0;
+  if (total > 0.0) {
+    double run = excl;
+    for (int b = b0; b < b1; ++b) {
+      const double nxt = run + bs[b];
+      if (found == INT_MAX && run <= target && target < nxt) {
+        found = b;
+        resid = target - run;
+      }
+      run = nxt;
+    }
+    if (found != INT_MAX) atomicMin(&s_blk, found);
+    for (int b = b1 - 1; b >= b0; --b)
+      if (bs[b] > 0.0) {
+        atomicMax(&s_last, b);
+        break;
+      }
+  }
+  __syncthreads();
+  if (found != INT_MAX && found == s_blk) s_resid = resid;
+  __syncthreads();
+  if (wave == 0) {
+    int pick;
+    if (!(total > 0.0)) {
+      pick = min((int)(u * (double)N), N - 1);
+    } else {
+      int b = s_blk;
+      bool exact = true;
+      if (b == INT_MAX) {
+        b = s_last;
+        exact = false;
+      }
+      b = clampi(b, 0, nblk - 1);
+      const int t0 = b * kSeedBlk + kSeedTPL * lane;
+      double d2[kSeedTPL];
+#pragma unroll
+      for (int i = 0; i < kSeedTPL; ++i) d2[i] = t0 + i < N ? D2[t0 + i] : 0.0;
+      const double lsum = ((d2[0] + d2[1]) + d2[2]) + d2[3];
+      const double inc = wave_inclusive_scan(lsum);
+      const double before = __shfl_up(inc, 1);
+      const double resid_b = s_resid;
+      const uint64_t above = exact ? __ballot(inc > resid_b) : 0ull;
+      int owner;
+      if (above) {
+        owner = __ffsll((unsigned long long)above) - 1;
+      } else {
+        const uint64_t pos = __ballot(lsum > 0.0);
+        owner = pos ? 63 - __clzll((long long)pos) : 0;
+      }
+      int cand = -1, last_pos = -1;
+      double run = lane == 0 ? 0.0 : before;
+#pragma unroll
+      for (int i = 0; i < kSeedTPL; ++i) {
+        run += d2[i];
+        if (d2[i] > 0.0) last_pos = t0 + i;
+        if (cand < 0 && above && run > resid_b) cand = t0 + i;
+      }
+      if (cand < 0) cand = last_pos;
+      pick = __shfl(cand, owner);
+    }
+    if (lane == 0) s_pick = clampi(pick, 0, N - 1);
+  }
+  __syncthreads();
+  const int t = s_pick;
+  for (int e = tid; e < D; e += 256) {
+    const float v = Elem<T>::get(Xp, (size_t)t * D + e);
+    s_cd[e] = (double)v;
+    C0[((size_t)p * n + k + 1) * D + e] = v;
+  }
+  if (tid == 0) {
+    picks[(size_t)p * n + k + 1] = t;
+    if (seed_index) seed_index[(size_t)p * n + k + 1] = t;
+  }
+  __syncthreads();
+  // distances from the new pick to picks 0..k, for the next update's skip test
+  for (int a = tid; a <= k; a += 256) {
+    const int ta = clampi(picks[(size_t)p * n + a], 0, N - 1);
+    ccg[(size_t)p * n + a] = ExactDist<T, D>::run(Xp + (size_t)ta * D, s_cd);
   }
 }
 
 hipError_t launch_kmeanspp(const void* x, bool bf16, int bh, int N, int d, int n, uint64_t seed,
                            double* d2_ws, int32_t* near_ws, float* centroids, int32_t* seed_index,
-                           hipStream_t s) {
+                           int32_t* picks_ws, double* cc_ws, double* bsum_ws, hipStream_t s) {
   float* xn_ws = reinterpret_cast<float*>(near_ws + (size_t)bh * N);
-#define SVG2_SEED(T, D)                                                                         \
-  hipLaunchKernelGGL((k_kmeanspp<T, D>), dim3(bh), dim3(kSeedThreads), 0, s,                  \
-                     static_cast<const T*>(x), N, n, seed, d2_ws, near_ws, xn_ws, centroids, \
-                     seed_index)
+  const int nblk = (N + kSeedBlk - 1) / kSeedBlk;
+  const dim3 ug((nblk + kSeedWavesPerWG - 1) / kSeedWavesPerWG, bh);
+#define SVG2_SEED(T, D)                                                                                   \
+  for (int k = 0; k < n; ++k) {                                                                         \
+    hipLaunchKernelGGL((k_seed_update<T, D>), ug, dim3(256), 0, s, static_cast<const T*>(x), N, n, k,   \
+                       seed, d2_ws, near_ws, xn_ws, picks_ws, cc_ws, bsum_ws, centroids, seed_index);   \
+    if (k + 1 < n)                                                                                      \
+      hipLaunchKernelGGL((k_seed_sample<T, D>), dim3(bh), dim3(256), 0, s, static_cast<const T*>(x), N, \
+                         n, k, seed, d2_ws, bsum_ws, picks_ws, cc_ws, centroids, seed_index);           \
+  }
   if (bf16) {
-    if (d == 128) SVG2_SEED(uint16_t, 128); else SVG2_SEED(uint16_t, 64);
+    if (d == 128) { SVG2_SEED(uint16_t, 128) } else { SVG2_SEED(uint16_t, 64) }
   } else {
-    if (d == 128) SVG2_SEED(float, 128); else SVG2_SEED(float, 64);
+    if (d == 128) { SVG2_SEED(float, 128) } else { SVG2_SEED(float, 64) }
   }
 #undef SVG2_SEED
   return hipGetLastError();

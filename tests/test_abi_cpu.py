@@ -58,7 +58,7 @@ def _km(**kw):
     (dict(bh=0), INVALID), (dict(N=0), INVALID), (dict(n=0), INVALID), (dict(n=1001), INVALID),
     (dict(n=4097, N=10000), INVALID), (dict(d=96), UNSUPPORTED), (dict(iters=-1), INVALID),
     (dict(iters=101), INVALID), (dict(cent=None), INVALID), (dict(lab=None), INVALID),
-    (dict(cnt=None), INVALID), (dict(N=300000), UNSUPPORTED), (dict(wsn=10), WORKSPACE),
+    (dict(cnt=None), INVALID), (dict(N=1 << 25), INVALID), (dict(wsn=10), WORKSPACE),
     (dict(ws=None), WORKSPACE), (dict(init=MISALIGNED), INVALID), (dict(lab=FAKE + 2), INVALID),
 ])
 def test_kmeans_validation(kw, code):
