@@ -71,10 +71,30 @@ struct KeyCursor {
     sel = s; koff = ko; nsel = ns; n_k = nk; N = n;
     next = 0; pos = 0; rem = 0;
   }
+  __device__ __forceinline__ void open_ranges() {
+    while (rem == 0 && next < nsel) {
+      const int j = sel[next++];
+      if ((unsigned)j >= (unsigned)n_k) continue;
+      const int a = clampi(koff[j], 0, N);
+      pos = a;
+      rem = clampi(koff[j + 1], a, N) - a;
+    }
+  }
   // Fills up to `tile` keys; slot_of[e] (this thread's slots) get key indices
-  // or -1.  Returns the number of keys in the tile.
+  // or -1.  Returns the number of keys in the tile; *contiguous tells that the
+  // tile is full and inside one key range (key = first key + slot).
   template <int NS>
-  __device__ __forceinline__ int fill(int tile, const int (&slot_of)[NS], int (&key)[NS]) {
+  __device__ __forceinline__ int fill(int tile, const int (&slot_of)[NS], int (&key)[NS], bool* contiguous) {
+    open_ranges();
+    if (rem >= tile) {
+#pragma unroll
+      for (int e = 0; e < NS; ++e) key[e] = slot_of[e] >= 0 ? pos + slot_of[e] : -1;
+      pos += tile;
+      rem -= tile;
+      *contiguous = true;
+      return tile;
+    }
+    *contiguous = false;
 #pragma unroll
     for (int e = 0; e < NS; ++e) key[e] = -1;
     int filled = 0;
@@ -110,10 +130,10 @@ struct KeyCursor {
 // softmax; only the intermediate scaling differs.
 constexpr float kLazyTau = 8.f;
 
-template <int D>
-struct AttnTileRegs {
-  u32x4_t r[8];
-};
+// Work items are taken in an order that keeps consecutive items (same
+// Q-cluster, same head) on one XCD: work-groups are dispatched round-robin
+// over the 8 XCDs, so block b runs item (b % 8) * per_xcd + b / 8.
+constexpr int kXcds = 8;
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void k_attn_bf16(
@@ -121,7 +141,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
     int N, const int32_t* __restrict__ q_off, int n_q, const int32_t* __restrict__ k_off, int n_k,
     const int32_t* __restrict__ sel_count, const int32_t* __restrict__ sel_idx, float scale_log2,
     uint16_t* __restrict__ O, float* __restrict__ lse, const int32_t* __restrict__ item_count,
-    const int32_t* __restrict__ items, int max_items) {
+    const int32_t* __restrict__ items, int max_items, int bh) {
   constexpr int BN = kAttnBN;
   constexpr int KS = D / 16;           // 16-wide k-steps of Q.K
   constexpr int DT = D / 32;           // 32-row tiles of O^T
@@ -131,18 +151,24 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
   constexpr int VUNITS = (BN / 8) * VPR;        // 8x8 transpose blocks of V
   constexpr int KUNITS = BN * VPR / 8;          // 8-vector groups of K
   static_assert(VUNITS + KUNITS <= 256, "one load unit per thread");
-  __shared__ __attribute__((aligned(16))) uint16_t sK[BN * KLD];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[D * VLD];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * KLD];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * VLD];
 
-  const int p = blockIdx.y;
-  if ((int)blockIdx.x >= item_count[p]) return;
-  const int item = items[(size_t)p * max_items + blockIdx.x];
+  const int total = max_items * bh;
+  const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int logical = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+  if (logical >= total) return;
+  const int p = logical / max_items, slot = logical % max_items;
+  if (slot >= item_count[p]) return;
+  const int item = items[(size_t)p * max_items + slot];
   const int ci = item & 0xfff, rb = item >> 12;
   const int32_t* qo = q_off + (size_t)p * (n_q + 1);
   const int qa = clampi(qo[ci], 0, N), qb = clampi(qo[ci + 1], qa, N);
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
   const int col = lane & 31, half = lane >> 5;
-  const int row = qa + rb * kAttnBM + wave * 32 + col;
+  const int row0 = qa + rb * kAttnBM + wave * 32;
+  const bool active = row0 < qb;                 // this wave has query rows
+  const int row = row0 + col;
   const bool row_ok = row < qb;
   const size_t base = (size_t)p * N * D;
 
@@ -173,144 +199,153 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
       slot_of[e] = -1;
     }
   }
-  const uint16_t* src = is_v ? V + base + vc * 8 : K + base;
+  // element offset of this thread's vector inside a key row
+  const int vec_off = is_v ? vc * 8 : (ku % VPR) * 8;
+  const uint16_t* src = (is_v ? V : K) + base + vec_off;
 
   KeyCursor cur;
-  {
-    int ns = sel_count[(size_t)p * n_q + ci];
-    ns = clampi(ns, 0, n_k);
-    cur.init(sel_idx + ((size_t)p * n_q + ci) * n_k, k_off + (size_t)p * (n_k + 1), ns, n_k, N);
-  }
+  cur.init(sel_idx + ((size_t)p * n_q + ci) * n_k, k_off + (size_t)p * (n_k + 1),
+           clampi(sel_count[(size_t)p * n_q + ci], 0, n_k), n_k, N);
 
-  // global -> registers for the tile whose keys are `key`
-  auto load_tile = [&](const int (&key)[8], AttnTileRegs<D>& t) {
+  u32x4_t rg[8];
+  auto load_tile = [&](const int (&key)[8], bool contiguous) {
+    if (!(is_v || is_k)) return;
+    if (contiguous) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      t.r[e] = u32x4_t{0u, 0u, 0u, 0u};
-      if (key[e] >= 0) {
-        const size_t off = is_v ? (size_t)key[e] * D : (size_t)key[e] * D + ((ku + KUNITS * e) % VPR) * 8;
-        if (is_v || is_k) t.r[e] = *reinterpret_cast<const u32x4_t*>(src + off);
+      for (int e = 0; e < 8; ++e) rg[e] = *reinterpret_cast<const u32x4_t*>(src + (size_t)key[e] * D);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        rg[e] = u32x4_t{0u, 0u, 0u, 0u};
+        if (key[e] >= 0) rg[e] = *reinterpret_cast<const u32x4_t*>(src + (size_t)key[e] * D);
       }
     }
   };
-  // registers -> LDS (V transposed into the permuted key order)
-  auto store_tile = [&](const AttnTileRegs<D>& t) {
+  // registers -> LDS buffer (V transposed into the permuted key order)
+  auto store_tile = [&](int buf) {
     if (is_v) {
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
         const uint32_t sel = (x & 1) ? 0x07060302u : 0x05040100u;
         u32x4_t w;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) w[q] = __builtin_amdgcn_perm(t.r[2 * q + 1][x >> 1], t.r[2 * q][x >> 1], sel);
+        for (int q = 0; q < 4; ++q) w[q] = __builtin_amdgcn_perm(rg[2 * q + 1][x >> 1], rg[2 * q][x >> 1], sel);
         const int d = vc * 8 + x;
-        const int blk = vg ^ ((d >> 3) & 7);
-        *reinterpret_cast<u32x4_t*>(&sV[d * VLD + blk * 8]) = w;
+        *reinterpret_cast<u32x4_t*>(&sV[buf][d * VLD + (vg ^ ((d >> 4) & 7)) * 8]) = w;
       }
     } else if (is_k) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int v = ku + KUNITS * e;
-        *reinterpret_cast<u32x4_t*>(&sK[(v / VPR) * KLD + (v % VPR) * 8]) = t.r[e];
+        *reinterpret_cast<u32x4_t*>(&sK[buf][(v / VPR) * KLD + (v % VPR) * 8]) = rg[e];
       }
     }
   };
 
   float m_ref = -__builtin_inff();
-  float l_run = 0.f;
-  f32x16_t o[DT];
+  f32x16_t o[DT], lsum;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) lsum[i] = 0.f;
+  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
 
-  AttnTileRegs<D> regs;
   int key[8];
-  int filled = cur.fill<8>(BN, slot_of, key);
+  bool contiguous;
+  int filled = cur.fill<8>(BN, slot_of, key, &contiguous);
   if (filled > 0) {
-    load_tile(key, regs);
-    store_tile(regs);
+    load_tile(key, contiguous);
+    store_tile(0);
   }
   __syncthreads();
 
+  int buf = 0;
   while (filled > 0) {
     // prefetch the next tile while this one is computed
-    const int next_filled = cur.fill<8>(BN, slot_of, key);
-    if (next_filled > 0) load_tile(key, regs);
+    bool next_contig;
+    const int next_filled = cur.fill<8>(BN, slot_of, key, &next_contig);
+    if (next_filled > 0) load_tile(key, next_contig);
 
-    // ---- S^T = K Q^T for 2 sub-tiles of 32 keys
-    f32x16_t s[2];
+    if (active) {
+      const uint16_t* kb = sK[buf];
+      const uint16_t* vb = sV[buf];
+      // ---- S^T = K Q^T for 2 sub-tiles of 32 keys
+      f32x16_t s[2];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
+      for (int st = 0; st < 2; ++st) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[st][i] = 0.f;
+        for (int i = 0; i < 16; ++i) s[st][i] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&sK[(st * 32 + col) * KLD + ks * 16 + half * 8]);
-        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[st], 0, 0, 0);
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&kb[(st * 32 + col) * KLD + ks * 16 + half * 8]);
+          s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[st], 0, 0, 0);
+        }
       }
-    }
-    // ---- online softmax; lane holds keys st*32 + (i/4)*8 + half*4 + i%4
-    if (filled < BN) {
+      // ---- online softmax; lane holds keys st*32 + (i/4)*8 + half*4 + i%4
+      if (filled < BN) {
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int ks = st * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+            if (ks >= filled) s[st][i] = -__builtin_inff();
+          }
+      }
+      float mx = s[0][0];
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int ks = st * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-          if (ks >= filled) s[st][i] = -__builtin_inff();
-        }
-    }
-    float mx = s[0][0];
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[st][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
-    if (mx > m_ref + kLazyTau) {
-      const float alpha = __builtin_amdgcn_exp2f(m_ref - mx);
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
-      m_ref = mx;
-    }
-    const float neg = -m_ref;
-    float rs = 0.f;
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(s[st][i], scale_log2, neg));
-        s[st][i] = e;
-        rs += e;
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[st][i]);
+      {
+        // lanes i and i+32 hold the same query: combine their maxima
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
       }
-    l_run += rs;
+      if (mx > m_ref + kLazyTau) {
+        const float alpha = __builtin_amdgcn_exp2f(m_ref - mx);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) lsum[i] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+        m_ref = mx;
+      }
+      const float neg = -m_ref;
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[st][i] = __builtin_amdgcn_exp2f(fmaf(s[st][i], scale_log2, neg));
 
-    // ---- O^T += V^T P^T, 4 k-steps of 16 keys
+      // ---- O^T += V^T P^T, 4 k-steps of 16 keys
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int st = kk >> 1, sub = kk & 1;
-      u32x4_t pw;
+      for (int kk = 0; kk < 4; ++kk) {
+        const int st = kk >> 1, sub = kk & 1;
+        u32x4_t pw;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) pw[q] = pack_bf16x2(s[st][8 * sub + 2 * q], s[st][8 * sub + 2 * q + 1]);
-      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
-      const int blk = 2 * kk + half;
+        for (int q = 0; q < 4; ++q) pw[q] = pack_bf16x2(s[st][8 * sub + 2 * q], s[st][8 * sub + 2 * q + 1]);
+        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
+        const int blk = 2 * kk + half;
+        // row sums of the bf16 P on the matrix core: an all-ones A operand
+        lsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb, lsum, 0, 0, 0);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int d = dt * 32 + col;
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&sV[d * VLD + ((blk ^ ((d >> 3) & 7)) * 8)]);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[dt], 0, 0, 0);
+        for (int dt = 0; dt < DT; ++dt) {
+          const int d = dt * 32 + col;
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&vb[d * VLD + ((blk ^ ((d >> 4) & 7)) * 8)]);
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[dt], 0, 0, 0);
+        }
       }
     }
-    __syncthreads();                       // every wave is done with this tile
-    if (next_filled > 0) {
-      store_tile(regs);
-      __syncthreads();
-    }
+    if (next_filled > 0) store_tile(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
     filled = next_filled;
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  // every row of the ones-product holds the sum over all keys of the tile
+  const float l_tot = lsum[0];
   if (row_ok) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     uint16_t* orow = O + base + (size_t)row * D;
@@ -371,7 +406,8 @@ __global__ __launch_bounds__(128) void k_attn_f32(
   float m_run = -__builtin_inff(), l_run = 0.f;
   for (;;) {
     int key[PER];
-    const int filled = cur.fill<PER>(BN, slot_of, key);
+    bool contiguous;
+    const int filled = cur.fill<PER>(BN, slot_of, key, &contiguous);
     if (filled == 0) break;
     __syncthreads();
 #pragma unroll
@@ -414,13 +450,15 @@ hipError_t launch_varblock_attn(const void* q, const void* k, const void* v, boo
   hipLaunchKernelGGL(k_attn_plan, dim3(bh), dim3(1024), 0, s, q_off, n_q, N, bm, max_items, item_count_ws,
                      items_ws);
   const dim3 grid(max_items, bh);
+  const int total = max_items * bh;
+  const dim3 grid_x((total + kXcds - 1) / kXcds * kXcds);
   if (bf16) {
     const float sl2 = scale * 1.4426950408889634f;
 #define SVG2_ATTN(D)                                                                                  \
-  hipLaunchKernelGGL(k_attn_bf16<D>, grid, dim3(256), 0, s, static_cast<const uint16_t*>(q),          \
+  hipLaunchKernelGGL(k_attn_bf16<D>, grid_x, dim3(256), 0, s, static_cast<const uint16_t*>(q),        \
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), N, q_off, n_q, \
                      k_off, n_k, sel_count, sel_idx, sl2, static_cast<uint16_t*>(out), lse,          \
-                     item_count_ws, items_ws, max_items)
+                     item_count_ws, items_ws, max_items, bh)
     if (d == 128) SVG2_ATTN(128); else SVG2_ATTN(64);
 #undef SVG2_ATTN
   } else {

@@ -22,8 +22,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   __bf16 h = (__bf16)f;
   return __builtin_bit_cast(uint16_t, h);
 }
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// two floats -> two bf16 (RNE) in one word: one v_cvt_pk_bf16_f32
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+  const f32x2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
 // element loaders: T is float or uint16_t (bf16 storage)

@@ -186,7 +186,9 @@ def test_varblock_attn_vs_oracle(dt, d, N, n_q, n_k, top_p):
         assert rel_l2(got, ref) <= tol[1]
         gl = lse[h].cpu().numpy().astype(np.float64)
         fin = np.isfinite(ref_lse)
-        np.testing.assert_allclose(gl[fin], ref_lse[fin], rtol=0, atol=1e-3 if dt == "bf16" else 1e-4)
+        # bf16: the normaliser sums the bf16-rounded probabilities (relative
+        # error <= 2^-9 each), so the log of the sum may move by up to 2^-9
+        np.testing.assert_allclose(gl[fin], ref_lse[fin], rtol=0, atol=2.5e-3 if dt == "bf16" else 1e-4)
         assert np.all(gl[~fin] == -np.inf) and np.all(got[~fin] == 0)
 
 
