@@ -44,7 +44,42 @@ def parse():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work in the CPU leg")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (counter calibration)")
     return ap.parse_args()
+
+
+ATTN_SOURCE = os.path.join(ROOT, "sparse_attention_video_head_amd", "csrc", "attn.hip")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "k_attn_bf16_hunyuan720p_counters.md")
+
+
+def attn_traffic_per_launch():
+    """HBM bytes per attention launch from the committed counter summary, if it
+    was taken on the attention source as it is now (else None)."""
+    import hashlib
+    try:
+        sha = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()[:16]
+        fields = {}
+        for line in open(TRAFFIC_PROFILE):
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip()
+        if fields.get("attn.hip sha256[:16]") != sha:
+            return None
+        return float(fields["calibrated HBM bytes per launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def copy_calibration(mib: int):
+    import torch
+    n = mib * (1 << 20) // 2
+    src = torch.empty(n, dtype=torch.bfloat16, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": 2 * n, "copy_bytes_written": 2 * n, "launches": 3}), flush=True)
 
 
 def cpu_baseline(host, cfg, top_p, budget_s):
@@ -117,6 +152,9 @@ def cpu_baseline(host, cfg, top_p, budget_s):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path shards by head with no "
               "exchange and is not run on several GPUs here.", file=sys.stderr)
@@ -240,6 +278,11 @@ def main():
     value = attn_flops / (cold_ms * 1e-3) / 1e12
     dense_flops = 4.0 * cfg.head_dim * cfg.bh * float(cfg.n_tokens) ** 2
 
+    e = 2 if cfg.dtype == "bf16" else 4
+    N, d, bhn = cfg.n_tokens, cfg.head_dim, cfg.bh
+    permute_bytes = bhn * (6.0 * N * d * e + 8.0 * N)      # Q, K, V read + written, labels, perm
+    unpermute_bytes = bhn * (2.0 * N * d * e + 4.0 * N)
+    traffic = attn_traffic_per_launch()
     res = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -271,9 +314,11 @@ def main():
         "dense_tflops": round(dense_flops / (dense_ms * 1e-3) / 1e12, 2) if dense_ms else None,
         "speedup_vs_dense_cold": round(dense_ms / cold_ms, 3) if dense_ms else None,
         "speedup_vs_dense_warm": round(dense_ms / warm_ms, 3) if dense_ms else None,
+        "permute_gbps": round(permute_bytes / (cold_stage[1] * 1e-3) / 1e9, 1),
+        "unpermute_gbps": round(unpermute_bytes / (cold_stage[4] * 1e-3) / 1e9, 1),
         "roofline": {"bound": "mfma", "kernel": "k_attn_bf16" if cfg.dtype == "bf16" else "k_attn_f32",
                      "achieved": round(attn_tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(attn_tflops / peak, 4), "traffic": None,
+                     "frac": round(attn_tflops / peak, 4), "traffic": traffic,
                      "flops_per_launch": attn_flops},
     }
     if not args.no_cpu_baseline:
