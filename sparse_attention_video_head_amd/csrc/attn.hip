@@ -135,6 +135,53 @@ constexpr float kLazyTau = 8.f;
 // over the 8 XCDs, so block b runs item (b % 8) * per_xcd + b / 8.
 constexpr int kXcds = 8;
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+template <typename Tp>
+__device__ __forceinline__ lds_u16_t* to_lds(Tp* p) {
+  return (lds_u16_t*)(lds_void_t*)(void*)p;
+}
+
+// K and V tiles sit row-major in LDS, 64 keys x D, with the 16-byte chunks of
+// each row XOR-swizzled (no padding, so they can be filled by direct
+// global -> LDS loads):
+//   K: chunk c of row r at c ^ (r % 16)      (conflict-free 16-byte reads of
+//      one chunk across 16 consecutive rows)
+//   V: chunk c of row r at c ^ 2 (r % 4)      (conflict-free transposing reads
+//      of 4 rows x 32 bytes)
+template <int D> struct TileGeom {
+  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  static __device__ __forceinline__ int k_chunk(int r, int c) { return c ^ (r & (CPR - 1) & 15); }
+  static __device__ __forceinline__ int v_chunk(int r, int c) { return c ^ (2 * (r & 3)); }
+};
+
+// One tile = 64 rows.  Each wave fills 16 rows of K and of V with 4 + 4
+// direct-to-LDS loads of 16 bytes per lane (lane -> row 4q + lane/16, slot
+// lane%16 of the row); rows past the key list load key 0 (never weighted:
+// their scores are masked to -inf).
+template <int D>
+__device__ __forceinline__ void dma_tile(const uint16_t* Kp, const uint16_t* Vp, lds_u16_t* sk, lds_u16_t* sv,
+                                         const int (&key)[4], int wave, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int RPI = kWave / CPR;                  // rows per instruction (4 at D=128)
+  constexpr int INS = 16 / RPI;                     // instructions per 16 rows
+#pragma unroll
+  for (int q = 0; q < INS; ++q) {
+    const int r = 16 * wave + RPI * q + lane / CPR;
+    const int phys = lane % CPR;
+    const size_t krow = (size_t)max(key[q], 0) * D;
+    const uint16_t* ksrc = Kp + krow + TileGeom<D>::k_chunk(r, phys) * 8;
+    const uint16_t* vsrc = Vp + krow + TileGeom<D>::v_chunk(r, phys) * 8;
+    lds_u16_t* kdst = sk + (16 * wave + RPI * q) * D;
+    lds_u16_t* vdst = sv + (16 * wave + RPI * q) * D;
+    __builtin_amdgcn_global_load_lds((const void*)ksrc, (lds_void_t*)kdst, 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)vsrc, (lds_void_t*)vdst, 16, 0, 0);
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void k_attn_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
@@ -145,14 +192,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
   constexpr int BN = kAttnBN;
   constexpr int KS = D / 16;           // 16-wide k-steps of Q.K
   constexpr int DT = D / 32;           // 32-row tiles of O^T
-  constexpr int KLD = D + 8;           // K tile row stride (elements)
-  constexpr int VLD = BN + 8;          // V^T tile row stride (elements)
-  constexpr int VPR = D / 8;           // 16-byte vectors per row
-  constexpr int VUNITS = (BN / 8) * VPR;        // 8x8 transpose blocks of V
-  constexpr int KUNITS = BN * VPR / 8;          // 8-vector groups of K
-  static_assert(VUNITS + KUNITS <= 256, "one load unit per thread");
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][BN * KLD];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * VLD];
+  constexpr int CPR = D / 8;
+  constexpr int RPI = kWave / CPR;
+  constexpr int INS = 16 / RPI;
+  static_assert(INS <= 4, "key slots per lane");
+  __shared__ __attribute__((aligned(16))) uint16_t sK0[BN * D], sK1[BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sV0[BN * D], sV1[BN * D];
 
   const int total = max_items * bh;
   const int per_xcd = (total + kXcds - 1) / kXcds;
@@ -171,6 +216,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
   const int row = row0 + col;
   const bool row_ok = row < qb;
   const size_t base = (size_t)p * N * D;
+  const uint16_t* Kp = K + base;
+  const uint16_t* Vp = V + base;
 
   bf16x8_t qf[KS];
 #pragma unroll
@@ -180,67 +227,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
     qf[ks] = __builtin_bit_cast(bf16x8_t, v);
   }
 
-  // this thread's load unit: a V transpose block (key group g, column chunk c)
-  // or a group of 8 K vectors
-  const bool is_v = tid < VUNITS;
-  const bool is_k = !is_v && tid < VUNITS + KUNITS;
-  const int vc = tid % VPR, vg = tid / VPR;
-  const int ku = tid - VUNITS;
-  int slot_of[8];
+  // this lane's tile rows (one per direct-to-LDS load)
+  int slot_of[4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    if (is_v) {
-      // group g = (kk, h) holds keys 16kk + 4h + {0..3} and 16kk + 8 + 4h + {0..3}
-      const int kk = vg >> 1, h = vg & 1;
-      slot_of[e] = 16 * kk + 8 * (e >> 2) + 4 * h + (e & 3);
-    } else if (is_k) {
-      slot_of[e] = (ku + KUNITS * e) / VPR;
-    } else {
-      slot_of[e] = -1;
-    }
-  }
-  // element offset of this thread's vector inside a key row
-  const int vec_off = is_v ? vc * 8 : (ku % VPR) * 8;
-  const uint16_t* src = (is_v ? V : K) + base + vec_off;
+  for (int q = 0; q < 4; ++q) slot_of[q] = q < INS ? 16 * wave + RPI * q + lane / CPR : -1;
 
   KeyCursor cur;
   cur.init(sel_idx + ((size_t)p * n_q + ci) * n_k, k_off + (size_t)p * (n_k + 1),
            clampi(sel_count[(size_t)p * n_q + ci], 0, n_k), n_k, N);
-
-  u32x4_t rg[8];
-  auto load_tile = [&](const int (&key)[8], bool contiguous) {
-    if (!(is_v || is_k)) return;
-    if (contiguous) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) rg[e] = *reinterpret_cast<const u32x4_t*>(src + (size_t)key[e] * D);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        rg[e] = u32x4_t{0u, 0u, 0u, 0u};
-        if (key[e] >= 0) rg[e] = *reinterpret_cast<const u32x4_t*>(src + (size_t)key[e] * D);
-      }
-    }
-  };
-  // registers -> LDS buffer (V transposed into the permuted key order)
-  auto store_tile = [&](int buf) {
-    if (is_v) {
-#pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        const uint32_t sel = (x & 1) ? 0x07060302u : 0x05040100u;
-        u32x4_t w;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) w[q] = __builtin_amdgcn_perm(rg[2 * q + 1][x >> 1], rg[2 * q][x >> 1], sel);
-        const int d = vc * 8 + x;
-        *reinterpret_cast<u32x4_t*>(&sV[buf][d * VLD + (vg ^ ((d >> 4) & 7)) * 8]) = w;
-      }
-    } else if (is_k) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int v = ku + KUNITS * e;
-        *reinterpret_cast<u32x4_t*>(&sK[buf][(v / VPR) * KLD + (v % VPR) * 8]) = rg[e];
-      }
-    }
-  };
 
   float m_ref = -__builtin_inff();
   f32x16_t o[DT], lsum;
@@ -252,99 +246,118 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
   for (int i = 0; i < 16; ++i) lsum[i] = 0.f;
   const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
 
-  int key[8];
-  bool contiguous;
-  int filled = cur.fill<8>(BN, slot_of, key, &contiguous);
-  if (filled > 0) {
-    load_tile(key, contiguous);
-    store_tile(0);
-  }
-  __syncthreads();
+  // per-lane LDS offsets (elements) of this lane's operand reads
+  // K (S^T = K Q^T): row st*32 + col, chunk 2 ks + half
+  // V^T (transposing read): rows kb + (lane%16)/4, columns d0 + 4 (lane%4)
+  const int vr = (lane & 15) >> 2;
+  const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-  int buf = 0;
-  while (filled > 0) {
-    // prefetch the next tile while this one is computed
-    bool next_contig;
-    const int next_filled = cur.fill<8>(BN, slot_of, key, &next_contig);
-    if (next_filled > 0) load_tile(key, next_contig);
-
-    if (active) {
-      const uint16_t* kb = sK[buf];
-      const uint16_t* vb = sV[buf];
-      // ---- S^T = K Q^T for 2 sub-tiles of 32 keys
-      f32x16_t s[2];
+  auto compute = [&](const lds_u16_t* kb, const lds_u16_t* vb, int filled) {
+    // ---- S^T = K Q^T for 2 sub-tiles of 32 keys
+    f32x16_t s[2];
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+    for (int st = 0; st < 2; ++st) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[st][i] = 0.f;
+      for (int i = 0; i < 16; ++i) s[st][i] = 0.f;
+      const int r = st * 32 + col;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&kb[(st * 32 + col) * KLD + ks * 16 + half * 8]);
-          s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[st], 0, 0, 0);
-        }
-      }
-      // ---- online softmax; lane holds keys st*32 + (i/4)*8 + half*4 + i%4
-      if (filled < BN) {
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int ks = st * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-            if (ks >= filled) s[st][i] = -__builtin_inff();
-          }
-      }
-      float mx = s[0][0];
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[st][i]);
-      {
-        // lanes i and i+32 hold the same query: combine their maxima
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
-      }
-      if (mx > m_ref + kLazyTau) {
-        const float alpha = __builtin_amdgcn_exp2f(m_ref - mx);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) lsum[i] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
-        m_ref = mx;
-      }
-      const float neg = -m_ref;
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[st][i] = __builtin_amdgcn_exp2f(fmaf(s[st][i], scale_log2, neg));
-
-      // ---- O^T += V^T P^T, 4 k-steps of 16 keys
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int st = kk >> 1, sub = kk & 1;
-        u32x4_t pw;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) pw[q] = pack_bf16x2(s[st][8 * sub + 2 * q], s[st][8 * sub + 2 * q + 1]);
-        const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
-        const int blk = 2 * kk + half;
-        // row sums of the bf16 P on the matrix core: an all-ones A operand
-        lsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb, lsum, 0, 0, 0);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const int d = dt * 32 + col;
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&vb[d * VLD + ((blk ^ ((d >> 4) & 7)) * 8)]);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[dt], 0, 0, 0);
-        }
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8_t a = *(const __attribute__((address_space(3))) bf16x8_t*)(
+            kb + r * D + TileGeom<D>::k_chunk(r, 2 * ks + half) * 8);
+        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[st], 0, 0, 0);
       }
     }
-    if (next_filled > 0) store_tile(buf ^ 1);
+    // ---- online softmax; lane holds keys st*32 + (i/4)*8 + half*4 + i%4
+    if (filled < BN) {
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int ks = st * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+          if (ks >= filled) s[st][i] = -__builtin_inff();
+        }
+    }
+    float mx = s[0][0];
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[st][i]);
+    {
+      // lanes i and i+32 hold the same query: combine their maxima
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
+    }
+    if (mx > m_ref + kLazyTau) {
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - mx);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) lsum[i] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+      m_ref = mx;
+    }
+    const float neg = -m_ref;
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[st][i] = __builtin_amdgcn_exp2f(fmaf(s[st][i], scale_log2, neg));
+
+    // ---- O^T += V^T P^T, 4 k-steps of 16 keys; key order inside a step:
+    // position h*8 + e <-> key 16 kk + 8 (e/4) + 4 h + e%4
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int st = kk >> 1, sub = kk & 1;
+      u32x4_t pw;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) pw[q] = pack_bf16x2(s[st][8 * sub + 2 * q], s[st][8 * sub + 2 * q + 1]);
+      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
+      lsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb, lsum, 0, 0, 0);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int c0 = dt * 32 + vcol;                       // column (element)
+        const int ra = 16 * kk + 4 * half + vr;              // keys 16kk + 4h + {0..3}
+        const int rb2 = ra + 8;                              // keys 16kk + 8 + 4h + {0..3}
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)(vb + ra * D + TileGeom<D>::v_chunk(ra, c0 >> 3) * 8 + (c0 & 7)));
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)(vb + rb2 * D + TileGeom<D>::v_chunk(rb2, c0 >> 3) * 8 + (c0 & 7)));
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[dt], 0, 0, 0);
+      }
+    }
+  };
+
+  lds_u16_t* k0 = to_lds(sK0);
+  lds_u16_t* k1 = to_lds(sK1);
+  lds_u16_t* v0 = to_lds(sV0);
+  lds_u16_t* v1 = to_lds(sV1);
+
+  int key[4];
+  bool contiguous;
+  int filled = cur.fill<4>(BN, slot_of, key, &contiguous);
+  if (filled > 0) dma_tile<D>(Kp, Vp, k0, v0, key, wave, lane);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  // two tiles per trip so that each LDS buffer is a distinct static array
+  while (filled > 0) {
+    int nf = cur.fill<4>(BN, slot_of, key, &contiguous);
+    if (nf > 0) dma_tile<D>(Kp, Vp, k1, v1, key, wave, lane);
+    if (active) compute(k0, v0, filled);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    buf ^= 1;
-    filled = next_filled;
+    filled = nf;
+    if (filled <= 0) break;
+    nf = cur.fill<4>(BN, slot_of, key, &contiguous);
+    if (nf > 0) dma_tile<D>(Kp, Vp, k0, v0, key, wave, lane);
+    if (active) compute(k1, v1, filled);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    filled = nf;
   }
 
-  // every row of the ones-product holds the sum over all keys of the tile
+  // every row of the ones-product holds the sum over all keys seen
   const float l_tot = lsum[0];
   if (row_ok) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;

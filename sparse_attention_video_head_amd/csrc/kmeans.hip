@@ -579,32 +579,53 @@ hipError_t launch_assign(const void* x, bool bf16, int bh, int N, int d, int n, 
 // ======================================================================
 // Lloyd update: centroid = mean of members (segmented over the sorted order)
 // ======================================================================
-// One work-group per (cluster, problem).  Thread (row lane rl, column pair cp)
-// sums rows offsets[c] + rl, + RL, ... of two columns in fp64; the RL partial
-// sums are combined in a fixed order, so the result is deterministic.
+// One work-group per (cluster, problem).  A row is read as 16-byte vectors
+// by VPR threads; RL = 256 / VPR rows are in flight per step (two steps
+// unrolled), each thread summing its 16-byte column chunk over rows
+// offsets[c] + rl, + RL, ... in fp64; the RL partial sums are then combined
+// in a fixed order, so the result is deterministic.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_centroid_mean(const T* __restrict__ X, int N, int n,
                                                        const int32_t* __restrict__ perm,
                                                        const int32_t* __restrict__ offsets,
                                                        float* __restrict__ C) {
-  constexpr int CP = D / 2;
-  constexpr int RL = 256 / CP;
+  constexpr int EPV = 16 / sizeof(T);          // elements per 16-byte vector
+  constexpr int VPR = D / EPV;                 // vectors per row
+  constexpr int RL = 256 / VPR;                // rows per step
   __shared__ double red[RL][D];
   const int c = blockIdx.x, p = blockIdx.y;
   const int a = offsets[(size_t)p * (n + 1) + c];
   const int b = offsets[(size_t)p * (n + 1) + c + 1];
   if (b <= a) return;                        // empty cluster keeps its centroid
-  const int cp = threadIdx.x % CP, rl = threadIdx.x / CP;
-  const T* Xp = X + (size_t)p * N * D;
+  const int cv = threadIdx.x % VPR, rl = threadIdx.x / VPR;
+  const T* Xp = X + (size_t)p * N * D + cv * EPV;
   const int32_t* pp = perm + (size_t)p * N;
-  double s0 = 0.0, s1 = 0.0;
-  for (int i = a + rl; i < b; i += RL) {
-    const int t = pp[i];
-    s0 += (double)Elem<T>::get(Xp, (size_t)t * D + 2 * cp);
-    s1 += (double)Elem<T>::get(Xp, (size_t)t * D + 2 * cp + 1);
+  double acc[EPV];
+#pragma unroll
+  for (int e = 0; e < EPV; ++e) acc[e] = 0.0;
+  auto add_row = [&](const u32x4_t v) {
+    if (sizeof(T) == 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += (double)bf16_lo(v[e]);
+        acc[2 * e + 1] += (double)bf16_hi(v[e]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += (double)__uint_as_float(v[e]);
+    }
+  };
+  int i = a + rl;
+  for (; i + RL < b; i += 2 * RL) {
+    const int t0 = pp[i], t1 = pp[i + RL];
+    const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(Xp + (size_t)t0 * D);
+    const u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(Xp + (size_t)t1 * D);
+    add_row(v0);
+    add_row(v1);
   }
-  red[rl][2 * cp] = s0;
-  red[rl][2 * cp + 1] = s1;
+  if (i < b) add_row(*reinterpret_cast<const u32x4_t*>(Xp + (size_t)pp[i] * D));
+#pragma unroll
+  for (int e = 0; e < EPV; ++e) red[rl][cv * EPV + e] = acc[e];
   __syncthreads();
   if (threadIdx.x < D) {
     double s = 0.0;
