@@ -130,10 +130,15 @@ struct KeyCursor {
 // softmax; only the intermediate scaling differs.
 constexpr float kLazyTau = 8.f;
 
-// Work items are taken in an order that keeps consecutive items (same
-// Q-cluster, same head) on one XCD: work-groups are dispatched round-robin
-// over the 8 XCDs, so block b runs item (b % 8) * per_xcd + b / 8.
+// Work-groups are dispatched round-robin over the 8 XCDs (block b runs on XCD
+// b % 8).  Items are handed out in chunks of kXcdChunk consecutive items per
+// XCD, so the slabs of one Q-cluster (which read the same key list) share an
+// XCD and its L2, while all XCDs still advance through the same head at the
+// same time (its K/V stays in the last-level cache):
+//   block b -> item ((b / 8 / C) * 8 + b % 8) * C + (b / 8) % C,  C = kXcdChunk
+// which is a bijection on [0, grid) when grid is a multiple of 8 C.
 constexpr int kXcds = 8;
+constexpr int kXcdChunk = 4;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
@@ -200,8 +205,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
   __shared__ __attribute__((aligned(16))) uint16_t sV0[BN * D], sV1[BN * D];
 
   const int total = max_items * bh;
-  const int per_xcd = (total + kXcds - 1) / kXcds;
-  const int logical = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+  const int jx = (int)(blockIdx.x / kXcds), xx = (int)(blockIdx.x % kXcds);
+  const int logical = ((jx / kXcdChunk) * kXcds + xx) * kXcdChunk + jx % kXcdChunk;
   if (logical >= total) return;
   const int p = logical / max_items, slot = logical % max_items;
   if (slot >= item_count[p]) return;
@@ -464,7 +469,8 @@ hipError_t launch_varblock_attn(const void* q, const void* k, const void* v, boo
                      items_ws);
   const dim3 grid(max_items, bh);
   const int total = max_items * bh;
-  const dim3 grid_x((total + kXcds - 1) / kXcds * kXcds);
+  constexpr int span = kXcds * kXcdChunk;
+  const dim3 grid_x((total + span - 1) / span * span);
   if (bf16) {
     const float sl2 = scale * 1.4426950408889634f;
 #define SVG2_ATTN(D)                                                                                  \

@@ -63,26 +63,6 @@ template <int D> struct ExactDist<float, D> {
   }
 };
 
-// fp32 x.c for bf16 rows: every product of two bf16 values is exact in fp32
-// and each of the D fused additions errs by at most 2^-24 of the running sum,
-// so |error| <= D * 2^-24 * sum|x_i c_i| <= D * 2^-25 (||x||^2 + ||c||^2).
-// Used only to skip exact evaluations that cannot lower D^2.
-template <int D>
-__device__ __forceinline__ float dot_bf16_f32(const uint16_t* x, const float* c) {
-  const u32x4_t* xv = reinterpret_cast<const u32x4_t*>(x);
-  float acc = 0.f;
-#pragma unroll 4
-  for (int q = 0; q < D / 8; ++q) {
-    const u32x4_t v = xv[q];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc = fmaf(bf16_lo(v[e]), c[8 * q + 2 * e], acc);
-      acc = fmaf(bf16_hi(v[e]), c[8 * q + 2 * e + 1], acc);
-    }
-  }
-  return acc;
-}
-
 // k-means++ runs as two kernels per pick so that every problem's tokens are
 // spread over the whole chip and the kernel boundaries order the picks:
 //   k_seed_update(k)  all tokens: D2 = min(D2, ||x - c_k||^2), then 256-token
@@ -93,134 +73,262 @@ __device__ __forceinline__ float dot_bf16_f32(const uint16_t* x, const float* c)
 // Per token the state is D2 (exact fp64), the nearest pick's number and
 // ||x||^2 (fp32).  A pick c can lower D2(x) only if ||c - c_near||^2 < 4 D2(x)
 // (triangle inequality, Elkan 2003), so other tokens are skipped without
-// reading x; the skip leaves D2 bit-identical to evaluating every token.
+// reading x; the skip leaves D2 equal to evaluating every token.  The tokens
+// that pass the test (typically 10-30%, scattered over nearly every wave) are
+// compacted per work-group and each candidate row is read by 16 lanes, so
+// only candidate rows are fetched and no lane idles on a skipped token.
 constexpr int kSeedTPL = 4;
-constexpr int kSeedBlk = kWave * kSeedTPL;        // 256 tokens per sampling block
+constexpr int kSeedBlk = kWave * kSeedTPL;            // 256 tokens per sampling block
 constexpr int kSeedWavesPerWG = 4;
-
-template <typename T, int D>
-__device__ __forceinline__ bool seed_lowers(const T* xr, const double* cd, const float* cf, float cn,
-                                            float xn, double cc_near, double& d2) {
-  if (cc_near >= 4.0 * d2 * (1.0 + 0x1p-20)) return false;
-  if (sizeof(T) == 2) {
-    // |approx - ||x - c||^2| <= D 2^-24 (xn + cn) plus the rounding of xn, cn
-    // and the two additions: below 2e-5 (xn + cn) at D = 128
-    const float approx = xn + cn - 2.f * dot_bf16_f32<D>(reinterpret_cast<const uint16_t*>(xr), cf);
-    if (!(approx <= (float)d2 + 5e-5f * (xn + cn) + 1e-30f)) return false;
-  }
-  const double nd = ExactDist<T, D>::run(xr, cd);
-  if (nd < d2) {
-    d2 = nd;
-    return true;
-  }
-  return false;
-}
+constexpr int kSeedWG = kSeedWavesPerWG * kSeedBlk;   // 1024 tokens per work-group
+constexpr int kSeedGroup = 16;                        // lanes per candidate row
+constexpr int kSeedUnroll = 4;                        // candidate rows in flight per group
 
 __device__ __forceinline__ int first_pick(uint64_t seed, int p, int N) {
   return min((int)(seed_uniform(seed, p, 0) * (double)N), N - 1);
 }
 
+// The slice of one row that lane `sub` of a 16-lane group holds: elements
+// [sub * E, (sub + 1) * E), E = D / 16, as 32-bit words.
+template <typename T, int D> struct RowSlice {
+  static constexpr int E = D / kSeedGroup;
+  static constexpr int W = E * (int)sizeof(T) / 4;
+  static_assert(W == 2 || W % 4 == 0, "slice of 8 or 16k bytes");
+  uint32_t w[W];
+  __device__ __forceinline__ void load(const T* row, int sub) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(row + sub * E);
+    if constexpr (W == 2) {
+      const uint2 v = *reinterpret_cast<const uint2*>(src);
+      w[0] = v.x;
+      w[1] = v.y;
+    } else {
+#pragma unroll
+      for (int q = 0; q < W / 4; ++q) {
+        const u32x4_t v = reinterpret_cast<const u32x4_t*>(src)[q];
+        w[4 * q] = v[0];
+        w[4 * q + 1] = v[1];
+        w[4 * q + 2] = v[2];
+        w[4 * q + 3] = v[3];
+      }
+    }
+  }
+  __device__ __forceinline__ float elem(int e) const {
+    if constexpr (sizeof(T) == 2) return (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
+    else return __uint_as_float(w[e]);
+  }
+};
+
+// Sum over the 16 lanes of a group by an xor butterfly.  Each step adds the
+// same two values in both partner lanes and IEEE addition commutes, so every
+// lane of the group ends with the identical sum.
+template <typename F>
+__device__ __forceinline__ F group16_sum(F v) {
+#pragma unroll
+  for (int m = kSeedGroup / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+// Pick 0: D2, nearest pick and ||x||^2 of every token, and the block sums.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void k_seed_update(
-    const T* __restrict__ X, int N, int n, int k, uint64_t seed, double* __restrict__ D2g,
+__global__ __launch_bounds__(256) void k_seed_first(
+    const T* __restrict__ X, int N, int n, uint64_t seed, double* __restrict__ D2g,
     int32_t* __restrict__ Ag, float* __restrict__ XNg, int32_t* __restrict__ picks,
-    const double* __restrict__ ccg, double* __restrict__ bsum, float* __restrict__ C0,
-    int32_t* __restrict__ seed_index) {
-  __shared__ float s_c[D];
+    double* __restrict__ bsum, float* __restrict__ C0, int32_t* __restrict__ seed_index) {
   __shared__ double s_cd[D];
   constexpr bool kBF16 = sizeof(T) == 2;
   const int p = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const T* Xp = X + (size_t)p * N * D;
-  double* D2 = D2g + (size_t)p * N;
-  int32_t* A = Ag + (size_t)p * N;
-  float* XN = XNg + (size_t)p * N;
   const int nblk = (N + kSeedBlk - 1) / kSeedBlk;
-  const int t = k == 0 ? first_pick(seed, p, N) : picks[(size_t)p * n + k];
+  const int t = first_pick(seed, p, N);
   for (int e = tid; e < D; e += 256) {
     const float v = Elem<T>::get(Xp, (size_t)t * D + e);
-    s_c[e] = v;
     s_cd[e] = (double)v;
-    if (k == 0 && blockIdx.x == 0) C0[(size_t)p * n * D + e] = v;
+    if (blockIdx.x == 0) C0[(size_t)p * n * D + e] = v;
   }
-  if (k == 0 && blockIdx.x == 0 && tid == 0) {
+  if (blockIdx.x == 0 && tid == 0) {
     picks[(size_t)p * n] = t;
     if (seed_index) seed_index[(size_t)p * n] = t;
   }
   __syncthreads();
-  float cn = 0.f;
-  for (int e = lane; e < D; e += kWave) cn = fmaf(s_c[e], s_c[e], cn);
-  cn = wave_sum(cn);
-
   const int b = blockIdx.x * kSeedWavesPerWG + wave;
   if (b >= nblk) return;
   const int t0 = b * kSeedBlk + kSeedTPL * lane;
   double d2[kSeedTPL];
-  if (k == 0) {
 #pragma unroll 1
-    for (int i = 0; i < kSeedTPL; ++i) {
-      d2[i] = 0.0;
-      const int tok = t0 + i;
-      if (tok < N) {
-        const T* xr = Xp + (size_t)tok * D;
-        d2[i] = ExactDist<T, D>::run(xr, s_cd);
-        D2[tok] = d2[i];
-        A[tok] = 0;
-        if (kBF16) {
-          const u32x4_t* xv = reinterpret_cast<const u32x4_t*>(xr);
-          float xn = 0.f;
-#pragma unroll 4
-          for (int q = 0; q < D / 8; ++q) {
-            const u32x4_t v = xv[q];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float a0 = bf16_lo(v[e]), a1 = bf16_hi(v[e]);
-              xn = fmaf(a0, a0, fmaf(a1, a1, xn));
-            }
-          }
-          XN[tok] = xn;
-        }
-      }
-    }
-  } else {
-    const double* cc = ccg + (size_t)p * n;
-    int a[kSeedTPL];
-    float xn[kSeedTPL];
-    // 16-byte state loads need every problem's arrays 16-byte aligned
-    if ((N % kSeedTPL) == 0 && t0 + kSeedTPL <= N) {
-      const double2 d01 = *reinterpret_cast<const double2*>(D2 + t0);
-      const double2 d23 = *reinterpret_cast<const double2*>(D2 + t0 + 2);
-      const int4 av = *reinterpret_cast<const int4*>(A + t0);
-      d2[0] = d01.x; d2[1] = d01.y; d2[2] = d23.x; d2[3] = d23.y;
-      a[0] = av.x; a[1] = av.y; a[2] = av.z; a[3] = av.w;
+  for (int i = 0; i < kSeedTPL; ++i) {
+    d2[i] = 0.0;
+    const int tok = t0 + i;
+    if (tok < N) {
+      const T* xr = Xp + (size_t)tok * D;
+      d2[i] = ExactDist<T, D>::run(xr, s_cd);
+      D2g[(size_t)p * N + tok] = d2[i];
+      Ag[(size_t)p * N + tok] = 0;
       if (kBF16) {
-        const float4 xv = *reinterpret_cast<const float4*>(XN + t0);
-        xn[0] = xv.x; xn[1] = xv.y; xn[2] = xv.z; xn[3] = xv.w;
-      } else {
-        xn[0] = xn[1] = xn[2] = xn[3] = 0.f;
-      }
-    } else {
+        const u32x4_t* xv = reinterpret_cast<const u32x4_t*>(xr);
+        float xn = 0.f;
+#pragma unroll 4
+        for (int q = 0; q < D / 8; ++q) {
+          const u32x4_t v = xv[q];
 #pragma unroll
-      for (int i = 0; i < kSeedTPL; ++i) {
-        const bool ok = t0 + i < N;
-        d2[i] = ok ? D2[t0 + i] : 0.0;
-        a[i] = ok ? clampi(A[t0 + i], 0, k - 1) : 0;
-        xn[i] = (ok && kBF16) ? XN[t0 + i] : 0.f;
-      }
-    }
-#pragma unroll 1
-    for (int i = 0; i < kSeedTPL; ++i) {
-      const int tok = t0 + i;
-      if (tok < N &&
-          seed_lowers<T, D>(Xp + (size_t)tok * D, s_cd, s_c, cn, xn[i], cc[clampi(a[i], 0, k - 1)], d2[i])) {
-        D2[tok] = d2[i];
-        A[tok] = k;
+          for (int e = 0; e < 4; ++e) {
+            const float a0 = bf16_lo(v[e]), a1 = bf16_hi(v[e]);
+            xn = fmaf(a0, a0, fmaf(a1, a1, xn));
+          }
+        }
+        XNg[(size_t)p * N + tok] = xn;
       }
     }
   }
   const double lsum = ((d2[0] + d2[1]) + d2[2]) + d2[3];
   const double inc = wave_inclusive_scan(lsum);
   if (lane == kWave - 1) bsum[(size_t)p * nblk + b] = inc;
+}
+
+// Pick k >= 1 (its token index is already in picks[k]): lower D2 and the
+// nearest pick where the new pick is closer, then the block sums.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_seed_update(
+    const T* __restrict__ X, int N, int n, int k, double* __restrict__ D2g, int32_t* __restrict__ Ag,
+    const float* __restrict__ XNg, const int32_t* __restrict__ picks, const double* __restrict__ ccg,
+    double* __restrict__ bsum) {
+  using Slice = RowSlice<T, D>;
+  constexpr int E = Slice::E;
+  constexpr int NG = 256 / kSeedGroup;              // candidate groups per work-group
+  constexpr bool kBF16 = sizeof(T) == 2;
+  __shared__ float s_c[D];
+  __shared__ double s_cd[D];
+  __shared__ double s_d2[kSeedWG];
+  __shared__ float s_xn[kSeedWG];
+  __shared__ uint16_t s_list[kSeedWG];
+  __shared__ int s_nc;
+  const int p = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const T* Xp = X + (size_t)p * N * D;
+  double* D2 = D2g + (size_t)p * N;
+  int32_t* A = Ag + (size_t)p * N;
+  const float* XN = XNg + (size_t)p * N;
+  const double* cc = ccg + (size_t)p * n;
+  const int nblk = (N + kSeedBlk - 1) / kSeedBlk;
+  const int t = clampi(picks[(size_t)p * n + k], 0, N - 1);
+  for (int e = tid; e < D; e += 256) {
+    const float v = Elem<T>::get(Xp, (size_t)t * D + e);
+    s_c[e] = v;
+    s_cd[e] = (double)v;
+  }
+  if (tid == 0) s_nc = 0;
+  __syncthreads();
+  float cn = 0.f;
+  if (kBF16) {
+    for (int e = lane; e < D; e += kWave) cn = fmaf(s_c[e], s_c[e], cn);
+    cn = wave_sum(cn);
+  }
+
+  // ---- state of this lane's 4 tokens, the skip test, compaction
+  const int b = blockIdx.x * kSeedWavesPerWG + wave;
+  const int tb = blockIdx.x * kSeedWG;               // first token of the work-group
+  const int l0 = wave * kSeedBlk + kSeedTPL * lane;  // first local token of the lane
+  const int t0 = tb + l0;
+  double d2[kSeedTPL];
+  int a[kSeedTPL];
+  float xn[kSeedTPL];
+  // 16-byte state loads need every problem's arrays 16-byte aligned
+  if ((N % kSeedTPL) == 0 && t0 + kSeedTPL <= N) {
+    const double2 d01 = *reinterpret_cast<const double2*>(D2 + t0);
+    const double2 d23 = *reinterpret_cast<const double2*>(D2 + t0 + 2);
+    const int4 av = *reinterpret_cast<const int4*>(A + t0);
+    d2[0] = d01.x; d2[1] = d01.y; d2[2] = d23.x; d2[3] = d23.y;
+    a[0] = av.x; a[1] = av.y; a[2] = av.z; a[3] = av.w;
+    if (kBF16) {
+      const float4 xv = *reinterpret_cast<const float4*>(XN + t0);
+      xn[0] = xv.x; xn[1] = xv.y; xn[2] = xv.z; xn[3] = xv.w;
+    } else {
+      xn[0] = xn[1] = xn[2] = xn[3] = 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kSeedTPL; ++i) {
+      const bool ok = t0 + i < N;
+      d2[i] = ok ? D2[t0 + i] : 0.0;
+      a[i] = ok ? A[t0 + i] : 0;
+      xn[i] = (ok && kBF16) ? XN[t0 + i] : 0.f;
+    }
+  }
+  unsigned m = 0;
+#pragma unroll
+  for (int i = 0; i < kSeedTPL; ++i) {
+    if (t0 + i < N && cc[clampi(a[i], 0, k - 1)] < 4.0 * d2[i] * (1.0 + 0x1p-20)) m |= 1u << i;
+    s_d2[l0 + i] = d2[i];
+    s_xn[l0 + i] = xn[i];
+  }
+  {
+    const int cnt = __popc(m);
+    const int inc = wave_inclusive_scan(cnt);
+    const int wtot = __shfl(inc, kWave - 1);
+    int base = 0;
+    if (lane == 0 && wtot > 0) base = atomicAdd(&s_nc, wtot);
+    int pos = __shfl(base, 0) + inc - cnt;
+#pragma unroll
+    for (int i = 0; i < kSeedTPL; ++i)
+      if ((m >> i) & 1u) s_list[pos++] = (uint16_t)(l0 + i);
+  }
+  __syncthreads();
+
+  // ---- candidates: 16 lanes per row, kSeedUnroll rows in flight per group
+  const int nc = s_nc;
+  const int grp = tid / kSeedGroup, sub = tid % kSeedGroup;
+  for (int c0 = grp; c0 < nc; c0 += NG * kSeedUnroll) {
+    Slice r[kSeedUnroll];
+    int loc[kSeedUnroll];
+#pragma unroll
+    for (int j = 0; j < kSeedUnroll; ++j) {
+      const int ci = c0 + j * NG;
+      loc[j] = ci < nc ? (int)s_list[ci] : -1;
+      if (loc[j] >= 0) r[j].load(Xp + (size_t)(tb + loc[j]) * D, sub);
+    }
+#pragma unroll
+    for (int j = 0; j < kSeedUnroll; ++j) {
+      if (loc[j] < 0) continue;                      // uniform over the group
+      const double dv = s_d2[loc[j]];
+      bool go = true;
+      if (kBF16) {
+        // fp32 screen: each bf16 x bf16 product is exact in fp32 and the D
+        // additions, in any order, err by at most D 2^-24 sum|x_i c_i|
+        // <= D 2^-25 (xn + cn); with the rounding of xn, cn and the final
+        // additions the screen is off by less than 2e-5 (xn + cn) at D = 128
+        float dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) dot = fmaf(r[j].elem(e), s_c[sub * E + e], dot);
+        dot = group16_sum(dot);
+        const float x_n = s_xn[loc[j]];
+        const float approx = x_n + cn - 2.f * dot;
+        go = approx <= (float)dv + 5e-5f * (x_n + cn) + 1e-30f;
+      }
+      if (go) {
+        // exact: differences and squares in fp64, the same order in every run
+        double acc = 0.0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const double df = (double)r[j].elem(e) - s_cd[sub * E + e];
+          acc = fma(df, df, acc);
+        }
+        acc = group16_sum(acc);
+        if (acc < dv && sub == 0) {
+          D2[tb + loc[j]] = acc;
+          A[tb + loc[j]] = k;
+          s_d2[loc[j]] = acc;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- block sums of the updated D2 (the same order as for pick 0)
+  if (b < nblk) {
+    const double lsum = ((s_d2[l0] + s_d2[l0 + 1]) + s_d2[l0 + 2]) + s_d2[l0 + 3];
+    const double inc = wave_inclusive_scan(lsum);
+    if (lane == kWave - 1) bsum[(size_t)p * nblk + b] = inc;
+  }
 }
 
 // Pick k+1 of problem blockIdx.x: the smallest token whose running D2 sum
@@ -343,8 +451,12 @@ hipError_t launch_kmeanspp(const void* x, bool bf16, int bh, int N, int d, int n
   const dim3 ug((nblk + kSeedWavesPerWG - 1) / kSeedWavesPerWG, bh);
 #define SVG2_SEED(T, D)                                                                                   \
   for (int k = 0; k < n; ++k) {                                                                         \
-    hipLaunchKernelGGL((k_seed_update<T, D>), ug, dim3(256), 0, s, static_cast<const T*>(x), N, n, k,   \
-                       seed, d2_ws, near_ws, xn_ws, picks_ws, cc_ws, bsum_ws, centroids, seed_index);   \
+    if (k == 0)                                                                                         \
+      hipLaunchKernelGGL((k_seed_first<T, D>), ug, dim3(256), 0, s, static_cast<const T*>(x), N, n,     \
+                         seed, d2_ws, near_ws, xn_ws, picks_ws, bsum_ws, centroids, seed_index);        \
+    else                                                                                                \
+      hipLaunchKernelGGL((k_seed_update<T, D>), ug, dim3(256), 0, s, static_cast<const T*>(x), N, n, k, \
+                         d2_ws, near_ws, xn_ws, picks_ws, cc_ws, bsum_ws);                              \
     if (k + 1 < n)                                                                                      \
       hipLaunchKernelGGL((k_seed_sample<T, D>), dim3(bh), dim3(256), 0, s, static_cast<const T*>(x), N, \
                          n, k, seed, d2_ws, bsum_ws, picks_ws, cc_ws, centroids, seed_index);           \
