@@ -45,7 +45,7 @@ struct Carve {
 
 struct KmeansWs {
   double* d2;
-  int32_t* near;      // 2 * bh * N ints: nearest pick, then ||x||^2 as float
+  int32_t* near;      // bh * N ints: the nearest pick of each token
   int32_t* picks;
   double* cc;
   double* bsum;
@@ -61,7 +61,7 @@ KmeansWs carve_kmeans(Carve& c, int bh, int N, int d, int n) {
   KmeansWs w;
   const size_t bN = (size_t)bh * N;
   w.d2 = c.take<double>(bN);
-  w.near = c.take<int32_t>(2 * bN);
+  w.near = c.take<int32_t>(bN);
   w.picks = c.take<int32_t>((size_t)bh * n);
   w.cc = c.take<double>((size_t)bh * n);
   w.bsum = c.take<double>((size_t)bh * ((N + 255) / 256));

@@ -70,8 +70,8 @@ template <int D> struct ExactDist<float, D> {
 //   k_seed_sample(k)  one work-group per problem: pick k+1 by inverse-CDF
 //                     sampling over the block sums, then the distances from
 //                     pick k+1 to every earlier pick for the next update.
-// Per token the state is D2 (exact fp64), the nearest pick's number and
-// ||x||^2 (fp32).  A pick c can lower D2(x) only if ||c - c_near||^2 < 4 D2(x)
+// Per token the state is D2 (exact fp64) and the nearest pick's number
+// (12 bytes, streamed once per pick).  A pick c can lower D2(x) only if ||c - c_near||^2 < 4 D2(x)
 // (triangle inequality, Elkan 2003), so other tokens are skipped without
 // reading x; the skip leaves D2 equal to evaluating every token.  The tokens
 // that pass the test (typically 10-30%, scattered over nearly every wave) are
@@ -128,14 +128,13 @@ __device__ __forceinline__ F group16_sum(F v) {
   return v;
 }
 
-// Pick 0: D2, nearest pick and ||x||^2 of every token, and the block sums.
+// Pick 0: D2 and nearest pick of every token, and the block sums.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_seed_first(
     const T* __restrict__ X, int N, int n, uint64_t seed, double* __restrict__ D2g,
-    int32_t* __restrict__ Ag, float* __restrict__ XNg, int32_t* __restrict__ picks,
-    double* __restrict__ bsum, float* __restrict__ C0, int32_t* __restrict__ seed_index) {
+    int32_t* __restrict__ Ag, int32_t* __restrict__ picks, double* __restrict__ bsum,
+    float* __restrict__ C0, int32_t* __restrict__ seed_index) {
   __shared__ double s_cd[D];
-  constexpr bool kBF16 = sizeof(T) == 2;
   const int p = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const T* Xp = X + (size_t)p * N * D;
@@ -164,20 +163,6 @@ __global__ __launch_bounds__(256) void k_seed_first(
       d2[i] = ExactDist<T, D>::run(xr, s_cd);
       D2g[(size_t)p * N + tok] = d2[i];
       Ag[(size_t)p * N + tok] = 0;
-      if (kBF16) {
-        const u32x4_t* xv = reinterpret_cast<const u32x4_t*>(xr);
-        float xn = 0.f;
-#pragma unroll 4
-        for (int q = 0; q < D / 8; ++q) {
-          const u32x4_t v = xv[q];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float a0 = bf16_lo(v[e]), a1 = bf16_hi(v[e]);
-            xn = fmaf(a0, a0, fmaf(a1, a1, xn));
-          }
-        }
-        XNg[(size_t)p * N + tok] = xn;
-      }
     }
   }
   const double lsum = ((d2[0] + d2[1]) + d2[2]) + d2[3];
@@ -185,13 +170,12 @@ __global__ __launch_bounds__(256) void k_seed_first(
   if (lane == kWave - 1) bsum[(size_t)p * nblk + b] = inc;
 }
 
-// Pick k >= 1 (its token index is already in picks[k]): lower D2 and the
-// nearest pick where the new pick is closer, then the block sums.
+// Pick k >= 1 (its row is already in C0[k]): lower D2 and the nearest pick
+// where the new pick is closer, then the block sums.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_seed_update(
     const T* __restrict__ X, int N, int n, int k, double* __restrict__ D2g, int32_t* __restrict__ Ag,
-    const float* __restrict__ XNg, const int32_t* __restrict__ picks, const double* __restrict__ ccg,
-    double* __restrict__ bsum) {
+    const float* __restrict__ C0, const double* __restrict__ ccg, double* __restrict__ bsum) {
   using Slice = RowSlice<T, D>;
   constexpr int E = Slice::E;
   constexpr int NG = 256 / kSeedGroup;              // candidate groups per work-group
@@ -199,7 +183,6 @@ __global__ __launch_bounds__(256) void k_seed_update(
   __shared__ float s_c[D];
   __shared__ double s_cd[D];
   __shared__ double s_d2[kSeedWG];
-  __shared__ float s_xn[kSeedWG];
   __shared__ uint16_t s_list[kSeedWG];
   __shared__ int s_nc;
   const int p = blockIdx.y;
@@ -207,31 +190,17 @@ __global__ __launch_bounds__(256) void k_seed_update(
   const T* Xp = X + (size_t)p * N * D;
   double* D2 = D2g + (size_t)p * N;
   int32_t* A = Ag + (size_t)p * N;
-  const float* XN = XNg + (size_t)p * N;
   const double* cc = ccg + (size_t)p * n;
   const int nblk = (N + kSeedBlk - 1) / kSeedBlk;
-  const int t = clampi(picks[(size_t)p * n + k], 0, N - 1);
-  for (int e = tid; e < D; e += 256) {
-    const float v = Elem<T>::get(Xp, (size_t)t * D + e);
-    s_c[e] = v;
-    s_cd[e] = (double)v;
-  }
-  if (tid == 0) s_nc = 0;
-  __syncthreads();
-  float cn = 0.f;
-  if (kBF16) {
-    for (int e = lane; e < D; e += kWave) cn = fmaf(s_c[e], s_c[e], cn);
-    cn = wave_sum(cn);
-  }
 
-  // ---- state of this lane's 4 tokens, the skip test, compaction
+  // ---- the state of this lane's 4 tokens and the skip test; nothing here
+  // waits on the new pick's row, so both loads are in flight together
   const int b = blockIdx.x * kSeedWavesPerWG + wave;
   const int tb = blockIdx.x * kSeedWG;               // first token of the work-group
   const int l0 = wave * kSeedBlk + kSeedTPL * lane;  // first local token of the lane
   const int t0 = tb + l0;
   double d2[kSeedTPL];
   int a[kSeedTPL];
-  float xn[kSeedTPL];
   // 16-byte state loads need every problem's arrays 16-byte aligned
   if ((N % kSeedTPL) == 0 && t0 + kSeedTPL <= N) {
     const double2 d01 = *reinterpret_cast<const double2*>(D2 + t0);
@@ -239,28 +208,33 @@ __global__ __launch_bounds__(256) void k_seed_update(
     const int4 av = *reinterpret_cast<const int4*>(A + t0);
     d2[0] = d01.x; d2[1] = d01.y; d2[2] = d23.x; d2[3] = d23.y;
     a[0] = av.x; a[1] = av.y; a[2] = av.z; a[3] = av.w;
-    if (kBF16) {
-      const float4 xv = *reinterpret_cast<const float4*>(XN + t0);
-      xn[0] = xv.x; xn[1] = xv.y; xn[2] = xv.z; xn[3] = xv.w;
-    } else {
-      xn[0] = xn[1] = xn[2] = xn[3] = 0.f;
-    }
   } else {
 #pragma unroll
     for (int i = 0; i < kSeedTPL; ++i) {
       const bool ok = t0 + i < N;
       d2[i] = ok ? D2[t0 + i] : 0.0;
       a[i] = ok ? A[t0 + i] : 0;
-      xn[i] = (ok && kBF16) ? XN[t0 + i] : 0.f;
     }
   }
+  for (int e = tid; e < D; e += 256) {
+    const float v = C0[((size_t)p * n + k) * D + e];
+    s_c[e] = v;
+    s_cd[e] = (double)v;
+  }
+  if (tid == 0) s_nc = 0;
   unsigned m = 0;
 #pragma unroll
   for (int i = 0; i < kSeedTPL; ++i) {
     if (t0 + i < N && cc[clampi(a[i], 0, k - 1)] < 4.0 * d2[i] * (1.0 + 0x1p-20)) m |= 1u << i;
     s_d2[l0 + i] = d2[i];
-    s_xn[l0 + i] = xn[i];
   }
+  __syncthreads();
+  float cn = 0.f;
+  if (kBF16) {
+    for (int e = lane; e < D; e += kWave) cn = fmaf(s_c[e], s_c[e], cn);
+    cn = wave_sum(cn);
+  }
+  // ---- compaction of the candidates into s_list
   {
     const int cnt = __popc(m);
     const int inc = wave_inclusive_scan(cnt);
@@ -296,11 +270,15 @@ __global__ __launch_bounds__(256) void k_seed_update(
         // additions, in any order, err by at most D 2^-24 sum|x_i c_i|
         // <= D 2^-25 (xn + cn); with the rounding of xn, cn and the final
         // additions the screen is off by less than 2e-5 (xn + cn) at D = 128
-        float dot = 0.f;
+        float dot = 0.f, x_n = 0.f;
 #pragma unroll
-        for (int e = 0; e < E; ++e) dot = fmaf(r[j].elem(e), s_c[sub * E + e], dot);
+        for (int e = 0; e < E; ++e) {
+          const float xe = r[j].elem(e);
+          dot = fmaf(xe, s_c[sub * E + e], dot);
+          x_n = fmaf(xe, xe, x_n);
+        }
         dot = group16_sum(dot);
-        const float x_n = s_xn[loc[j]];
+        x_n = group16_sum(x_n);
         const float approx = x_n + cn - 2.f * dot;
         go = approx <= (float)dv + 5e-5f * (x_n + cn) + 1e-30f;
       }
@@ -333,12 +311,17 @@ __global__ __launch_bounds__(256) void k_seed_update(
 
 // Pick k+1 of problem blockIdx.x: the smallest token whose running D2 sum
 // exceeds u_{k+1} * sum D2 (block sums, then the 256 tokens of the block).
+// Then ||c_{k+1} - c_a||^2 for every earlier pick a, from the centroid rows.
+// kSampleSplit work-groups per problem take the same (deterministic) pick and
+// share the distances; work-group 0 alone writes the pick.
+constexpr int kSampleThreads = 1024;
+constexpr int kSampleSplit = 8;
+
 template <typename T, int D>
-__global__ __launch_bounds__(256) void k_seed_sample(const T* __restrict__ X, int N, int n, int k,
-                                                     uint64_t seed, const double* __restrict__ D2g,
-                                                     const double* __restrict__ bsum,
-                                                     int32_t* __restrict__ picks, double* __restrict__ ccg,
-                                                     float* __restrict__ C0, int32_t* __restrict__ seed_index) {
+__global__ __launch_bounds__(kSampleThreads) void k_seed_sample(
+    const T* __restrict__ X, int N, int n, int k, uint64_t seed, const double* __restrict__ D2g,
+    const double* __restrict__ bsum, int32_t* __restrict__ picks, double* __restrict__ ccg,
+    float* __restrict__ C0, int32_t* __restrict__ seed_index) {
   __shared__ double s_red[17];
   __shared__ double s_cd[D];
   __shared__ int s_blk, s_last, s_pick;
@@ -347,13 +330,13 @@ __global__ __launch_bounds__(256) void k_seed_sample(const T* __restrict__ X, in
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const T* Xp = X + (size_t)p * N * D;
   const double* D2 = D2g + (size_t)p * N;
-  const double* bs = bsum + (size_t)p * ((N + kSeedBlk - 1) / kSeedBlk);
   const int nblk = (N + kSeedBlk - 1) / kSeedBlk;
+  const double* bs = bsum + (size_t)p * nblk;
   if (tid == 0) {
     s_blk = INT_MAX;
     s_last = -1;
   }
-  const int per = (nblk + 255) / 256;
+  const int per = (nblk + kSampleThreads - 1) / kSampleThreads;
   const int b0 = min(tid * per, nblk), b1 = min(b0 + per, nblk);
   double loc = 0.0;
   for (int b = b0; b < b1; ++b) loc += bs[b];
@@ -426,39 +409,67 @@ __global__ __launch_bounds__(256) void k_seed_sample(const T* __restrict__ X, in
   }
   __syncthreads();
   const int t = s_pick;
-  for (int e = tid; e < D; e += 256) {
+  for (int e = tid; e < D; e += kSampleThreads) {
     const float v = Elem<T>::get(Xp, (size_t)t * D + e);
     s_cd[e] = (double)v;
-    C0[((size_t)p * n + k + 1) * D + e] = v;
+    if (blockIdx.y == 0) C0[((size_t)p * n + k + 1) * D + e] = v;
   }
-  if (tid == 0) {
+  if (blockIdx.y == 0 && tid == 0) {
     picks[(size_t)p * n + k + 1] = t;
     if (seed_index) seed_index[(size_t)p * n + k + 1] = t;
   }
   __syncthreads();
-  // distances from the new pick to picks 0..k, for the next update's skip test
-  for (int a = tid; a <= k; a += 256) {
-    const int ta = clampi(picks[(size_t)p * n + a], 0, N - 1);
-    ccg[(size_t)p * n + a] = ExactDist<T, D>::run(Xp + (size_t)ta * D, s_cd);
+  // distances from the new pick to picks 0..k from the rows of C0 (which hold
+  // the picked tokens exactly): 16 lanes per row, fp64 differences and squares
+  constexpr int E = D / kSeedGroup;                 // floats per lane
+  const int sub = tid % kSeedGroup;
+  const int grp = (tid / kSeedGroup) * kSampleSplit + (int)blockIdx.y;
+  constexpr int NG = kSampleThreads / kSeedGroup * kSampleSplit;
+  for (int a0 = grp; a0 <= k; a0 += NG * kSeedUnroll) {
+    float v[kSeedUnroll][E];
+#pragma unroll
+    for (int j = 0; j < kSeedUnroll; ++j) {
+      const int a = a0 + j * NG;
+      if (a <= k) {
+        const float* cr = C0 + ((size_t)p * n + a) * D + sub * E;
+#pragma unroll
+        for (int q = 0; q < E / 4; ++q) {
+          const float4 f = reinterpret_cast<const float4*>(cr)[q];
+          v[j][4 * q] = f.x; v[j][4 * q + 1] = f.y; v[j][4 * q + 2] = f.z; v[j][4 * q + 3] = f.w;
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kSeedUnroll; ++j) {
+      const int a = a0 + j * NG;
+      if (a > k) break;                              // uniform over the group
+      double acc = 0.0;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const double df = (double)v[j][e] - s_cd[sub * E + e];
+        acc = fma(df, df, acc);
+      }
+      acc = group16_sum(acc);
+      if (sub == 0) ccg[(size_t)p * n + a] = acc;
+    }
   }
 }
 
 hipError_t launch_kmeanspp(const void* x, bool bf16, int bh, int N, int d, int n, uint64_t seed,
                            double* d2_ws, int32_t* near_ws, float* centroids, int32_t* seed_index,
                            int32_t* picks_ws, double* cc_ws, double* bsum_ws, hipStream_t s) {
-  float* xn_ws = reinterpret_cast<float*>(near_ws + (size_t)bh * N);
   const int nblk = (N + kSeedBlk - 1) / kSeedBlk;
   const dim3 ug((nblk + kSeedWavesPerWG - 1) / kSeedWavesPerWG, bh);
 #define SVG2_SEED(T, D)                                                                                   \
   for (int k = 0; k < n; ++k) {                                                                         \
     if (k == 0)                                                                                         \
       hipLaunchKernelGGL((k_seed_first<T, D>), ug, dim3(256), 0, s, static_cast<const T*>(x), N, n,     \
-                         seed, d2_ws, near_ws, xn_ws, picks_ws, bsum_ws, centroids, seed_index);        \
+                         seed, d2_ws, near_ws, picks_ws, bsum_ws, centroids, seed_index);               \
     else                                                                                                \
       hipLaunchKernelGGL((k_seed_update<T, D>), ug, dim3(256), 0, s, static_cast<const T*>(x), N, n, k, \
-                         d2_ws, near_ws, xn_ws, picks_ws, cc_ws, bsum_ws);                              \
+                         d2_ws, near_ws, centroids, cc_ws, bsum_ws);                                    \
     if (k + 1 < n)                                                                                      \
-      hipLaunchKernelGGL((k_seed_sample<T, D>), dim3(bh), dim3(256), 0, s, static_cast<const T*>(x), N, \
+      hipLaunchKernelGGL((k_seed_sample<T, D>), dim3(bh, kSampleSplit), dim3(kSampleThreads), 0, s, static_cast<const T*>(x), N, \
                          n, k, seed, d2_ws, bsum_ws, picks_ws, cc_ws, centroids, seed_index);           \
   }
   if (bf16) {
