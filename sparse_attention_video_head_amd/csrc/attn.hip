@@ -16,13 +16,15 @@
 //                      and V^T is staged in LDS in the same permuted order.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.hpp"
 
 namespace svg2 {
 
 constexpr int kAttnBM = 128;     // query rows per work item (bf16 kernel)
-constexpr int kAttnBN = 64;      // keys per tile
+constexpr int kAttnBN = 32;      // keys per tile (bf16 kernel)
 constexpr int kAttnF32BM = 64;   // query rows per work item (fp32 kernel)
 
 int attn_block_rows(bool bf16) { return bf16 ? kAttnBM : kAttnF32BM; }
@@ -145,48 +147,151 @@ typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
+// Work-group barrier for the tile loop.  The direct-to-LDS tile loads are
+// ordered by explicit vmcnt waits before it; a fenced __syncthreads would also
+// wait for the loads that are meant to stay in flight.  This waits for the
+// wave's own LDS accesses (lgkmcnt 0) and then meets the other waves; the asm
+// statement's memory clobber keeps the compiler from moving memory accesses
+// across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0); vmcnt, expcnt not waited for
+  asm volatile("s_barrier" ::: "memory");
+}
+
 template <typename Tp>
 __device__ __forceinline__ lds_u16_t* to_lds(Tp* p) {
   return (lds_u16_t*)(lds_void_t*)(void*)p;
 }
 
-// K and V tiles sit row-major in LDS, 64 keys x D, with the 16-byte chunks of
+// K and V tiles sit row-major in LDS, keys x D, with the 16-byte chunks of
 // each row XOR-swizzled (no padding, so they can be filled by direct
-// global -> LDS loads):
-//   K: chunk c of row r at c ^ (r % 16)      (conflict-free 16-byte reads of
-//      one chunk across 16 consecutive rows)
-//   V: chunk c of row r at c ^ 2 (r % 4)      (conflict-free transposing reads
-//      of 4 rows x 32 bytes)
+// global -> LDS loads).  LDS serves a 16-byte read 16 lanes at a time and an
+// 8-byte transposing read 32 lanes at a time, over 64 banks of 4 bytes:
+//   K: chunk c of row r at c ^ (r % 16): the 16 rows of one pass hit 16
+//      different chunk positions;
+//   V: a transposing read covers 4 rows x 4 chunks per 16 lanes and two such
+//      groups (columns 16 apart) per pass.  At D = 128 a row spans all 64
+//      banks, so chunk c of row r sits at c ^ 4 (r % 4) and the 4 rows use 4
+//      disjoint blocks of 4 chunks; at D = 64 two rows share the banks and
+//      c ^ 2 (r % 4) separates rows r and r + 2.
 template <int D> struct TileGeom {
   static constexpr int CPR = D / 8;                 // 16-byte chunks per row
   static __device__ __forceinline__ int k_chunk(int r, int c) { return c ^ (r & (CPR - 1) & 15); }
-  static __device__ __forceinline__ int v_chunk(int r, int c) { return c ^ (2 * (r & 3)); }
+  static __device__ __forceinline__ int v_chunk(int r, int c) {
+    return c ^ ((CPR == 16 ? 4 : 2) * (r & 3));
+  }
 };
 
-// One tile = 64 rows.  Each wave fills 16 rows of K and of V with 4 + 4
-// direct-to-LDS loads of 16 bytes per lane (lane -> row 4q + lane/16, slot
-// lane%16 of the row); rows past the key list load key 0 (never weighted:
-// their scores are masked to -inf).
-template <int D>
-__device__ __forceinline__ void dma_tile(const uint16_t* Kp, const uint16_t* Vp, lds_u16_t* sk, lds_u16_t* sv,
-                                         const int (&key)[4], int wave, int lane) {
+// Key ranges of the selected K-clusters, staged in LDS this many at a time.
+constexpr int kRangeChunk = 512;
+
+// Walks the concatenated key ranges of the selected clusters from an LDS copy
+// of (first key, length) per cluster.  Every thread of the work-group runs the
+// same cursor on the same data (uniform control flow); staging the next chunk
+// of ranges synchronises the group.
+struct LdsCursor {
+  const int32_t* sel;
+  const int32_t* koff;
+  int* s_start;
+  int* s_len;
+  int nsel, n_k, N;
+  int base, nst, r, pos, rem;
+
+  __device__ __forceinline__ void stage() {
+    for (int i = threadIdx.x; i < nst; i += blockDim.x) {
+      const int j = sel[base + i];
+      int a = 0, l = 0;
+      if ((unsigned)j < (unsigned)n_k) {
+        a = clampi(koff[j], 0, N);
+        l = clampi(koff[j + 1], a, N) - a;
+      }
+      s_start[i] = a;
+      s_len[i] = l;
+    }
+    __syncthreads();
+  }
+  __device__ __forceinline__ void init(const int32_t* s, const int32_t* ko, int ns, int nk, int n, int* ss,
+                                       int* sl) {
+    sel = s; koff = ko; nsel = ns; n_k = nk; N = n; s_start = ss; s_len = sl;
+    base = 0; nst = min(ns, kRangeChunk); r = 0; pos = 0; rem = 0;
+    stage();
+  }
+  // Leaves rem > 0 unless every range has been consumed.
+  __device__ __forceinline__ void open() {
+    while (rem == 0) {
+      if (r == nst) {
+        if (base + nst >= nsel) return;
+        __syncthreads();                       // all reads of this chunk are done
+        base += nst;
+        nst = min(nsel - base, kRangeChunk);
+        r = 0;
+        stage();
+      }
+      pos = s_start[r];
+      rem = s_len[r];
+      ++r;
+    }
+  }
+  // Keys of the next tile of `tile` slots: slot_of[e] (this thread's slots)
+  // get key indices or -1.  Returns the number of keys in the tile.
+  template <int NS>
+  __device__ __forceinline__ int fill(int tile, const int (&slot_of)[NS], int (&key)[NS]) {
+    open();
+    if (rem >= tile) {
+#pragma unroll
+      for (int e = 0; e < NS; ++e) key[e] = slot_of[e] >= 0 ? pos + slot_of[e] : -1;
+      pos += tile;
+      rem -= tile;
+      return tile;
+    }
+#pragma unroll
+    for (int e = 0; e < NS; ++e) key[e] = -1;
+    int filled = 0;
+    while (filled < tile) {
+      open();
+      if (rem == 0) break;
+      const int take = min(rem, tile - filled);
+#pragma unroll
+      for (int e = 0; e < NS; ++e) {
+        const int s = slot_of[e] - filled;
+        if (s >= 0 && s < take) key[e] = pos + s;
+      }
+      filled += take;
+      pos += take;
+      rem -= take;
+    }
+    return filled;
+  }
+};
+
+// One tile = 32 rows of K (or V).  Each wave fills 8 rows with direct-to-LDS
+// loads of 16 bytes per lane (lane -> row RPI q + lane/CPR, slot lane%CPR of
+// the row); rows past the key list load key 0 (never weighted: their scores
+// are masked to -inf).  `swz` is the tile's chunk swizzle.
+template <int D, typename Swz>
+__device__ __forceinline__ void dma_rows(const uint16_t* src, lds_u16_t* dst, const int (&key)[4], int wave,
+                                         int lane, Swz swz) {
   constexpr int CPR = D / 8;
   constexpr int RPI = kWave / CPR;                  // rows per instruction (4 at D=128)
-  constexpr int INS = 16 / RPI;                     // instructions per 16 rows
+  constexpr int INS = 8 / RPI;                      // instructions per 8 rows
 #pragma unroll
   for (int q = 0; q < INS; ++q) {
-    const int r = 16 * wave + RPI * q + lane / CPR;
-    const int phys = lane % CPR;
-    const size_t krow = (size_t)max(key[q], 0) * D;
-    const uint16_t* ksrc = Kp + krow + TileGeom<D>::k_chunk(r, phys) * 8;
-    const uint16_t* vsrc = Vp + krow + TileGeom<D>::v_chunk(r, phys) * 8;
-    lds_u16_t* kdst = sk + (16 * wave + RPI * q) * D;
-    lds_u16_t* vdst = sv + (16 * wave + RPI * q) * D;
-    __builtin_amdgcn_global_load_lds((const void*)ksrc, (lds_void_t*)kdst, 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)vsrc, (lds_void_t*)vdst, 16, 0, 0);
+    const int r = 8 * wave + RPI * q + lane / CPR;
+    const uint16_t* g = src + (size_t)max(key[q], 0) * D + swz(r, lane % CPR) * 8;
+    __builtin_amdgcn_global_load_lds((const void*)g, (lds_void_t*)(dst + (8 * wave + RPI * q) * D), 16, 0, 0);
   }
 }
 
+// Per wave and 32-key tile the work is two matrix-core phases, S^T = K Q^T
+// (D/16 MFMAs) and O^T += V^T P^T (D/16 MFMAs), with the softmax of the tile
+// between them on the vector ALU.  The loop is software-pipelined by one tile:
+// the scores of tile t+1 accumulate while the exponentials of tile t are
+// evaluated, so a wave keeps the matrix core and the vector ALU busy at once.
+// K and V tiles go through rings of 4 LDS buffers (tile j in slot j % 4) and
+// are loaded 3 tiles ahead, so two tiles' loads are in flight at any time:
+//   iteration t:  load K, V of tile t+3 -> slot (t+3) % 4
+//                 S[t+1] = K[t+1] Q^T  ||  softmax(S[t]);  O += V[t]^T P[t]^T
+//                 wait for the loads of tiles <= t+2, barrier
 template <int D>
 __global__ __launch_bounds__(256, 2) void k_attn_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
@@ -199,10 +304,18 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
   constexpr int DT = D / 32;           // 32-row tiles of O^T
   constexpr int CPR = D / 8;
   constexpr int RPI = kWave / CPR;
-  constexpr int INS = 16 / RPI;
-  static_assert(INS <= 4, "key slots per lane");
-  __shared__ __attribute__((aligned(16))) uint16_t sK0[BN * D], sK1[BN * D];
-  __shared__ __attribute__((aligned(16))) uint16_t sV0[BN * D], sV1[BN * D];
+  constexpr int INS = 8 / RPI;
+  static_assert(BN == 32 && INS >= 1 && INS <= 4, "tile geometry");
+  // s_waitcnt immediates: vmcnt = the loads of one tile, or 0; expcnt and
+  // lgkmcnt left at their maxima (not waited for)
+  constexpr int kWaitTile = 0xF70 | (2 * INS);
+  constexpr int kWaitAll = 0xF70;
+  // ring slot j: K tile at [0, BN*D), V tile at [BN*D, 2*BN*D); one array per
+  // slot keeps the number of distinct LDS objects that the loads write small
+  // enough for the compiler to track each of them separately
+  __shared__ __attribute__((aligned(16))) uint16_t sT0[2 * BN * D], sT1[2 * BN * D], sT2[2 * BN * D],
+      sT3[2 * BN * D];
+  __shared__ int s_rs[kRangeChunk], s_rl[kRangeChunk];
 
   const int total = max_items * bh;
   const int jx = (int)(blockIdx.x / kXcds), xx = (int)(blockIdx.x % kXcds);
@@ -235,58 +348,61 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
   // this lane's tile rows (one per direct-to-LDS load)
   int slot_of[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) slot_of[q] = q < INS ? 16 * wave + RPI * q + lane / CPR : -1;
+  for (int q = 0; q < 4; ++q) slot_of[q] = q < INS ? 8 * wave + RPI * q + lane / CPR : -1;
 
-  KeyCursor cur;
+  LdsCursor cur;
   cur.init(sel_idx + ((size_t)p * n_q + ci) * n_k, k_off + (size_t)p * (n_k + 1),
-           clampi(sel_count[(size_t)p * n_q + ci], 0, n_k), n_k, N);
+           clampi(sel_count[(size_t)p * n_q + ci], 0, n_k), n_k, N, s_rs, s_rl);
 
   float m_ref = -__builtin_inff();
-  f32x16_t o[DT], lsum;
+  float l_part = 0.f;                            // this lane's share of the row sum
+  f32x16_t o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) lsum[i] = 0.f;
-  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, u32x4_t{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
 
-  // per-lane LDS offsets (elements) of this lane's operand reads
-  // K (S^T = K Q^T): row st*32 + col, chunk 2 ks + half
-  // V^T (transposing read): rows kb + (lane%16)/4, columns d0 + 4 (lane%4)
+  // per-lane LDS offsets (elements) of the operand reads
+  //   K (S^T = K Q^T): row col, chunk 2 ks + half
+  //   V^T (transposing read): rows 4 half + (lane%16)/4 (+ 16 kk, + 8),
+  //   columns dt*32 + 16 ((lane/16)%2) + 4 (lane%4); the swizzle depends on
+  //   the row only through row % 4, which the added rows keep
+  int koff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) koff[ks] = col * D + TileGeom<D>::k_chunk(col, 2 * ks + half) * 8;
   const int vr = (lane & 15) >> 2;
   const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  int voff[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const int r = 4 * half + vr, c0 = dt * 32 + vcol;
+    voff[dt] = r * D + TileGeom<D>::v_chunk(r, c0 >> 3) * 8 + (c0 & 7);
+  }
+  auto kswz = [](int r, int c) { return TileGeom<D>::k_chunk(r, c); };
+  auto vswz = [](int r, int c) { return TileGeom<D>::v_chunk(r, c); };
 
-  auto compute = [&](const lds_u16_t* kb, const lds_u16_t* vb, int filled) {
-    // ---- S^T = K Q^T for 2 sub-tiles of 32 keys
-    f32x16_t s[2];
+  // S^T for the 32 keys of a K tile; lane holds query `col` and keys
+  // (i/4)*8 + half*4 + i%4
+  auto scores = [&](const lds_u16_t* kb, f32x16_t& s) {
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
+    for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[st][i] = 0.f;
-      const int r = st * 32 + col;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8_t a = *(const __attribute__((address_space(3))) bf16x8_t*)(
-            kb + r * D + TileGeom<D>::k_chunk(r, 2 * ks + half) * 8);
-        s[st] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[st], 0, 0, 0);
-      }
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8_t a = *(const __attribute__((address_space(3))) bf16x8_t*)(kb + koff[ks]);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
     }
-    // ---- online softmax; lane holds keys st*32 + (i/4)*8 + half*4 + i%4
+  };
+  // Softmax of tile `sc` (filled keys) and O^T += V^T P^T from V buffer `vb`,
+  // while the scores of the next tile accumulate into `sn` from K buffer `kn`.
+  auto step = [&](f32x16_t& sc, int filled, const lds_u16_t* vb, const lds_u16_t* kn, f32x16_t& sn) {
     if (filled < BN) {
 #pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int ks = st * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-          if (ks >= filled) s[st][i] = -__builtin_inff();
-        }
+      for (int i = 0; i < 16; ++i)
+        if ((i >> 2) * 8 + half * 4 + (i & 3) >= filled) sc[i] = -__builtin_inff();
     }
-    float mx = s[0][0];
+    float mx = sc[0];
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[st][i]);
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
     {
       // lanes i and i+32 hold the same query: combine their maxima
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
@@ -294,76 +410,135 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
     }
     if (mx > m_ref + kLazyTau) {
       const float alpha = __builtin_amdgcn_exp2f(m_ref - mx);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) lsum[i] *= alpha;
+      l_part *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
       m_ref = mx;
     }
+    // next tile's scores: independent of everything below
+    scores(kn, sn);
     const float neg = -m_ref;
+    u32x4_t pw[2];
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
+    for (int i = 0; i < 16; i += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[i], scale_log2, neg));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[i + 1], scale_log2, neg));
+      l_part += p0 + p1;
+      // k-step kk = i/8 of the P operand; key order inside a step:
+      // position h*8 + e <-> key 16 kk + 8 (e/4) + 4 h + e%4
+      pw[i >> 3][(i & 7) >> 1] = pack_bf16x2(p0, p1);
+    }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) s[st][i] = __builtin_amdgcn_exp2f(fmaf(s[st][i], scale_log2, neg));
-
-    // ---- O^T += V^T P^T, 4 k-steps of 16 keys; key order inside a step:
-    // position h*8 + e <-> key 16 kk + 8 (e/4) + 4 h + e%4
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int st = kk >> 1, sub = kk & 1;
-      u32x4_t pw;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) pw[q] = pack_bf16x2(s[st][8 * sub + 2 * q], s[st][8 * sub + 2 * q + 1]);
-      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
-      lsum = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb, lsum, 0, 0, 0);
+    for (int kk = 0; kk < 2; ++kk) {
+      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw[kk]);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const int c0 = dt * 32 + vcol;                       // column (element)
-        const int ra = 16 * kk + 4 * half + vr;              // keys 16kk + 4h + {0..3}
-        const int rb2 = ra + 8;                              // keys 16kk + 8 + 4h + {0..3}
-        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_t*)(vb + ra * D + TileGeom<D>::v_chunk(ra, c0 >> 3) * 8 + (c0 & 7)));
-        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_t*)(vb + rb2 * D + TileGeom<D>::v_chunk(rb2, c0 >> 3) * 8 + (c0 & 7)));
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb + (voff[dt] + 16 * kk * D)));
+        const s16x4_t hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb + (voff[dt] + (16 * kk + 8) * D)));
         const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[dt], 0, 0, 0);
       }
     }
+    // instruction order: the next tile's score MFMAs interleaved with this
+    // tile's exponentials, then the P.V MFMAs with their transposing reads
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);        // LDS reads
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x402, 7, 0);      // VALU incl. exp
+    }
+#pragma unroll
+    for (int i = 0; i < 2 * DT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);      // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x402, 1, 0);      // VALU
+    }
   };
 
-  lds_u16_t* k0 = to_lds(sK0);
-  lds_u16_t* k1 = to_lds(sK1);
-  lds_u16_t* v0 = to_lds(sV0);
-  lds_u16_t* v1 = to_lds(sV1);
+  lds_u16_t* k0 = to_lds(sT0);
+  lds_u16_t* k1 = to_lds(sT1);
+  lds_u16_t* k2 = to_lds(sT2);
+  lds_u16_t* k3 = to_lds(sT3);
+  lds_u16_t* v0 = k0 + BN * D;
+  lds_u16_t* v1 = k1 + BN * D;
+  lds_u16_t* v2 = k2 + BN * D;
+  lds_u16_t* v3 = k3 + BN * D;
 
+  // keys of tiles t, t+1, t+2 (0: no such tile)
   int key[4];
-  bool contiguous;
-  int filled = cur.fill<4>(BN, slot_of, key, &contiguous);
-  if (filled > 0) dma_tile<D>(Kp, Vp, k0, v0, key, wave, lane);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  int f0 = cur.fill<4>(BN, slot_of, key);
+  if (f0 > 0) {
+    dma_rows<D>(Kp, k0, key, wave, lane, kswz);
+    dma_rows<D>(Vp, v0, key, wave, lane, vswz);
+  }
+  int f1 = f0 > 0 ? cur.fill<4>(BN, slot_of, key) : 0;
+  if (f1 > 0) {
+    dma_rows<D>(Kp, k1, key, wave, lane, kswz);
+    dma_rows<D>(Vp, v1, key, wave, lane, vswz);
+  }
+  int f2 = f1 > 0 ? cur.fill<4>(BN, slot_of, key) : 0;
+  if (f2 > 0) {
+    dma_rows<D>(Kp, k2, key, wave, lane, kswz);
+    dma_rows<D>(Vp, v2, key, wave, lane, vswz);
+    __builtin_amdgcn_s_waitcnt(kWaitTile);       // tiles 0 and 1 have landed
+  } else {
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
+  }
+  lds_barrier();
+  f32x16_t sA, sB;
+  if (active && f0 > 0) scores(k0, sA);
 
-  // two tiles per trip so that each LDS buffer is a distinct static array
-  while (filled > 0) {
-    int nf = cur.fill<4>(BN, slot_of, key, &contiguous);
-    if (nf > 0) dma_tile<D>(Kp, Vp, k1, v1, key, wave, lane);
-    if (active) compute(k0, v0, filled);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    filled = nf;
-    if (filled <= 0) break;
-    nf = cur.fill<4>(BN, slot_of, key, &contiguous);
-    if (nf > 0) dma_tile<D>(Kp, Vp, k0, v0, key, wave, lane);
-    if (active) compute(k1, v1, filled);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    filled = nf;
+  // iteration t: S[t] in sc, K[t+1] in kn, V[t] in vc; tile t+3 -> kd, vd
+  // The loads are issued even past the end of the key list (all slots then
+  // read key 0 and the tile is never used): an unconditional load keeps the
+  // compiler's per-buffer tracking of them intact, so it adds no waits of its
+  // own before the LDS reads.  At the loop head that tracking is lost and the
+  // compiler waits for every load before the first LDS read, so the first
+  // tile of each trip issues its loads after its compute (`late`).
+  auto iter = [&](auto late, f32x16_t& sc, f32x16_t& sn, const lds_u16_t* kn, const lds_u16_t* vc,
+                  lds_u16_t* kd, lds_u16_t* vd) -> bool {
+    int f3 = 0;
+    if (f2 > 0) {
+      f3 = cur.fill<4>(BN, slot_of, key);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) key[q] = -1;
+    }
+    if constexpr (!decltype(late)::value) {
+      dma_rows<D>(Kp, kd, key, wave, lane, kswz);
+      dma_rows<D>(Vp, vd, key, wave, lane, vswz);
+    }
+    if (active) step(sc, f0, vc, kn, sn);
+    if constexpr (decltype(late)::value) {
+      dma_rows<D>(Kp, kd, key, wave, lane, kswz);
+      dma_rows<D>(Vp, vd, key, wave, lane, vswz);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitTile);       // tiles <= t+2 have landed
+    lds_barrier();
+    f0 = f1;
+    f1 = f2;
+    f2 = f3;
+    return f0 > 0;
+  };
+  // four tiles per trip so that every LDS buffer is a distinct static array
+  if (f0 > 0) {
+    constexpr std::true_type late{};
+    constexpr std::false_type early{};
+    while (iter(late, sA, sB, k1, v0, k3, v3) && iter(early, sB, sA, k2, v1, k0, v0) &&
+           iter(early, sA, sB, k3, v2, k1, v1) && iter(early, sB, sA, k0, v3, k2, v2)) {
+    }
   }
 
-  // every row of the ones-product holds the sum over all keys seen
-  const float l_tot = lsum[0];
+  // lanes i and i+32 hold the two halves of query col's keys
+  float l_tot;
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part), __float_as_uint(l_part), false, false);
+    l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
   if (row_ok) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     uint16_t* orow = O + base + (size_t)row * D;
