@@ -267,18 +267,20 @@ struct LdsCursor {
 // One tile = 32 rows of K (or V).  Each wave fills 8 rows with direct-to-LDS
 // loads of 16 bytes per lane (lane -> row RPI q + lane/CPR, slot lane%CPR of
 // the row); rows past the key list load key 0 (never weighted: their scores
-// are masked to -inf).  `swz` is the tile's chunk swizzle.
-template <int D, typename Swz>
-__device__ __forceinline__ void dma_rows(const uint16_t* src, lds_u16_t* dst, const int (&key)[4], int wave,
-                                         int lane, Swz swz) {
+// are masked to -inf).  `lane_off[q]` is the lane's swizzled byte offset
+// inside its row; one head's rows span less than 4 GiB (N <= 2^24), so the
+// address is the uniform head base plus a 32-bit per-lane offset.
+template <int D>
+__device__ __forceinline__ void dma_rows(const uint16_t* src, lds_u16_t* dst, const int (&key)[4],
+                                         const uint32_t (&lane_off)[4], int wave) {
   constexpr int CPR = D / 8;
   constexpr int RPI = kWave / CPR;                  // rows per instruction (4 at D=128)
   constexpr int INS = 8 / RPI;                      // instructions per 8 rows
 #pragma unroll
   for (int q = 0; q < INS; ++q) {
-    const int r = 8 * wave + RPI * q + lane / CPR;
-    const uint16_t* g = src + (size_t)max(key[q], 0) * D + swz(r, lane % CPR) * 8;
-    __builtin_amdgcn_global_load_lds((const void*)g, (lds_void_t*)(dst + (8 * wave + RPI * q) * D), 16, 0, 0);
+    const uint32_t off = (uint32_t)max(key[q], 0) * (uint32_t)(D * 2) + lane_off[q];
+    const void* g = (const void*)((const char*)src + off);
+    __builtin_amdgcn_global_load_lds(g, (lds_void_t*)(dst + (8 * wave + RPI * q) * D), 16, 0, 0);
   }
 }
 
@@ -327,7 +329,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
   const int ci = item & 0xfff, rb = item >> 12;
   const int32_t* qo = q_off + (size_t)p * (n_q + 1);
   const int qa = clampi(qo[ci], 0, N), qb = clampi(qo[ci + 1], qa, N);
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int col = lane & 31, half = lane >> 5;
   const int row0 = qa + rb * kAttnBM + wave * 32;
   const bool active = row0 < qb;                 // this wave has query rows
@@ -378,8 +381,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
     const int r = 4 * half + vr, c0 = dt * 32 + vcol;
     voff[dt] = r * D + TileGeom<D>::v_chunk(r, c0 >> 3) * 8 + (c0 & 7);
   }
-  auto kswz = [](int r, int c) { return TileGeom<D>::k_chunk(r, c); };
-  auto vswz = [](int r, int c) { return TileGeom<D>::v_chunk(r, c); };
+  // byte offsets of this lane's 16-byte slot within its tile row, swizzled
+  uint32_t kl_off[4], vl_off[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = 8 * wave + RPI * q + lane / CPR;
+    kl_off[q] = (uint32_t)TileGeom<D>::k_chunk(r, lane % CPR) * 16u;
+    vl_off[q] = (uint32_t)TileGeom<D>::v_chunk(r, lane % CPR) * 16u;
+  }
 
   // S^T for the 32 keys of a K tile; lane holds query `col` and keys
   // (i/4)*8 + half*4 + i%4
@@ -472,18 +481,18 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
   int key[4];
   int f0 = cur.fill<4>(BN, slot_of, key);
   if (f0 > 0) {
-    dma_rows<D>(Kp, k0, key, wave, lane, kswz);
-    dma_rows<D>(Vp, v0, key, wave, lane, vswz);
+    dma_rows<D>(Kp, k0, key, kl_off, wave);
+    dma_rows<D>(Vp, v0, key, vl_off, wave);
   }
   int f1 = f0 > 0 ? cur.fill<4>(BN, slot_of, key) : 0;
   if (f1 > 0) {
-    dma_rows<D>(Kp, k1, key, wave, lane, kswz);
-    dma_rows<D>(Vp, v1, key, wave, lane, vswz);
+    dma_rows<D>(Kp, k1, key, kl_off, wave);
+    dma_rows<D>(Vp, v1, key, vl_off, wave);
   }
   int f2 = f1 > 0 ? cur.fill<4>(BN, slot_of, key) : 0;
   if (f2 > 0) {
-    dma_rows<D>(Kp, k2, key, wave, lane, kswz);
-    dma_rows<D>(Vp, v2, key, wave, lane, vswz);
+    dma_rows<D>(Kp, k2, key, kl_off, wave);
+    dma_rows<D>(Vp, v2, key, vl_off, wave);
     __builtin_amdgcn_s_waitcnt(kWaitTile);       // tiles 0 and 1 have landed
   } else {
     __builtin_amdgcn_s_waitcnt(kWaitAll);
@@ -509,13 +518,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
       for (int q = 0; q < 4; ++q) key[q] = -1;
     }
     if constexpr (!decltype(late)::value) {
-      dma_rows<D>(Kp, kd, key, wave, lane, kswz);
-      dma_rows<D>(Vp, vd, key, wave, lane, vswz);
+      dma_rows<D>(Kp, kd, key, kl_off, wave);
+      dma_rows<D>(Vp, vd, key, vl_off, wave);
     }
     if (active) step(sc, f0, vc, kn, sn);
     if constexpr (decltype(late)::value) {
-      dma_rows<D>(Kp, kd, key, wave, lane, kswz);
-      dma_rows<D>(Vp, vd, key, wave, lane, vswz);
+      dma_rows<D>(Kp, kd, key, kl_off, wave);
+      dma_rows<D>(Vp, vd, key, vl_off, wave);
     }
     __builtin_amdgcn_s_waitcnt(kWaitTile);       // tiles <= t+2 have landed
     lds_barrier();
