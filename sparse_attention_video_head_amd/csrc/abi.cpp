@@ -65,9 +65,9 @@ KmeansWs carve_kmeans(Carve& c, int bh, int N, int d, int n) {
   w.picks = c.take<int32_t>((size_t)bh * n);
   w.cc = c.take<double>((size_t)bh * n);
   w.bsum = c.take<double>((size_t)bh * ((N + 255) / 256));
-  w.c_hi = c.take<uint16_t>((size_t)bh * n * d);
-  w.c_lo = c.take<uint16_t>((size_t)bh * n * d);
-  w.c_norm = c.take<float>((size_t)bh * n);
+  w.c_hi = c.take<uint16_t>((size_t)bh * centroid_rows(n) * d);
+  w.c_lo = c.take<uint16_t>((size_t)bh * centroid_rows(n) * d);
+  w.c_norm = c.take<float>((size_t)bh * centroid_rows(n));
   w.hist = c.take<int32_t>((size_t)bh * sort_chunks(N) * n);
   w.perm = c.take<int32_t>(bN);
   w.offsets = c.take<int32_t>((size_t)bh * (n + 1));

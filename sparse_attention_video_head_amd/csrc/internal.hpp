@@ -32,7 +32,10 @@ hipError_t launch_scatter_rows(const void* src, void* dst, int esize, int d, int
 hipError_t launch_kmeanspp(const void* x, bool bf16, int bh, int N, int d, int n, uint64_t seed,
                            double* d2_ws, int32_t* near_ws, float* centroids, int32_t* seed_index,
                            int32_t* picks_ws, double* cc_ws, double* bsum_ws, hipStream_t s);
-// centroid split for the matrix-core assignment: c_hi + c_lo (bf16 pair) and ||c||^2
+// centroid split for the matrix-core assignment: c_hi + c_lo (bf16 pair) and ||c||^2,
+// kCentroidPad-row padded per problem (padding rows: zeros, ||c||^2 = +inf)
+constexpr int kCentroidPad = 32;
+__host__ __device__ inline int centroid_rows(int n) { return (n + kCentroidPad - 1) / kCentroidPad * kCentroidPad; }
 hipError_t launch_prep_centroids(const float* c, int bh, int n, int d, uint16_t* c_hi,
                                  uint16_t* c_lo, float* c_norm, hipStream_t s);
 hipError_t launch_assign(const void* x, bool bf16, int bh, int N, int d, int n, const float* c,

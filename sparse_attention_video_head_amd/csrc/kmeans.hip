@@ -6,6 +6,8 @@
 //     its members (the counting sort of sort.hip groups the members).
 #include <limits.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -485,17 +487,29 @@ hipError_t launch_kmeanspp(const void* x, bool bf16, int bh, int N, int d, int n
 // Lloyd assignment
 // ======================================================================
 // c = c_hi + c_lo with both halves bf16 (|c - c_hi - c_lo| <= 2^-18 |c|), and
-// ||c||^2 in fp32, for the bf16 matrix-core distance contraction.
-__global__ __launch_bounds__(256) void k_prep_centroids(const float* __restrict__ c, int rows, int d,
-                                                        uint16_t* __restrict__ hi,
+// ||c||^2 in fp32, for the bf16 matrix-core distance contraction.  Each
+// problem's rows are padded to a multiple of kCentroidPad: padding rows are
+// zero with ||c||^2 = +inf, so they are never the nearest centroid.
+__global__ __launch_bounds__(256) void k_prep_centroids(const float* __restrict__ c, int bh, int n, int npad,
+                                                        int d, uint16_t* __restrict__ hi,
                                                         uint16_t* __restrict__ lo,
                                                         float* __restrict__ cn) {
   const int row = blockIdx.x * 4 + threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
-  if (row >= rows) return;
+  if (row >= bh * npad) return;
+  const int p = row / npad, j = row % npad;
+  if (j >= n) {
+    for (int e = lane; e < d; e += kWave) {
+      hi[(size_t)row * d + e] = 0;
+      lo[(size_t)row * d + e] = 0;
+    }
+    if (lane == 0) cn[row] = __builtin_inff();
+    return;
+  }
+  const float* src = c + ((size_t)p * n + j) * d;
   float acc = 0.f;
   for (int e = lane; e < d; e += kWave) {
-    const float v = c[(size_t)row * d + e];
+    const float v = src[e];
     const uint16_t h = f32_to_bf16(v);
     const uint16_t l = f32_to_bf16(v - bf16_to_f32(h));
     hi[(size_t)row * d + e] = h;
@@ -508,8 +522,9 @@ __global__ __launch_bounds__(256) void k_prep_centroids(const float* __restrict_
 
 hipError_t launch_prep_centroids(const float* c, int bh, int n, int d, uint16_t* c_hi,
                                  uint16_t* c_lo, float* c_norm, hipStream_t s) {
-  const int rows = bh * n;
-  hipLaunchKernelGGL(k_prep_centroids, dim3((rows + 3) / 4), dim3(256), 0, s, c, rows, d, c_hi, c_lo,
+  const int npad = centroid_rows(n);
+  const int rows = bh * npad;
+  hipLaunchKernelGGL(k_prep_centroids, dim3((rows + 3) / 4), dim3(256), 0, s, c, bh, n, npad, d, c_hi, c_lo,
                      c_norm);
   return hipGetLastError();
 }
@@ -518,28 +533,77 @@ hipError_t launch_prep_centroids(const float* c, int bh, int n, int d, uint16_t*
 // S^T = C x X^T (centroids as rows, tokens as columns) so that each lane holds
 // 16 centroid distances of ONE token and the argmin is mostly in-lane.
 // A work-group holds 512 tokens (4 waves x 4 blocks of 32) in registers and
-// streams the centroids through LDS in chunks of 64.
-constexpr int kAsgTB = 4;        // 32-token blocks per wave
-constexpr int kAsgCB = 64;       // centroids per LDS chunk
+// streams the centroids through a 4-deep LDS ring of 32-centroid chunks (bf16
+// hi and lo rows plus ||c||^2), filled by direct global -> LDS loads three
+// chunks ahead; the rows' 16-byte chunks are XOR-swizzled by row % 16 so that
+// the operand reads are conflict-free without padding.
+constexpr int kAsgTB = 4;                 // 32-token blocks per wave
+constexpr int kAsgCB = kCentroidPad;      // centroids per LDS chunk
+
+// s_waitcnt immediates (vmcnt only; expcnt and lgkmcnt not waited for)
+constexpr int asg_wait_vm(int n) { return 0xF70 | n; }
+
+__device__ __forceinline__ void lds_barrier_asg() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0); vmcnt, expcnt not waited for
+  asm volatile("s_barrier" ::: "memory");
+}
 
 template <int D>
-__global__ __launch_bounds__(256) void k_assign_bf16(const uint16_t* __restrict__ X, int N, int n,
-                                                     const uint16_t* __restrict__ Chi,
-                                                     const uint16_t* __restrict__ Clo,
-                                                     const float* __restrict__ Cn,
-                                                     int32_t* __restrict__ labels,
-                                                     float* __restrict__ min_dist) {
+__global__ __launch_bounds__(256, 2) void k_assign_bf16(const uint16_t* __restrict__ X, int N, int n,
+                                                        const uint16_t* __restrict__ Chi,
+                                                        const uint16_t* __restrict__ Clo,
+                                                        const float* __restrict__ Cn,
+                                                        int32_t* __restrict__ labels,
+                                                        float* __restrict__ min_dist) {
+  typedef __attribute__((address_space(3))) void lds_void_t;
+  typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
+  typedef __attribute__((address_space(3))) float lds_f32_t;
   constexpr int KS = D / 16;
-  constexpr int LDR = D + 8;                  // padded LDS row, elements
-  __shared__ __attribute__((aligned(16))) uint16_t sh_hi[kAsgCB * LDR];
-  __shared__ __attribute__((aligned(16))) uint16_t sh_lo[kAsgCB * LDR];
-  __shared__ float sh_cn[kAsgCB];
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int RPI = kWave / CPR;           // rows per load instruction
+  constexpr int INS = kAsgCB / 4 / RPI;      // load instructions per wave per half
+  static_assert(INS >= 1 && kAsgCB == 32, "chunk geometry");
+  // ring slot j: hi rows [0, CB*D), lo rows [CB*D, 2*CB*D), then CB norms
+  constexpr int SLOT = 2 * kAsgCB * D + 2 * kAsgCB;   // uint16 elements
+  __shared__ __attribute__((aligned(16))) uint16_t sC0[SLOT], sC1[SLOT], sC2[SLOT], sC3[SLOT];
 
   const int p = blockIdx.y;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int col = lane & 31, half = lane >> 5;
   const int tok0 = blockIdx.x * (4 * kAsgTB * 32) + wave * (kAsgTB * 32);
   const uint16_t* Xp = X + (size_t)p * N * D;
+  const int npad = centroid_rows(n);
+  const int nchunk = npad / kAsgCB;
+  const uint16_t* Hp = Chi + (size_t)p * npad * D;
+  const uint16_t* Lp = Clo + (size_t)p * npad * D;
+  const float* Np = Cn + (size_t)p * npad;
+
+  // this lane's part of a chunk load: row 8 wave + RPI q + lane / CPR,
+  // 16-byte slot lane % CPR holding source chunk (lane % CPR) ^ (row % 16)
+  uint32_t loff[INS];
+#pragma unroll
+  for (int q = 0; q < INS; ++q) {
+    const int r = 8 * wave + RPI * q + lane / CPR;
+    loff[q] = (uint32_t)(r * D + ((lane % CPR) ^ (r & (CPR - 1) & 15)) * 8) * 2u;
+  }
+  // loads chunk `ch` (clamped to the last one: past the end the slot is
+  // filled but never read) into a ring slot
+  auto load_chunk = [&](int ch, uint16_t* slot) __attribute__((always_inline)) {
+    ch = min(ch, nchunk - 1);
+    const uint32_t cbase = (uint32_t)ch * (uint32_t)(kAsgCB * D * 2);
+    lds_u16_t* dst = (lds_u16_t*)(lds_void_t*)(void*)slot;
+#pragma unroll
+    for (int q = 0; q < INS; ++q) {
+      lds_u16_t* d = dst + (8 * wave + RPI * q) * D;
+      __builtin_amdgcn_global_load_lds((const void*)((const char*)Hp + cbase + loff[q]), (lds_void_t*)d, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)((const char*)Lp + cbase + loff[q]),
+                                       (lds_void_t*)(d + kAsgCB * D), 16, 0, 0);
+    }
+    if (wave == 0 && lane < kAsgCB)
+      __builtin_amdgcn_global_load_lds((const void*)(Np + (size_t)ch * kAsgCB + lane),
+                                       (lds_void_t*)(dst + 2 * kAsgCB * D), 4, 0, 0);
+  };
 
   bf16x8_t xb[kAsgTB][KS];
   float xn[kAsgTB];
@@ -568,55 +632,66 @@ __global__ __launch_bounds__(256) void k_assign_bf16(const uint16_t* __restrict_
     best[tb] = __builtin_inff();
     bidx[tb] = 0;
   }
+  // operand row col: its chunk (2 ks + half) sits at (2 ks + half) ^ (col % 16)
+  const int arow = col * D, aswz = col & (CPR - 1) & 15;
 
-  const uint16_t* Hp = Chi + (size_t)p * n * D;
-  const uint16_t* Lp = Clo + (size_t)p * n * D;
-  for (int c0 = 0; c0 < n; c0 += kAsgCB) {
-    __syncthreads();
-    for (int v = threadIdx.x; v < kAsgCB * D / 8; v += 256) {
-      const int r = v / (D / 8), cv = v % (D / 8);
-      u32x4_t h = {0u, 0u, 0u, 0u}, l = {0u, 0u, 0u, 0u};
-      if (c0 + r < n) {
-        h = *reinterpret_cast<const u32x4_t*>(Hp + (size_t)(c0 + r) * D + cv * 8);
-        l = *reinterpret_cast<const u32x4_t*>(Lp + (size_t)(c0 + r) * D + cv * 8);
+  auto compute = [&](const uint16_t* slot, int c0) __attribute__((always_inline)) {
+    const lds_u16_t* sh = (const lds_u16_t*)(const lds_void_t*)(const void*)slot;
+    const lds_f32_t* sn = (const lds_f32_t*)(sh + 2 * kAsgCB * D);
+    f32x16_t acc[kAsgTB];
+#pragma unroll
+    for (int tb = 0; tb < kAsgTB; ++tb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[tb][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int aoff = arow + (((2 * ks + half) ^ aswz) * 8);
+      const bf16x8_t ah = *(const __attribute__((address_space(3))) bf16x8_t*)(sh + aoff);
+      const bf16x8_t al = *(const __attribute__((address_space(3))) bf16x8_t*)(sh + kAsgCB * D + aoff);
+#pragma unroll
+      for (int tb = 0; tb < kAsgTB; ++tb) {
+        acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xb[tb][ks], acc[tb], 0, 0, 0);
+        acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xb[tb][ks], acc[tb], 0, 0, 0);
       }
-      *reinterpret_cast<u32x4_t*>(&sh_hi[r * LDR + cv * 8]) = h;
-      *reinterpret_cast<u32x4_t*>(&sh_lo[r * LDR + cv * 8]) = l;
     }
-    for (int r = threadIdx.x; r < kAsgCB; r += 256)
-      sh_cn[r] = (c0 + r < n) ? Cn[(size_t)p * n + c0 + r] : __builtin_inff();
-    __syncthreads();
+    // lane (col, half) holds centroid rows (i/4)*8 + half*4 + i%4 of the chunk
 #pragma unroll
-    for (int mb = 0; mb < kAsgCB / 32; ++mb) {
-      f32x16_t acc[kAsgTB];
+    for (int tb = 0; tb < kAsgTB; ++tb)
 #pragma unroll
-      for (int tb = 0; tb < kAsgTB; ++tb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[tb][i] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int off = (mb * 32 + col) * LDR + ks * 16 + half * 8;
-        const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&sh_hi[off]);
-        const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&sh_lo[off]);
-#pragma unroll
-        for (int tb = 0; tb < kAsgTB; ++tb) {
-          acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xb[tb][ks], acc[tb], 0, 0, 0);
-          acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xb[tb][ks], acc[tb], 0, 0, 0);
+      for (int i = 0; i < 16; ++i) {
+        const int r = (i / 4) * 8 + half * 4 + (i % 4);
+        const float dist = sn[r] - 2.f * acc[tb][i];
+        if (dist < best[tb]) {
+          best[tb] = dist;
+          bidx[tb] = c0 + r;
         }
       }
-      // lane (col, half) holds centroid rows (i/4)*8 + half*4 + i%4 of this block
-#pragma unroll
-      for (int tb = 0; tb < kAsgTB; ++tb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = mb * 32 + (i / 4) * 8 + half * 4 + (i % 4);
-          const float dist = sh_cn[r] - 2.f * acc[tb][i];
-          if (dist < best[tb]) {
-            best[tb] = dist;
-            bidx[tb] = c0 + r;
-          }
-        }
-    }
+  };
+
+  // prologue: chunks 0..2 in flight, chunks 0 and 1 landed
+  load_chunk(0, sC0);
+  load_chunk(1, sC1);
+  load_chunk(2, sC2);
+  constexpr int kLoadsPerChunk = 2 * INS + 1;   // wave 0 issues one more (the norms)
+  if (wave == 0) __builtin_amdgcn_s_waitcnt(asg_wait_vm(kLoadsPerChunk));
+  else __builtin_amdgcn_s_waitcnt(asg_wait_vm(2 * INS));
+  lds_barrier_asg();
+  // chunk c: compute slot c % 4, load chunk c + 3 into slot (c + 3) % 4; the
+  // first chunk of each trip loads after computing (at the loop head the
+  // compiler's tracking of the loads is lost and it would wait for all of them)
+  int c = 0;
+  auto iter = [&](auto late, const uint16_t* cur, uint16_t* nxt) __attribute__((always_inline)) -> bool {
+    if constexpr (!decltype(late)::value) load_chunk(c + 3, nxt);
+    compute(cur, c * kAsgCB);
+    if constexpr (decltype(late)::value) load_chunk(c + 3, nxt);
+    if (wave == 0) __builtin_amdgcn_s_waitcnt(asg_wait_vm(kLoadsPerChunk));
+    else __builtin_amdgcn_s_waitcnt(asg_wait_vm(2 * INS));
+    lds_barrier_asg();
+    return ++c < nchunk;
+  };
+  constexpr std::true_type late{};
+  constexpr std::false_type early{};
+  while (iter(late, sC0, sC3) && iter(early, sC1, sC0) && iter(early, sC2, sC1) && iter(early, sC3, sC2)) {
   }
 
 #pragma unroll
