@@ -46,6 +46,10 @@ def parse():
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work in the CPU leg")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (counter calibration)")
+    ap.add_argument("--denoise", action="store_true",
+                    help="warm-start study on the denoising sequence instead of the layer step")
+    ap.add_argument("--agree-heads", type=int, default=4,
+                    help="--denoise: heads whose labels are compared (ARI, matched agreement)")
     return ap.parse_args()
 
 
@@ -150,6 +154,203 @@ def cpu_baseline(host, cfg, top_p, budget_s):
             "stage_s_per_head": {k_: round(v_, 3) for k_, v_ in T.items()}}
 
 
+def padding_ratios(layer):
+    """Computed work over real query-key pairs for the current selection:
+    fixed 128-token blocks (every selected (Q-cluster, K-cluster) block padded
+    to multiples of 128 in both dimensions) and this kernel's own padding
+    (rows to 32 per Q-cluster, keys to 32 per concatenated key list)."""
+    import torch
+    szq = (layer.off_q[:, 1:] - layer.off_q[:, :-1]).to(torch.int64)
+    szk = (layer.off_k[:, 1:] - layer.off_k[:, :-1]).to(torch.int64)
+    n_q, n_k = szq.shape[1], szk.shape[1]
+    valid = torch.arange(n_k, device=szk.device)[None, None, :] < layer.sel_count[:, :, None]
+    idx = layer.sel_idx.clamp(0, n_k - 1).to(torch.int64)
+    ksel = torch.gather(szk[:, None, :].expand(-1, n_q, -1), 2, idx) * valid
+    keys = ksel.sum(2)
+    keys128 = ((ksel + 127) // 128 * 128).sum(2)
+    pairs = float((szq * keys).sum().item())
+    fixed = float((((szq + 127) // 128 * 128) * keys128).sum().item())
+    own = float((((szq + 31) // 32 * 32) * ((keys + 31) // 32 * 32)).sum().item())
+    return fixed / pairs, own / pairs
+
+
+def _match_agreement(a, b, n):
+    """Fraction of tokens whose labels agree under the best one-to-one matching
+    of the two labelings' clusters (Hungarian method on the contingency table)."""
+    import numpy as np
+    from scipy.optimize import linear_sum_assignment
+    cont = np.zeros((n, n), dtype=np.int64)
+    np.add.at(cont, (a, b), 1)
+    r, c = linear_sum_assignment(-cont)
+    return float(cont[r, c].sum()) / len(a)
+
+
+def _objective(x, labels, cent):
+    """sum_t ||x_t - c_{label(t)}||^2 over every head (fp32, per head)."""
+    import torch
+    tot = 0.0
+    for h in range(x.shape[0]):
+        c = cent[h].index_select(0, labels[h].long())
+        tot += float(((x[h].float() - c) ** 2).sum().item())
+    return tot
+
+
+def denoise_run(args):
+    """Warm start along the denoising sequence: step 0 clusters cold (k-means++
+    and the config's rounds); every later step warm-starts from the previous
+    step's centroids with --warm-iters rounds, and is compared with a cold start
+    on the same step (time, objective, labels, output)."""
+    import numpy as np
+    import torch
+    from sklearn.metrics import adjusted_rand_score
+    from sparse_attention_video_head_amd import binding as B
+    from sparse_attention_video_head_amd import synth
+    from sparse_attention_video_head_amd.pipeline import SVG2Layer
+
+    cfg = synth.CONFIGS["denoise"]
+    dev = torch.device("cuda:0")
+    log(f"libsvg2 {B.version()}; denoising sequence: {cfg.steps} steps, bh={cfg.bh} N={cfg.n_tokens} "
+        f"d={cfg.head_dim} n_q={cfg.n_q} n_k={cfg.n_k}, warm {args.warm_iters} rounds")
+    mk = lambda: SVG2Layer(cfg.bh, cfg.n_tokens, cfg.head_dim, cfg.torch_dtype, cfg.n_q, cfg.n_k, device=dev)
+    warm_l, cold_l = mk(), mk()
+    seeds = dict(seed_q=(cfg.seed << 8) | 0, seed_k=(cfg.seed << 8) | 1)
+    E = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed_layer(layer, x, warm, iters, top_p):
+        ev = [E() for _ in range(3)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        layer.kmeans(x["q"], x["k"], iters, warm, **seeds)
+        ev[1].record()
+        layer.permute(x["q"], x["k"], x["v"])
+        layer.select(top_p)
+        layer.attend()
+        out = layer.unpermute()
+        ev[2].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]), ev[0].elapsed_time(ev[2]), out
+
+    steps, keep, top_p = [], {}, args.top_p
+    t_gen = 0.0
+    gen = synth.denoise_sequence(cfg, workers=min(16, os.cpu_count() or 1))
+    for s in range(cfg.steps):
+        t0 = time.time()
+        host = next(gen)
+        t_gen += time.time() - t0
+        x = {c: host[c].to(dev) for c in "qkv"}
+        if s == 0:
+            # clustering and top-p of the sequence's first step (cold); warm-up launches first
+            warm_l.kmeans(x["q"], x["k"], cfg.iters, False, **seeds)
+            warm_l.permute(x["q"], x["k"], x["v"])
+            if top_p is None:
+                lo, hi = 0.01, 1.0
+                for _ in range(30):
+                    top_p = 0.5 * (lo + hi)
+                    warm_l.select(top_p)
+                    dens = warm_l.density()
+                    if abs(dens - args.density) <= 0.005:
+                        break
+                    lo, hi = (lo, top_p) if dens > args.density else (top_p, hi)
+            km, lay, _ = timed_layer(warm_l, x, False, cfg.iters, top_p)
+            steps.append({"step": 0, "kmeans_ms": round(km, 3), "layer_ms": round(lay, 3), "start": "cold"})
+            log(f"step 0 cold: k-means {km:.2f} ms, layer {lay:.2f} ms, top_p {top_p:.5f}")
+            if not args.no_cpu_baseline:
+                keep["q0"] = host["q"][0].clone()
+            continue
+        km_w, lay_w, out_w = timed_layer(warm_l, x, True, args.warm_iters, top_p)
+        out_w = out_w.clone()
+        if s == 1 and not args.no_cpu_baseline:
+            keep.update(q1=host["q"][0].clone(), labels1=warm_l.labels_q[0].cpu().numpy(),
+                        cent1=warm_l.cq[0].cpu().double().numpy())
+        km_c, lay_c, out_c = timed_layer(cold_l, x, False, cfg.iters, top_p)
+        J = {}
+        for side, xs in (("q", x["q"]), ("k", x["k"])):
+            lw, lc = getattr(warm_l, f"labels_{side}"), getattr(cold_l, f"labels_{side}")
+            cw, cc = getattr(warm_l, f"c{side}"), getattr(cold_l, f"c{side}")
+            J[side] = _objective(xs, lw, cw) / _objective(xs, lc, cc)
+        ari, agree = [], []
+        for side, n in (("q", cfg.n_q), ("k", cfg.n_k)):
+            lw = getattr(warm_l, f"labels_{side}")[: args.agree_heads].cpu().numpy()
+            lc = getattr(cold_l, f"labels_{side}")[: args.agree_heads].cpu().numpy()
+            for h in range(lw.shape[0]):
+                ari.append(adjusted_rand_score(lc[h], lw[h]))
+                agree.append(_match_agreement(lc[h], lw[h], n))
+        rel = float(torch.linalg.vector_norm((out_w.float() - out_c.float())).item()
+                    / torch.linalg.vector_norm(out_c.float()).item())
+        rec = {"step": s, "kmeans_ms_warm": round(km_w, 3), "kmeans_ms_cold": round(km_c, 3),
+               "layer_ms_warm": round(lay_w, 3), "layer_ms_cold": round(lay_c, 3),
+               "J_warm_over_cold_q": round(J["q"], 5), "J_warm_over_cold_k": round(J["k"], 5),
+               "ari_mean": round(float(np.mean(ari)), 4), "matched_agreement_mean": round(float(np.mean(agree)), 4),
+               "rel_l2_out_warm_vs_cold": round(rel, 5)}
+        steps.append(rec)
+        log(f"step {s}: k-means warm {km_w:.2f} / cold {km_c:.2f} ms; J ratio q {J['q']:.4f} k {J['k']:.4f}; "
+            f"ARI {np.mean(ari):.3f}; agreement {np.mean(agree):.3f}; rel-L2(O) {rel:.4f}")
+    warm_steps = steps[1:]
+    mean = lambda key: float(np.mean([r[key] for r in warm_steps]))
+    km_ratio = mean("kmeans_ms_cold") / mean("kmeans_ms_warm")
+    res = {
+        "metric": "k-means time saved by centroid caching along the denoising sequence (cold / warm)",
+        "value": round(km_ratio, 3),
+        "unit": "x",
+        "n_gpus": 1,
+        "higher_is_better": True,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": "denoise-hunyuan720p", "heads": cfg.bh, "n_tokens": cfg.n_tokens,
+                   "head_dim": cfg.head_dim, "n_q": cfg.n_q, "n_k": cfg.n_k, "steps": cfg.steps,
+                   "drift": cfg.drift, "cold_iters": cfg.iters, "warm_iters": args.warm_iters,
+                   "top_p": round(top_p, 6), "agree_heads": args.agree_heads},
+        "layer_ms_warm_mean": round(mean("layer_ms_warm"), 3),
+        "layer_ms_cold_mean": round(mean("layer_ms_cold"), 3),
+        "J_warm_over_cold_q_mean": round(mean("J_warm_over_cold_q"), 5),
+        "J_warm_over_cold_k_mean": round(mean("J_warm_over_cold_k"), 5),
+        "ari_mean": round(mean("ari_mean"), 4),
+        "matched_agreement_mean": round(mean("matched_agreement_mean"), 4),
+        "rel_l2_out_warm_vs_cold_mean": round(mean("rel_l2_out_warm_vs_cold"), 5),
+        "input_generation_s": round(t_gen, 1),
+        "steps_detail": steps,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = denoise_cpu_baseline(keep, cfg, args)
+    print(json.dumps(res), flush=True)
+
+
+def denoise_cpu_baseline(keep, cfg, args):
+    """The fp64 oracle as it stands on head 0, Q side: a cold k-means of step 0
+    (k-means++ and the config's rounds), a warm start of step 1 from those
+    centroids (--warm-iters rounds) and a cold k-means of step 1, timed.  Value
+    = the oracle's own cold / warm k-means time on step 1.  The cold step-1
+    result is also the reference for the GPU's warm-started labels of that
+    head (ARI, matched agreement, objective ratio)."""
+    import numpy as np
+    import oracle
+    from sklearn.metrics import adjusted_rand_score
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    seed_q = (cfg.seed << 8) | 0
+    x0, x1 = keep["q0"].double().numpy(), keep["q1"].double().numpy()
+    c0 = oracle.kmeans(x0, cfg.n_q, cfg.iters, seed=seed_q, problem=0)
+    t = time.perf_counter()
+    oracle.kmeans(x1, cfg.n_q, args.warm_iters, init=c0.centroids)
+    t_warm = time.perf_counter() - t
+    t = time.perf_counter()
+    c1 = oracle.kmeans(x1, cfg.n_q, cfg.iters, seed=seed_q, problem=0)
+    t_cold = time.perf_counter() - t
+    gl = keep["labels1"].astype(np.int64)
+    j_gpu = oracle.objective(x1, keep["cent1"], gl)
+    j_orc = oracle.objective(x1, c1.centroids, c1.labels)
+    return {"value": round(t_cold / t_warm, 3), "unit": "x", "cores": threads, "kind": "oracle",
+            "sample": (f"head 0, Q side (n={cfg.n_q}): fp64 cold k-means of step 0, warm start of step 1 "
+                       f"({args.warm_iters} rounds), cold k-means of step 1"),
+            "oracle_cold_s": round(t_cold, 2), "oracle_warm_s": round(t_warm, 2),
+            "gpu_warm_vs_oracle_cold_ari": round(float(adjusted_rand_score(c1.labels, gl)), 4),
+            "gpu_warm_vs_oracle_cold_matched_agreement": round(_match_agreement(c1.labels, gl, cfg.n_q), 4),
+            "gpu_warm_J_over_oracle_cold_J": round(j_gpu / j_orc, 5)}
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -159,6 +360,9 @@ def main():
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path shards by head with no "
               "exchange and is not run on several GPUs here.", file=sys.stderr)
         sys.exit(2)
+    if args.denoise:
+        denoise_run(args)
+        return
 
     import numpy as np
     import torch
@@ -258,17 +462,23 @@ def main():
     ms_per_iter = (km[1] - km[0]) / 4.0
     seeding_ms = cold_stage[0] - cfg.iters * ms_per_iter
 
-    dense_ms = None
+    dense_ms = rel_dense = None
     if not args.no_dense:
         layer.dense(q, k, v)
         a, b = E(), E()
         torch.cuda.synchronize()
         a.record()
-        layer.dense(q, k, v)
+        o_dense = layer.dense(q, k, v)
         b.record()
         torch.cuda.synchronize()
         dense_ms = a.elapsed_time(b)
-        log(f"dense attention {dense_ms:.2f} ms")
+        # the cold step's sparse output (last timed step) against dense attention
+        step(False, cfg.iters)
+        torch.cuda.synchronize()
+        rel_dense = float(torch.linalg.vector_norm(layer.out.float() - o_dense.float()).item()
+                          / torch.linalg.vector_norm(o_dense.float()).item())
+        del o_dense
+        log(f"dense attention {dense_ms:.2f} ms; sparse vs dense rel-L2 {rel_dense:.4f}")
 
     pairs = int(layer.pairs.sum().item())
     attn_flops = 4.0 * cfg.head_dim * pairs
@@ -283,6 +493,10 @@ def main():
     permute_bytes = bhn * (6.0 * N * d * e + 8.0 * N)      # Q, K, V read + written, labels, perm
     unpermute_bytes = bhn * (2.0 * N * d * e + 4.0 * N)
     traffic = attn_traffic_per_launch()
+    pad_fixed128, pad_own = padding_ratios(layer)
+    # Lloyd distance contraction: 2 d N (n_Q + n_K) flop per head and round
+    # (the matrix core issues twice that for the hi/lo centroid halves)
+    lloyd_flops = 2.0 * d * N * (cfg.n_q + cfg.n_k) * bhn
     res = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -314,6 +528,11 @@ def main():
         "dense_tflops": round(dense_flops / (dense_ms * 1e-3) / 1e12, 2) if dense_ms else None,
         "speedup_vs_dense_cold": round(dense_ms / cold_ms, 3) if dense_ms else None,
         "speedup_vs_dense_warm": round(dense_ms / warm_ms, 3) if dense_ms else None,
+        "lloyd_round_distance_tflops": round(lloyd_flops / (ms_per_iter * 1e-3) / 1e12, 2) if ms_per_iter > 0 else None,
+        "select_share_of_dense": round(float(cold_stage[2]) / dense_ms, 5) if dense_ms else None,
+        "rel_l2_sparse_vs_dense": round(rel_dense, 5) if rel_dense is not None else None,
+        "padding_ratio_fixed128_blocks": round(pad_fixed128, 4),
+        "padding_ratio_this_kernel": round(pad_own, 4),
         "permute_gbps": round(permute_bytes / (cold_stage[1] * 1e-3) / 1e9, 1),
         "unpermute_gbps": round(unpermute_bytes / (cold_stage[4] * 1e-3) / 1e9, 1),
         "roofline": {"bound": "mfma", "kernel": "k_attn_bf16" if cfg.dtype == "bf16" else "k_attn_f32",

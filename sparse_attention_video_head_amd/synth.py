@@ -168,6 +168,61 @@ def make_layer(cfg, heads: Optional[Sequence[int]] = None, step: int = 0):
                 labels=torch.stack(ls), cfg=cfg, heads=heads)
 
 
+def _head_sequence(args):
+    """Rounded (q, k, v) of one head for steps 0..steps-1 (fp64 masters kept)."""
+    cfg, h, steps = args
+    q, k, v, lab = head_master(cfg, h)
+    m = [q, k, v]
+    out = []
+    for s in range(steps):
+        if s > 0:
+            for which in range(3):
+                m[which] = drift_step(cfg, h, s, m[which], which)
+        out.append(tuple(_round(x, cfg.torch_dtype) for x in m))
+    return out, torch.from_numpy(lab.astype(np.int64))
+
+
+def denoise_sequence(cfg, heads: Optional[Sequence[int]] = None, steps: Optional[int] = None,
+                     workers: int = 0):
+    """The denoising sequence step by step: yields ``make_layer(cfg, heads, s)``
+    for s = 0, 1, ..., steps - 1 (default ``cfg.steps``), keeping the fp64
+    masters between steps so that each step costs one drift pass.  With
+    ``workers > 0`` the heads are generated in that many processes (the whole
+    sequence is then produced before the first step is yielded)."""
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    if heads is None:
+        heads = range(cfg.bh)
+    heads = list(heads)
+    steps = cfg.steps if steps is None else steps
+    if workers > 0:
+        import multiprocessing
+        from concurrent.futures import ProcessPoolExecutor
+        # fresh interpreters: a forked copy of a process that already ran torch
+        # can deadlock on its thread pools
+        ctx = multiprocessing.get_context("spawn")
+        with ProcessPoolExecutor(max_workers=min(workers, len(heads)), mp_context=ctx) as ex:
+            per_head = list(ex.map(_head_sequence, [(cfg, h, steps) for h in heads]))
+        for s in range(steps):
+            yield dict(q=torch.stack([ph[0][s][0] for ph in per_head]),
+                       k=torch.stack([ph[0][s][1] for ph in per_head]),
+                       v=torch.stack([ph[0][s][2] for ph in per_head]),
+                       labels=torch.stack([ph[1] for ph in per_head]), cfg=cfg, heads=heads, step=s)
+        return
+    dt = cfg.torch_dtype
+    masters = [list(head_master(cfg, h)) for h in heads]
+    for s in range(steps):
+        if s > 0:
+            for h, m in zip(heads, masters):
+                for which in range(3):
+                    m[which] = drift_step(cfg, h, s, m[which], which)
+        yield dict(q=torch.stack([_round(m[0], dt) for m in masters]),
+                   k=torch.stack([_round(m[1], dt) for m in masters]),
+                   v=torch.stack([_round(m[2], dt) for m in masters]),
+                   labels=torch.stack([torch.from_numpy(m[3].astype(np.int64)) for m in masters]),
+                   cfg=cfg, heads=heads, step=s)
+
+
 def uniform_rows(n_rows: int, n_cols: int, seed: int, dtype=torch.float32) -> torch.Tensor:
     """Plain N(0,1) matrix, used for data-movement tests (permute / unpermute)."""
     rng = np.random.default_rng(np.random.SeedSequence([seed, 0, 99]))
