@@ -165,6 +165,7 @@ size_t svg2_permute_workspace_size(int32_t bh, int32_t n_tokens, int32_t n_clust
   if (!shape_ok(bh, n_tokens, n_clusters)) return 0;
   Carve c(nullptr);
   c.take<int32_t>((size_t)bh * sort_chunks(n_tokens) * n_clusters);
+  c.take<int32_t>((size_t)bh * n_clusters);
   return c.off;
 }
 
@@ -189,8 +190,9 @@ int svg2_permute(const int32_t* labels, int32_t bh, int32_t n_tokens, int32_t n_
 
   Carve c(workspace);
   int32_t* hist = c.take<int32_t>((size_t)bh * sort_chunks(n_tokens) * n_clusters);
+  int32_t* counts = c.take<int32_t>((size_t)bh * n_clusters);
   int st = hip_status(launch_counting_sort(labels, bh, n_tokens, n_clusters, hist, perm, offsets,
-                                           nullptr, stream));
+                                           counts, stream));
   if (st) return st;
   return hip_status(launch_gather_rows(n_tensors, src, dst, esize(dtype), head_dim, bh, n_tokens, heads,
                                        src_b_stride, src_h_stride, src_token_stride, perm, stream));

@@ -7,12 +7,12 @@
 namespace svg2 {
 
 constexpr int kMaxClusters = 4096;
-constexpr int kSortChunk = 2048;             // tokens per counting-sort chunk
+constexpr int kSortChunk = 1024;             // tokens per counting-sort chunk
 inline int sort_chunks(int n_tokens) { return (n_tokens + kSortChunk - 1) / kSortChunk; }
 
 // ----------------------------------------------------------------- sort.hip
 // Stable counting sort of labels [bh, N] in [0, n): perm, offsets [bh, n+1],
-// counts [bh, n] (counts may be null).  hist_ws holds bh * sort_chunks(N) * n ints.
+// counts [bh, n] (required).  hist_ws holds bh * sort_chunks(N) * n ints.
 hipError_t launch_counting_sort(const int32_t* labels, int bh, int N, int n, int32_t* hist_ws,
                                 int32_t* perm, int32_t* offsets, int32_t* counts, hipStream_t s);
 // dst[t][p][i][:] = src[t] row perm[p][i] of problem p (strided source), t < n_tensors <= 2.
