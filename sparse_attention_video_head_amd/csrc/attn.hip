@@ -286,16 +286,16 @@ __device__ __forceinline__ void dma_rows(const uint16_t* src, lds_u16_t* dst, co
 
 // Per wave and 32-key tile the work is two matrix-core phases, S^T = K Q^T
 // (D/16 MFMAs) and O^T += V^T P^T (D/16 MFMAs), with the softmax of the tile
-// between them on the vector ALU.  The loop is software-pipelined by one tile:
-// the scores of tile t+1 accumulate while the exponentials of tile t are
-// evaluated, so a wave keeps the matrix core and the vector ALU busy at once.
-// K and V tiles go through rings of 4 LDS buffers (tile j in slot j % 4) and
-// are loaded 3 tiles ahead, so two tiles' loads are in flight at any time:
-//   iteration t:  load K, V of tile t+3 -> slot (t+3) % 4
-//                 S[t+1] = K[t+1] Q^T  ||  softmax(S[t]);  O += V[t]^T P[t]^T
-//                 wait for the loads of tiles <= t+2, barrier
+// between them on the vector ALU.  Three work-groups share a CU (52 KB of LDS
+// and at most 168 registers each), so every SIMD holds three waves and the
+// matrix core of one overlaps the softmax of another.  K and V tiles go
+// through rings of 3 LDS buffers (tile j in slot j % 3) and are loaded 2
+// tiles ahead:
+//   iteration t:  load K, V of tile t+2 -> slot (t+2) % 3
+//                 S[t] = K[t] Q^T;  softmax;  O += V[t]^T P[t]^T
+//                 wait for the loads of tiles <= t+1, barrier
 template <int D>
-__global__ __launch_bounds__(256, 2) void k_attn_bf16(
+__global__ __launch_bounds__(256, 3) void k_attn_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     int N, const int32_t* __restrict__ q_off, int n_q, const int32_t* __restrict__ k_off, int n_k,
     const int32_t* __restrict__ sel_count, const int32_t* __restrict__ sel_idx, float scale_log2,
@@ -315,8 +315,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
   // ring slot j: K tile at [0, BN*D), V tile at [BN*D, 2*BN*D); one array per
   // slot keeps the number of distinct LDS objects that the loads write small
   // enough for the compiler to track each of them separately
-  __shared__ __attribute__((aligned(16))) uint16_t sT0[2 * BN * D], sT1[2 * BN * D], sT2[2 * BN * D],
-      sT3[2 * BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sT0[2 * BN * D], sT1[2 * BN * D], sT2[2 * BN * D];
   __shared__ int s_rs[kRangeChunk], s_rl[kRangeChunk];
 
   const int total = max_items * bh;
@@ -401,9 +400,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
     }
   };
-  // Softmax of tile `sc` (filled keys) and O^T += V^T P^T from V buffer `vb`,
-  // while the scores of the next tile accumulate into `sn` from K buffer `kn`.
-  auto step = [&](f32x16_t& sc, int filled, const lds_u16_t* vb, const lds_u16_t* kn, f32x16_t& sn) {
+  // Scores, softmax and O^T += V^T P^T of one tile (K from `kb`, V from `vb`).
+  auto step = [&](const lds_u16_t* kb, const lds_u16_t* vb, int filled) __attribute__((always_inline)) {
+    f32x16_t sc;
+    scores(kb, sc);
     if (filled < BN) {
 #pragma unroll
       for (int i = 0; i < 16; ++i)
@@ -413,7 +413,6 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
     {
-      // lanes i and i+32 hold the same query: combine their maxima
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
       mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
     }
@@ -426,8 +425,6 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
         for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
       m_ref = mx;
     }
-    // next tile's scores: independent of everything below
-    scores(kn, sn);
     const float neg = -m_ref;
     u32x4_t pw[2];
 #pragma unroll
@@ -435,8 +432,6 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
       const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[i], scale_log2, neg));
       const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[i + 1], scale_log2, neg));
       l_part += p0 + p1;
-      // k-step kk = i/8 of the P operand; key order inside a step:
-      // position h*8 + e <-> key 16 kk + 8 (e/4) + 4 h + e%4
       pw[i >> 3][(i & 7) >> 1] = pack_bf16x2(p0, p1);
     }
 #pragma unroll
@@ -451,33 +446,16 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[dt], 0, 0, 0);
       }
     }
-    // instruction order: the next tile's score MFMAs interleaved with this
-    // tile's exponentials, then the P.V MFMAs with their transposing reads
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);        // LDS reads
-#pragma unroll
-    for (int i = 0; i < KS; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x402, 7, 0);      // VALU incl. exp
-    }
-#pragma unroll
-    for (int i = 0; i < 2 * DT; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);      // LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x402, 1, 0);      // VALU
-    }
   };
 
   lds_u16_t* k0 = to_lds(sT0);
   lds_u16_t* k1 = to_lds(sT1);
   lds_u16_t* k2 = to_lds(sT2);
-  lds_u16_t* k3 = to_lds(sT3);
   lds_u16_t* v0 = k0 + BN * D;
   lds_u16_t* v1 = k1 + BN * D;
   lds_u16_t* v2 = k2 + BN * D;
-  lds_u16_t* v3 = k3 + BN * D;
 
-  // keys of tiles t, t+1, t+2 (0: no such tile)
+  // keys of tiles t, t+1 (0: no such tile)
   int key[4];
   int f0 = cur.fill<4>(BN, slot_of, key);
   if (f0 > 0) {
@@ -488,31 +466,23 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
   if (f1 > 0) {
     dma_rows<D>(Kp, k1, key, kl_off, wave);
     dma_rows<D>(Vp, v1, key, vl_off, wave);
-  }
-  int f2 = f1 > 0 ? cur.fill<4>(BN, slot_of, key) : 0;
-  if (f2 > 0) {
-    dma_rows<D>(Kp, k2, key, kl_off, wave);
-    dma_rows<D>(Vp, v2, key, vl_off, wave);
-    __builtin_amdgcn_s_waitcnt(kWaitTile);       // tiles 0 and 1 have landed
+    __builtin_amdgcn_s_waitcnt(kWaitTile);       // tile 0 has landed
   } else {
     __builtin_amdgcn_s_waitcnt(kWaitAll);
   }
   lds_barrier();
-  f32x16_t sA, sB;
-  if (active && f0 > 0) scores(k0, sA);
 
-  // iteration t: S[t] in sc, K[t+1] in kn, V[t] in vc; tile t+3 -> kd, vd
   // The loads are issued even past the end of the key list (all slots then
   // read key 0 and the tile is never used): an unconditional load keeps the
   // compiler's per-buffer tracking of them intact, so it adds no waits of its
   // own before the LDS reads.  At the loop head that tracking is lost and the
   // compiler waits for every load before the first LDS read, so the first
   // tile of each trip issues its loads after its compute (`late`).
-  auto iter = [&](auto late, f32x16_t& sc, f32x16_t& sn, const lds_u16_t* kn, const lds_u16_t* vc,
-                  lds_u16_t* kd, lds_u16_t* vd) -> bool {
-    int f3 = 0;
-    if (f2 > 0) {
-      f3 = cur.fill<4>(BN, slot_of, key);
+  auto iter = [&](auto late, const lds_u16_t* kc, const lds_u16_t* vc, lds_u16_t* kd, lds_u16_t* vd)
+      __attribute__((always_inline)) -> bool {
+    int f2 = 0;
+    if (f1 > 0) {
+      f2 = cur.fill<4>(BN, slot_of, key);
     } else {
 #pragma unroll
       for (int q = 0; q < 4; ++q) key[q] = -1;
@@ -521,24 +491,22 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
       dma_rows<D>(Kp, kd, key, kl_off, wave);
       dma_rows<D>(Vp, vd, key, vl_off, wave);
     }
-    if (active) step(sc, f0, vc, kn, sn);
+    if (active) step(kc, vc, f0);
     if constexpr (decltype(late)::value) {
       dma_rows<D>(Kp, kd, key, kl_off, wave);
       dma_rows<D>(Vp, vd, key, vl_off, wave);
     }
-    __builtin_amdgcn_s_waitcnt(kWaitTile);       // tiles <= t+2 have landed
+    __builtin_amdgcn_s_waitcnt(kWaitTile);       // tiles <= t+1 have landed
     lds_barrier();
     f0 = f1;
     f1 = f2;
-    f2 = f3;
     return f0 > 0;
   };
-  // four tiles per trip so that every LDS buffer is a distinct static array
+  // three tiles per trip so that every LDS buffer is a distinct static array
   if (f0 > 0) {
     constexpr std::true_type late{};
     constexpr std::false_type early{};
-    while (iter(late, sA, sB, k1, v0, k3, v3) && iter(early, sB, sA, k2, v1, k0, v0) &&
-           iter(early, sA, sB, k3, v2, k1, v1) && iter(early, sB, sA, k0, v3, k2, v2)) {
+    while (iter(late, k0, v0, k2, v2) && iter(early, k1, v1, k0, v0) && iter(early, k2, v2, k1, v1)) {
     }
   }
 
