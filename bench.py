@@ -445,10 +445,14 @@ def main():
     log("warm-up done")
     cold_stage, cold_ms, cold_wall = timed(False, cfg.iters, args.steps)
     log(f"cold step {cold_ms:.2f} ms (wall {cold_wall:.2f}); stages {np.round(cold_stage, 3).tolist()}")
+    # work of the cold steps' selection (the layer keeps only the last select)
+    cold_pairs = int(layer.pairs.sum().item())
+    pad_fixed128, pad_own = padding_ratios(layer)
     # warm start: centroid cache from the previous step, fewer Lloyd rounds
     step(True, args.warm_iters)
     warm_stage, warm_ms, _ = timed(True, args.warm_iters, args.steps)
     log(f"warm step {warm_ms:.2f} ms; stages {np.round(warm_stage, 3).tolist()}")
+    warm_pairs = int(layer.pairs.sum().item())
     # k-means rounds without seeding: iterations per second of the layer (Q and K)
     km = []
     for it in (1, 5):
@@ -480,8 +484,7 @@ def main():
         del o_dense
         log(f"dense attention {dense_ms:.2f} ms; sparse vs dense rel-L2 {rel_dense:.4f}")
 
-    pairs = int(layer.pairs.sum().item())
-    attn_flops = 4.0 * cfg.head_dim * pairs
+    attn_flops = 4.0 * cfg.head_dim * cold_pairs
     attn_ms = float(cold_stage[3])
     attn_tflops = attn_flops / (attn_ms * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
@@ -493,7 +496,6 @@ def main():
     permute_bytes = bhn * (6.0 * N * d * e + 8.0 * N)      # Q, K, V read + written, labels, perm
     unpermute_bytes = bhn * (2.0 * N * d * e + 4.0 * N)
     traffic = attn_traffic_per_launch()
-    pad_fixed128, pad_own = padding_ratios(layer)
     # Lloyd distance contraction: 2 d N (n_Q + n_K) flop per head and round
     # (the matrix core issues twice that for the hi/lo centroid halves)
     lloyd_flops = 2.0 * d * N * (cfg.n_q + cfg.n_k) * bhn
@@ -521,6 +523,9 @@ def main():
         "stage_ms_warm": dict(zip(["kmeans", "permute", "select", "attention", "unpermute"],
                                   [round(float(x), 4) for x in warm_stage])),
         "attn_tflops": round(attn_tflops, 2),
+        "attn_tflops_warm": round(4.0 * cfg.head_dim * warm_pairs / (float(warm_stage[3]) * 1e-3) / 1e12, 2),
+        "pairs_cold": cold_pairs,
+        "pairs_warm": warm_pairs,
         "kmeans_ms_per_iter": round(ms_per_iter, 4),
         "kmeans_iters_per_s": round(1e3 / ms_per_iter, 1) if ms_per_iter > 0 else None,
         "kmeanspp_seeding_ms": round(float(seeding_ms), 3),

@@ -240,6 +240,7 @@ size_t svg2_varblock_attn_workspace_size(int32_t bh, int32_t n_tokens, int32_t n
   // the fp32 kernel uses the smaller row block, hence the larger item list
   const int bm = attn_block_rows(false) < attn_block_rows(true) ? attn_block_rows(false) : attn_block_rows(true);
   Carve c(nullptr);
+  c.take<int32_t>((size_t)bh * n_q);
   c.take<int32_t>((size_t)bh);
   c.take<int32_t>((size_t)bh * attn_max_items(n_tokens, n_q, bm));
   return c.off;
@@ -264,12 +265,13 @@ int svg2_varblock_attn(const void* q, const void* k, const void* v, int32_t dtyp
   if (workspace_bytes < need || !workspace) return SVG2_ERR_WORKSPACE;
   if (!aligned(workspace, kAlign)) return SVG2_ERR_INVALID_ARG;
   Carve c(workspace);
+  int32_t* tiles = c.take<int32_t>((size_t)bh * n_q);
   int32_t* item_count = c.take<int32_t>((size_t)bh);
   const bool bf16 = dtype == SVG2_BF16;
   int32_t* items = c.take<int32_t>((size_t)bh * attn_max_items(n_tokens, n_q, attn_block_rows(bf16)));
   return hip_status(launch_varblock_attn(q, k, v, bf16, bh, n_tokens, head_dim, q_offsets, n_q, k_offsets,
-                                         n_k, sel_count, sel_idx, scale, out, lse, item_count, items,
-                                         stream));
+                                         n_k, sel_count, sel_idx, scale, out, lse, tiles, item_count,
+                                         items, stream));
 }
 
 // ------------------------------------------------------------------ unpermute

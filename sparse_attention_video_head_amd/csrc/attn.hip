@@ -30,23 +30,85 @@ constexpr int kAttnF32BM = 64;   // query rows per work item (fp32 kernel)
 int attn_block_rows(bool bf16) { return bf16 ? kAttnBM : kAttnF32BM; }
 
 // ---------------------------------------------------------------- planning
-// One work-group per problem: the list of (cluster, slab) items.
+// The items of one problem differ in length by orders of magnitude (a Q-cluster
+// may select a handful of keys or nearly all of them), and the launch ends
+// with its slowest work-group.  The plan therefore hands out the items of each
+// problem longest key list first, so that the short ones fill the tail.
+//
+// Key tiles per Q-cluster: one wave per cluster, capped at kSortTilesMax for
+// the sort key.
+constexpr int kSortTilesMax = (1 << 19) - 1;
+
+__global__ __launch_bounds__(256) void k_attn_lengths(const int32_t* __restrict__ k_off, int n_k, int N,
+                                                      const int32_t* __restrict__ sel_count,
+                                                      const int32_t* __restrict__ sel_idx, int n_q,
+                                                      int tile, int32_t* __restrict__ tiles) {
+  const int p = blockIdx.y;
+  const int i = blockIdx.x * (blockDim.x / kWave) + (int)(threadIdx.x / kWave);
+  if (i >= n_q) return;
+  const int lane = lane_id();
+  const int32_t* ko = k_off + (size_t)p * (n_k + 1);
+  const int32_t* sel = sel_idx + ((size_t)p * n_q + i) * n_k;
+  const int cnt = clampi(sel_count[(size_t)p * n_q + i], 0, n_k);
+  long long keys = 0;
+  for (int j = lane; j < cnt; j += kWave) {
+    const int c = sel[j];
+    if ((unsigned)c < (unsigned)n_k) {
+      const int a = clampi(ko[c], 0, N);
+      keys += clampi(ko[c + 1], a, N) - a;
+    }
+  }
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) keys += __shfl_xor(keys, o);
+  if (lane == 0) tiles[(size_t)p * n_q + i] = (int32_t)min((keys + tile - 1) / tile, (long long)kSortTilesMax);
+}
+
+// One work-group per problem: the list of (cluster, slab) items, clusters in
+// decreasing order of key tiles (ties: lower cluster index first).  The order
+// comes from a bitonic sort in LDS of (tiles << 12 | 4095 - cluster).
 __global__ __launch_bounds__(1024) void k_attn_plan(const int32_t* __restrict__ q_off, int n_q, int N,
                                                     int bm, int max_items,
+                                                    const int32_t* __restrict__ tiles,
                                                     int32_t* __restrict__ item_count,
                                                     int32_t* __restrict__ items) {
   __shared__ int32_t scratch[17];
+  __shared__ uint32_t order[kMaxClusters];
   const int p = blockIdx.x;
   const int32_t* qo = q_off + (size_t)p * (n_q + 1);
-  int nb[4];
+  int P = 64;
+  while (P < n_q) P <<= 1;
+  for (int i = threadIdx.x; i < P; i += blockDim.x)
+    order[i] = i < n_q ? ((uint32_t)tiles[(size_t)p * n_q + i] << 12) | (uint32_t)(kMaxClusters - 1 - i) : 0u;
+  __syncthreads();
+  // descending bitonic sort; the padding entries (0) end up past n_q because
+  // every real entry with i < 4095 is positive
+  for (int k = 2; k <= P; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int t = threadIdx.x; t < P / 2; t += blockDim.x) {
+        const int a = 2 * t - (t & (j - 1));
+        const int b = a + j;
+        const uint32_t x = order[a], y = order[b];
+        const bool first_larger = (a & k) == 0;
+        if (first_larger ? x < y : x > y) {
+          order[a] = y;
+          order[b] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  int nb[4], cl[4];
   int local = 0;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int i = 4 * threadIdx.x + e;
+    const int s = 4 * threadIdx.x + e;
     nb[e] = 0;
-    if (i < n_q) {
+    cl[e] = 0;
+    if (s < n_q) {
+      const int i = kMaxClusters - 1 - (int)(order[s] & (kMaxClusters - 1));
       const int a = clampi(qo[i], 0, N), b = clampi(qo[i + 1], a, N);
       nb[e] = (b - a + bm - 1) / bm;
+      cl[e] = i;
     }
     local += nb[e];
   }
@@ -54,10 +116,8 @@ __global__ __launch_bounds__(1024) void k_attn_plan(const int32_t* __restrict__ 
   int base = block_exclusive_scan(local, scratch, &total);
   int32_t* it = items + (size_t)p * max_items;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int i = 4 * threadIdx.x + e;
-    for (int r = 0; r < nb[e] && base < max_items; ++r, ++base) it[base] = i | (r << 12);
-  }
+  for (int e = 0; e < 4; ++e)
+    for (int r = 0; r < nb[e] && base < max_items; ++r, ++base) it[base] = cl[e] | (r << 12);
   if (threadIdx.x == 0) item_count[p] = min(total, max_items);
 }
 
@@ -613,12 +673,14 @@ __global__ __launch_bounds__(128) void k_attn_f32(
 hipError_t launch_varblock_attn(const void* q, const void* k, const void* v, bool bf16, int bh,
                                 int N, int d, const int32_t* q_off, int n_q, const int32_t* k_off,
                                 int n_k, const int32_t* sel_count, const int32_t* sel_idx,
-                                float scale, void* out, float* lse, int32_t* item_count_ws,
-                                int32_t* items_ws, hipStream_t s) {
+                                float scale, void* out, float* lse, int32_t* tiles_ws,
+                                int32_t* item_count_ws, int32_t* items_ws, hipStream_t s) {
   const int bm = attn_block_rows(bf16);
   const int max_items = attn_max_items(N, n_q, bm);
-  hipLaunchKernelGGL(k_attn_plan, dim3(bh), dim3(1024), 0, s, q_off, n_q, N, bm, max_items, item_count_ws,
-                     items_ws);
+  hipLaunchKernelGGL(k_attn_lengths, dim3((n_q + 3) / 4, bh), dim3(256), 0, s, k_off, n_k, N, sel_count,
+                     sel_idx, n_q, bf16 ? kAttnBN : 32, tiles_ws);
+  hipLaunchKernelGGL(k_attn_plan, dim3(bh), dim3(1024), 0, s, q_off, n_q, N, bm, max_items, tiles_ws,
+                     item_count_ws, items_ws);
   const dim3 grid(max_items, bh);
   const int total = max_items * bh;
   constexpr int span = kXcds * kXcdChunk;

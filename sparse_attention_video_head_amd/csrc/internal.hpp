@@ -55,10 +55,11 @@ hipError_t launch_select_topp(const float* cq, const int32_t* q_counts, int n_q,
 // ----------------------------------------------------------------- attn.hip
 int attn_block_rows(bool bf16);
 inline int attn_max_items(int N, int n_q, int bm) { return (N + bm - 1) / bm + n_q; }
+// workspace: tiles [bh, n_q], item_count [bh], items [bh, attn_max_items] (all int32)
 hipError_t launch_varblock_attn(const void* q, const void* k, const void* v, bool bf16, int bh,
                                 int N, int d, const int32_t* q_off, int n_q, const int32_t* k_off,
                                 int n_k, const int32_t* sel_count, const int32_t* sel_idx,
-                                float scale, void* out, float* lse, int32_t* item_count_ws,
-                                int32_t* items_ws, hipStream_t s);
+                                float scale, void* out, float* lse, int32_t* tiles_ws,
+                                int32_t* item_count_ws, int32_t* items_ws, hipStream_t s);
 
 }  // namespace svg2

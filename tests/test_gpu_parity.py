@@ -170,6 +170,8 @@ def _attn_case(dt, d, bh, N, n_q, n_k, top_p, seed, empty_rows=False):
 @pytest.mark.parametrize("dt,d,N,n_q,n_k,top_p", [
     ("bf16", 128, 3000, 20, 50, 0.9), ("bf16", 128, 4099, 7, 130, 0.6), ("bf16", 64, 2500, 30, 40, 0.95),
     ("f32", 64, 2000, 16, 32, 0.9), ("f32", 128, 1500, 9, 25, 0.7), ("bf16", 128, 700, 1, 1, 1.0),
+    # many Q-clusters: the plan's longest-first sort over more than 1024 clusters, and at the limit
+    ("bf16", 64, 6000, 1500, 200, 0.8), ("bf16", 128, 8192, 4096, 300, 0.9),
 ])
 def test_varblock_attn_vs_oracle(dt, d, N, n_q, n_k, top_p):
     bh = 2
