@@ -451,13 +451,29 @@ __global__ __launch_bounds__(256, 3) void k_attn_bf16(
 
   // S^T for the 32 keys of a K tile; lane holds query `col` and keys
   // (i/4)*8 + half*4 + i%4
-  auto scores = [&](const lds_u16_t* kb, f32x16_t& s) {
+  // The K fragments are read kAhead k-steps ahead of their MFMA, so the LDS
+  // latency overlaps the matrix core instead of sitting before every step.
+  // The scheduling groups pin that order (mask 0x100: LDS reads, 0x008: MFMA);
+  // left alone, the scheduler pairs each read with its MFMA and waits on it.
+  auto scores = [&](const lds_u16_t* kb, f32x16_t& s) __attribute__((always_inline)) {
+    constexpr int kAhead = KS < 2 ? KS : 2;
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = 0.f;
+    bf16x8_t a[KS];
+#pragma unroll
+    for (int ks = 0; ks < kAhead; ++ks) a[ks] = *(const __attribute__((address_space(3))) bf16x8_t*)(kb + koff[ks]);
+    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8_t a = *(const __attribute__((address_space(3))) bf16x8_t*)(kb + koff[ks]);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s, 0, 0, 0);
+      if (ks + kAhead < KS)
+        a[ks + kAhead] = *(const __attribute__((address_space(3))) bf16x8_t*)(kb + koff[ks + kAhead]);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qf[ks], s, 0, 0, 0);
+      if (ks + kAhead < KS) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
     }
   };
   // Scores, softmax and O^T += V^T P^T of one tile (K from `kb`, V from `vb`).
@@ -465,9 +481,12 @@ __global__ __launch_bounds__(256, 3) void k_attn_bf16(
     f32x16_t sc;
     scores(kb, sc);
     if (filled < BN) {
+      // key of score i: (i/4)*8 + 4*half + i%4; compared against the list end
+      // shifted by this lane's half, so every compare takes an inline constant
+      const int lim = filled - 4 * half;
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        if ((i >> 2) * 8 + half * 4 + (i & 3) >= filled) sc[i] = -__builtin_inff();
+        if ((i >> 2) * 8 + (i & 3) >= lim) sc[i] = -__builtin_inff();
     }
     float mx = sc[0];
 #pragma unroll
@@ -494,17 +513,27 @@ __global__ __launch_bounds__(256, 3) void k_attn_bf16(
       l_part += p0 + p1;
       pw[i >> 3][(i & 7) >> 1] = pack_bf16x2(p0, p1);
     }
+    // V^T fragments: two transposing reads per MFMA, issued kAhead MFMAs early
+    constexpr int NV = 2 * DT;
+    constexpr int kAhead = NV < 2 ? NV : 2;
+    auto vread = [&](int j) __attribute__((always_inline)) {
+      const int kk = j / DT, dt = j % DT;
+      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb + (voff[dt] + 16 * kk * D)));
+      const s16x4_t hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb + (voff[dt] + (16 * kk + 8) * D)));
+      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8_t va[NV];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw[kk]);
+    for (int j = 0; j < kAhead; ++j) va[j] = vread(j);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb + (voff[dt] + 16 * kk * D)));
-        const s16x4_t hi =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb + (voff[dt] + (16 * kk + 8) * D)));
-        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[dt], 0, 0, 0);
-      }
+    for (int j = 0; j < NV; ++j) {
+      if (j + kAhead < NV) va[j + kAhead] = vread(j + kAhead);
+      const int kk = j / DT, dt = j % DT;
+      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j], __builtin_bit_cast(bf16x8_t, pw[kk]), o[dt], 0, 0, 0);
+      if (j + kAhead < NV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
   };
 
