@@ -28,6 +28,46 @@ PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz)
 PEAK_F32_TFLOPS = 157.3
 
 
+PEAK_CLOCK_MHZ = 2400.0         # the clock the published peaks assume
+
+
+class ClockSampler:
+    """Samples the shader clock (``rocm-smi -g --json``, in a child process)
+    every ~0.2 s between start() and stop(); under sustained matrix-core load
+    the clock drops well below the one the published peak assumes."""
+
+    def __init__(self):
+        self.mhz, self._stop, self._th = [], False, None
+
+    def _run(self):
+        import re
+        import subprocess
+        while not self._stop:
+            try:
+                out = subprocess.run(["rocm-smi", "-g", "--json"], capture_output=True, text=True,
+                                     timeout=10).stdout
+                m = re.search(r"\((\d+)\s*Mhz\)", out, re.IGNORECASE)
+                if m:
+                    self.mhz.append(int(m.group(1)))
+            except Exception:
+                return
+            time.sleep(0.2)
+
+    def start(self):
+        import threading
+        self._th = threading.Thread(target=self._run, daemon=True)
+        self._th.start()
+
+    def stop(self):
+        self._stop = True
+        if self._th:
+            self._th.join(timeout=15)
+        if not self.mhz:
+            return None
+        v = sorted(self.mhz)
+        return {"samples": len(v), "min": v[0], "median": v[len(v) // 2], "max": v[-1]}
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -65,8 +105,9 @@ def attn_traffic_per_launch():
         sha = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()[:16]
         fields = {}
         for line in open(TRAFFIC_PROFILE):
-            if ":" in line and line.startswith("- "):
-                k, v = line[2:].split(":", 1)
+            # "- key: value" lines; the hash key itself holds a colon ("[:16]")
+            if ": " in line and line.startswith("- "):
+                k, v = line[2:].split(": ", 1)
                 fields[k.strip()] = v.strip()
         if fields.get("attn.hip sha256[:16]") != sha:
             return None
@@ -443,6 +484,8 @@ def main():
         step(False, cfg.iters)
     torch.cuda.synchronize()
     log("warm-up done")
+    clock = ClockSampler()
+    clock.start()
     cold_stage, cold_ms, cold_wall = timed(False, cfg.iters, args.steps)
     log(f"cold step {cold_ms:.2f} ms (wall {cold_wall:.2f}); stages {np.round(cold_stage, 3).tolist()}")
     # work of the cold steps' selection (the layer keeps only the last select)
@@ -451,7 +494,8 @@ def main():
     # warm start: centroid cache from the previous step, fewer Lloyd rounds
     step(True, args.warm_iters)
     warm_stage, warm_ms, _ = timed(True, args.warm_iters, args.steps)
-    log(f"warm step {warm_ms:.2f} ms; stages {np.round(warm_stage, 3).tolist()}")
+    gpu_clock = clock.stop()
+    log(f"warm step {warm_ms:.2f} ms; stages {np.round(warm_stage, 3).tolist()}; shader clock MHz {gpu_clock}")
     warm_pairs = int(layer.pairs.sum().item())
     # k-means rounds without seeding: iterations per second of the layer (Q and K)
     km = []
@@ -544,6 +588,9 @@ def main():
                      "achieved": round(attn_tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / peak, 4), "traffic": traffic,
                      "flops_per_launch": attn_flops},
+        # shader clock over the timed steps, and the peak scaled to its median
+        "gpu_clock_mhz": gpu_clock,
+        "peak_at_measured_clock": (round(peak * gpu_clock["median"] / PEAK_CLOCK_MHZ, 1) if gpu_clock else None),
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(host, cfg, top_p, args.cpu_budget)

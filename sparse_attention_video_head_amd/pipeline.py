@@ -5,8 +5,8 @@
     ->  centroid scores + top-p  ->  variable-block attention  ->  un-permute
 
 Buffers (outputs and workspaces) are allocated once per shape, so repeated
-calls launch kernels only.  The Q-side and K-side k-means may run on two
-streams.  The centroid cache of the method is the ``centroids_q`` /
+calls launch kernels only.  The Q side's k-means and permutation may run on a
+second stream, beside the K side's.  The centroid cache of the method is the ``centroids_q`` /
 ``centroids_k`` state: ``run(..., warm=True)`` warm-starts from it.
 """
 from __future__ import annotations
@@ -78,10 +78,25 @@ class SVG2Layer:
         main.wait_stream(self.side)
 
     def permute(self, q, k, v):
-        B.permute(self.labels_q, self.n_q, q, outs=[self.qp], perm=self.perm_q, offsets=self.off_q,
-                  workspace=self.ws_pq)
-        B.permute(self.labels_k, self.n_k, k, v, outs=[self.kp, self.vp], perm=self.perm_k,
-                  offsets=self.off_k, workspace=self.ws_pk)
+        def side_q():
+            B.permute(self.labels_q, self.n_q, q, outs=[self.qp], perm=self.perm_q, offsets=self.off_q,
+                      workspace=self.ws_pq)
+
+        def side_k():
+            B.permute(self.labels_k, self.n_k, k, v, outs=[self.kp, self.vp], perm=self.perm_k,
+                      offsets=self.off_k, workspace=self.ws_pk)
+
+        if self.side is None:
+            side_q()
+            side_k()
+            return
+        # the Q side on the second stream: its small sort kernels overlap the K/V row moves
+        main = torch.cuda.current_stream(self.dev)
+        self.side.wait_stream(main)
+        with torch.cuda.stream(self.side):
+            side_q()
+        side_k()
+        main.wait_stream(self.side)
 
     def select(self, top_p: float):
         B.select_topp(self.cq, self.counts_q, self.ck, self.counts_k, top_p, scale=self.scale,
