@@ -55,6 +55,7 @@ struct KmeansWs {
   int32_t* hist;
   int32_t* perm;
   int32_t* offsets;
+  double* partial;    // bh * (n + mean_chunks(N)) * d: per-chunk centroid sums
 };
 
 KmeansWs carve_kmeans(Carve& c, int bh, int N, int d, int n) {
@@ -71,6 +72,7 @@ KmeansWs carve_kmeans(Carve& c, int bh, int N, int d, int n) {
   w.hist = c.take<int32_t>((size_t)bh * sort_chunks(N) * n);
   w.perm = c.take<int32_t>(bN);
   w.offsets = c.take<int32_t>((size_t)bh * (n + 1));
+  w.partial = c.take<double>((size_t)bh * (n + mean_chunks(N)) * d);
   return w;
 }
 
@@ -154,7 +156,7 @@ int svg2_kmeans(const void* x, int32_t dtype, int32_t bh, int32_t n_tokens, int3
     if (st) return st;
     st = hip_status(launch_counting_sort(labels, bh, N, n, w.hist, w.perm, w.offsets, counts, stream));
     if (st) return st;
-    st = hip_status(launch_centroid_mean(x, bf16, bh, N, d, n, w.perm, w.offsets, centroids, stream));
+    st = hip_status(launch_centroid_mean(x, bf16, bh, N, d, n, w.perm, w.offsets, w.partial, centroids, stream));
     if (st) return st;
   }
   return SVG2_OK;

@@ -42,8 +42,11 @@ hipError_t launch_assign(const void* x, bool bf16, int bh, int N, int d, int n, 
                          const uint16_t* c_hi, const uint16_t* c_lo, const float* c_norm,
                          int32_t* labels, float* min_dist, hipStream_t s);
 // centroid c = mean of the rows perm[offsets[c] .. offsets[c+1]); empty keeps c.
+// partial_ws: bh * (n + mean_chunks(N)) * d doubles.
+constexpr int kMeanChunk = 512;              // sorted positions per partial-sum work-group
+inline int mean_chunks(int n_tokens) { return (n_tokens + kMeanChunk - 1) / kMeanChunk; }
 hipError_t launch_centroid_mean(const void* x, bool bf16, int bh, int N, int d, int n,
-                                const int32_t* perm, const int32_t* offsets, float* c,
+                                const int32_t* perm, const int32_t* offsets, double* partial_ws, float* c,
                                 hipStream_t s);
 
 // --------------------------------------------------------------- select.hip

@@ -777,73 +777,118 @@ hipError_t launch_assign(const void* x, bool bf16, int bh, int N, int d, int n, 
 // ======================================================================
 // Lloyd update: centroid = mean of members (segmented over the sorted order)
 // ======================================================================
-// One work-group per (cluster, problem).  A row is read as 16-byte vectors
-// by VPR threads; RL = 256 / VPR rows are in flight per step (two steps
-// unrolled), each thread summing its 16-byte column chunk over rows
-// offsets[c] + rl, + RL, ... in fp64; the RL partial sums are then combined
-// in a fixed order, so the result is deterministic.
+// Centroid c = mean of the rows perm[offsets[c] .. offsets[c+1]).
+// Cluster sizes are heavy-tailed, so the work is cut along the sorted order
+// instead of per cluster: work-group k sums the rows of sorted positions
+// [512 k, 512 (k+1)), one cluster segment after the other, and writes one
+// fp64 partial sum per (cluster c, chunk k) to slot c + k (unique, because
+// every cluster is a contiguous, increasing range of the sorted order).  A
+// second kernel adds each cluster's partials in chunk order.  Every sum runs
+// in a fixed order, so the result is the same run to run.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void k_centroid_mean(const T* __restrict__ X, int N, int n,
-                                                       const int32_t* __restrict__ perm,
-                                                       const int32_t* __restrict__ offsets,
-                                                       float* __restrict__ C) {
+__global__ __launch_bounds__(256) void k_centroid_partial(const T* __restrict__ X, int N, int n,
+                                                          const int32_t* __restrict__ perm,
+                                                          const int32_t* __restrict__ offsets,
+                                                          double* __restrict__ partial) {
   constexpr int EPV = 16 / sizeof(T);          // elements per 16-byte vector
-  constexpr int VPR = D / EPV;                 // vectors per row
-  constexpr int RL = 256 / VPR;                // rows per step
-  __shared__ double red[RL][D];
-  const int c = blockIdx.x, p = blockIdx.y;
-  const int a = offsets[(size_t)p * (n + 1) + c];
-  const int b = offsets[(size_t)p * (n + 1) + c + 1];
-  if (b <= a) return;                        // empty cluster keeps its centroid
-  const int cv = threadIdx.x % VPR, rl = threadIdx.x / VPR;
-  const T* Xp = X + (size_t)p * N * D + cv * EPV;
+  constexpr int VPR = D / EPV;                 // lanes per row
+  constexpr int G = 256 / VPR;                 // row groups
+  constexpr int U = 4;                         // rows in flight per lane
+  __shared__ double red[G][D];
+  __shared__ int32_t s_perm[kMeanChunk];
+  __shared__ int s_c0;
+  const int p = blockIdx.y, k = blockIdx.x;
+  const int chunks = gridDim.x;
+  const int j0 = k * kMeanChunk, j1 = min(j0 + kMeanChunk, N);
+  const int32_t* off = offsets + (size_t)p * (n + 1);
   const int32_t* pp = perm + (size_t)p * N;
-  double acc[EPV];
-#pragma unroll
-  for (int e = 0; e < EPV; ++e) acc[e] = 0.0;
-  auto add_row = [&](const u32x4_t v) {
-    if (sizeof(T) == 2) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[2 * e] += (double)bf16_lo(v[e]);
-        acc[2 * e + 1] += (double)bf16_hi(v[e]);
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] += (double)__uint_as_float(v[e]);
+  for (int j = threadIdx.x; j < j1 - j0; j += blockDim.x) s_perm[j] = clampi(pp[j0 + j], 0, N - 1);
+  if (threadIdx.x == 0) {
+    // the cluster holding position j0: the largest c < n with offsets[c] <= j0
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (off[mid] <= j0) lo = mid; else hi = mid - 1;
     }
-  };
-  int i = a + rl;
-  for (; i + RL < b; i += 2 * RL) {
-    const int t0 = pp[i], t1 = pp[i + RL];
-    const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(Xp + (size_t)t0 * D);
-    const u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(Xp + (size_t)t1 * D);
-    add_row(v0);
-    add_row(v1);
+    s_c0 = lo;
   }
-  if (i < b) add_row(*reinterpret_cast<const u32x4_t*>(Xp + (size_t)pp[i] * D));
-#pragma unroll
-  for (int e = 0; e < EPV; ++e) red[rl][cv * EPV + e] = acc[e];
   __syncthreads();
-  if (threadIdx.x < D) {
-    double s = 0.0;
+  const int cv = threadIdx.x % VPR, g = threadIdx.x / VPR;
+  const T* Xp = X + (size_t)p * N * D + cv * EPV;
+  double* part = partial + (size_t)p * (n + chunks) * D;
+  int c = s_c0, pos = j0;
+  while (pos < j1 && c < n) {
+    const int end = min(max(off[c + 1], pos), j1);
+    double acc[EPV];
 #pragma unroll
-    for (int r = 0; r < RL; ++r) s += red[r][threadIdx.x];
-    C[((size_t)p * n + c) * D + threadIdx.x] = (float)(s / (double)(b - a));
+    for (int e = 0; e < EPV; ++e) acc[e] = 0.0;
+    for (int i = pos + g; i < end; i += G * U) {
+      u32x4_t v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int r = i + u * G;
+        if (r < end) v[u] = *reinterpret_cast<const u32x4_t*>(Xp + (size_t)s_perm[r - j0] * D);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (i + u * G >= end) break;
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += (double)bf16_lo(v[u][e]);
+            acc[2 * e + 1] += (double)bf16_hi(v[u][e]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[e] += (double)__uint_as_float(v[u][e]);
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) red[g][cv * EPV + e] = acc[e];
+    __syncthreads();
+    if (end > pos && threadIdx.x < D) {
+      double sum = 0.0;
+#pragma unroll
+      for (int q = 0; q < G; ++q) sum += red[q][threadIdx.x];
+      part[(size_t)(c + k) * D + threadIdx.x] = sum;
+    }
+    __syncthreads();
+    pos = max(end, pos);
+    // next cluster holding `pos` (empty clusters end where they start)
+    ++c;
+    while (c < n && off[c + 1] <= pos) ++c;
   }
 }
 
+template <int D>
+__global__ __launch_bounds__(D) void k_centroid_finish(int n, int chunks, const int32_t* __restrict__ offsets,
+                                                       const double* __restrict__ partial,
+                                                       float* __restrict__ C) {
+  const int c = blockIdx.x, p = blockIdx.y;
+  const int32_t* off = offsets + (size_t)p * (n + 1);
+  const int a = off[c], b = off[c + 1];
+  if (b <= a) return;                          // empty cluster keeps its centroid
+  const double* part = partial + (size_t)p * (n + chunks) * D;
+  const int k0 = a / kMeanChunk, k1 = (b - 1) / kMeanChunk;
+  double sum = 0.0;
+  for (int k = k0; k <= k1; ++k) sum += part[(size_t)(c + k) * D + threadIdx.x];
+  C[((size_t)p * n + c) * D + threadIdx.x] = (float)(sum / (double)(b - a));
+}
+
 hipError_t launch_centroid_mean(const void* x, bool bf16, int bh, int N, int d, int n,
-                                const int32_t* perm, const int32_t* offsets, float* c,
+                                const int32_t* perm, const int32_t* offsets, double* partial_ws, float* c,
                                 hipStream_t s) {
-  const dim3 grid(n, bh);
-#define SVG2_MEAN(T, D)                                                                           \
-  hipLaunchKernelGGL((k_centroid_mean<T, D>), grid, dim3(256), 0, s, static_cast<const T*>(x), N, n, \
-                     perm, offsets, c)
+  const int chunks = mean_chunks(N);
+  const dim3 grid(chunks, bh);
+#define SVG2_MEAN(T, D)                                                                               \
+  hipLaunchKernelGGL((k_centroid_partial<T, D>), grid, dim3(256), 0, s, static_cast<const T*>(x), N, n, \
+                     perm, offsets, partial_ws);                                                      \
+  hipLaunchKernelGGL((k_centroid_finish<D>), dim3(n, bh), dim3(D), 0, s, n, chunks, offsets, partial_ws, c)
   if (bf16) {
-    if (d == 128) SVG2_MEAN(uint16_t, 128); else SVG2_MEAN(uint16_t, 64);
+    if (d == 128) { SVG2_MEAN(uint16_t, 128); } else { SVG2_MEAN(uint16_t, 64); }
   } else {
-    if (d == 128) SVG2_MEAN(float, 128); else SVG2_MEAN(float, 64);
+    if (d == 128) { SVG2_MEAN(float, 128); } else { SVG2_MEAN(float, 64); }
   }
 #undef SVG2_MEAN
   return hipGetLastError();
