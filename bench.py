@@ -90,6 +90,10 @@ def parse():
                     help="warm-start study on the denoising sequence instead of the layer step")
     ap.add_argument("--agree-heads", type=int, default=4,
                     help="--denoise: heads whose labels are compared (ARI, matched agreement)")
+    ap.add_argument("--driver", action="store_true",
+                    help="the denoising run through the driver (dense warm-up, cold, warm) against dense "
+                         "attention on every step")
+    ap.add_argument("--dense-fraction", type=float, default=0.1, help="--driver: leading dense share of the steps")
     return ap.parse_args()
 
 
@@ -392,6 +396,96 @@ def denoise_cpu_baseline(keep, cfg, args):
             "gpu_warm_J_over_oracle_cold_J": round(j_gpu / j_orc, 5)}
 
 
+def driver_run(args):
+    """The denoising run around the path: the Hunyuan-shaped layer over the
+    drifting 10-step sequence through DenoiseDriver (the leading
+    --dense-fraction of the steps dense, then a cold start, then warm starts
+    from the centroid cache), against the library's dense attention on every
+    step.  Per-step HIP-event times; the whole run is also extrapolated to 50
+    steps from the per-mode means."""
+    import numpy as np
+    import torch
+    from sparse_attention_video_head_amd import binding as B
+    from sparse_attention_video_head_amd import synth
+    from sparse_attention_video_head_amd.driver import DenoiseDriver, dense_steps
+
+    cfg = synth.CONFIGS["denoise"]
+    dev = torch.device("cuda:0")
+    log(f"libsvg2 {B.version()}; driver over {cfg.steps} steps, bh={cfg.bh} N={cfg.n_tokens} d={cfg.head_dim} "
+        f"n_q={cfg.n_q} n_k={cfg.n_k}, dense share {args.dense_fraction}, warm {args.warm_iters} rounds")
+    drv = DenoiseDriver(cfg.bh, cfg.n_tokens, cfg.head_dim, cfg.torch_dtype, cfg.n_q, cfg.n_k, cfg.steps,
+                        top_p=1.0, dense_fraction=args.dense_fraction, cold_iters=cfg.iters,
+                        warm_iters=args.warm_iters, seed=cfg.seed, device=dev)
+    e = drv.engine
+    E = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        a, b = E(), E()
+        torch.cuda.synchronize()
+        a.record()
+        r = fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b), r
+
+    gen = synth.denoise_sequence(cfg, workers=min(16, os.cpu_count() or 1))
+    t0 = time.time()
+    seq = [next(gen)]
+    top_p = args.top_p
+    rows, dense_out = [], torch.empty(cfg.bh, cfg.n_tokens, cfg.head_dim, dtype=cfg.torch_dtype, device=dev)
+    for s in range(cfg.steps):
+        host = seq[-1] if s == 0 else next(gen)
+        x = [host[c].to(dev) for c in "qkv"]
+        if s == 0:
+            log(f"inputs of step 0 in {time.time() - t0:.1f}s")
+            # warm-up launches, and top-p bisected on a cold clustering of step 0
+            e.dense(*x, out=dense_out)
+            e.kmeans(x[0], x[1], cfg.iters, False, 1, 2)
+            e.permute(*x)
+            if top_p is None:
+                lo, hi = 0.01, 1.0
+                for _ in range(30):
+                    top_p = 0.5 * (lo + hi)
+                    e.select(top_p)
+                    dens = e.density()
+                    if abs(dens - args.density) <= 0.005:
+                        break
+                    lo, hi = (lo, top_p) if dens > args.density else (top_p, hi)
+            drv.top_p = top_p
+            drv.reset()
+        mode = drv.mode(0, s)
+        ms, out = timed(lambda: drv(0, s, *x))
+        out = out.clone()
+        dms, _ = timed(lambda: e.dense(*x, out=dense_out))
+        rel = float(torch.linalg.vector_norm(out.float() - dense_out.float()).item()
+                    / torch.linalg.vector_norm(dense_out.float()).item())
+        rows.append({"step": s, "mode": mode, "ms": round(ms, 3), "dense_ms": round(dms, 3),
+                     "rel_l2_vs_dense": round(rel, 5)})
+        log(f"step {s} {mode}: {ms:.2f} ms (dense {dms:.2f} ms), rel-L2 vs dense {rel:.4f}")
+    run_ms = sum(r["ms"] for r in rows)
+    dense_ms = sum(r["dense_ms"] for r in rows)
+    mean = lambda m: float(np.mean([r["ms"] for r in rows if r["mode"] == m]))
+    d50 = dense_steps(50, args.dense_fraction)
+    dense_mean = float(np.mean([r["dense_ms"] for r in rows]))
+    run50 = d50 * dense_mean + mean("cold") + (50 - d50 - 1) * mean("warm")
+    res = {
+        "metric": "attention time over a denoising run, all-dense / this driver",
+        "value": round(dense_ms / run_ms, 3), "unit": "x", "n_gpus": 1, "higher_is_better": True,
+        "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": "denoise-hunyuan720p-driver", "heads": cfg.bh, "n_tokens": cfg.n_tokens,
+                   "head_dim": cfg.head_dim, "n_q": cfg.n_q, "n_k": cfg.n_k, "steps": cfg.steps,
+                   "dense_fraction": args.dense_fraction, "cold_iters": cfg.iters, "warm_iters": args.warm_iters,
+                   "top_p": round(top_p, 6)},
+        "run_ms": round(run_ms, 3), "all_dense_ms": round(dense_ms, 3),
+        "mean_ms": {m: round(mean(m), 3) for m in ("dense", "cold", "warm") if any(r["mode"] == m for r in rows)},
+        "extrapolated_50_steps": {"dense_steps": d50, "run_ms": round(run50, 1),
+                                  "all_dense_ms": round(50 * dense_mean, 1),
+                                  "speedup": round(50 * dense_mean / run50, 3)},
+        "steps_detail": rows,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -403,6 +497,9 @@ def main():
         sys.exit(2)
     if args.denoise:
         denoise_run(args)
+        return
+    if args.driver:
+        driver_run(args)
         return
 
     import numpy as np

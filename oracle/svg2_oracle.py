@@ -433,3 +433,54 @@ def layer(q, k, v, n_q: int, n_k: int, iters: int, top_p: float,
 def density(pairs_per_head, n_tokens: int) -> float:
     """Share of the N^2 (query, key) pairs per head that the selection computes."""
     return float(np.sum(pairs_per_head)) / (len(pairs_per_head) * float(n_tokens) ** 2)
+
+
+# --------------------------------------------------------------------------
+# Around the layer: one layer along a denoising run  [wiki: Method, stage (1)
+# and its dense warm-up paragraph; Key claims, §4.3 / Fig. 7(a)]
+# reading: "the first ~10% of steps run dense" = step s (0-based) is dense
+# when s < fraction * steps, less a 1e-9 guard so that float rounding of the
+# product never adds a step (5 of 50 steps, 1 of 10).  The first sparse step
+# of a layer seeds with k-means++ and runs the cold rounds; every later step
+# starts from the centroids the layer ended the previous step with (the
+# centroid cache) and runs the warm rounds.  Dense steps leave the cache
+# untouched.
+# --------------------------------------------------------------------------
+def is_dense_step(step: int, steps: int, fraction: float) -> bool:
+    return step < fraction * steps - 1e-9
+
+
+@dataclass
+class DenoiseResult:
+    outs: list        # per step: [N, d] output in the input's token order
+    modes: list       # per step: "dense", "cold" or "warm"
+    layers: list      # per step: LayerResult, or None on dense steps
+
+
+def denoise_layer(steps_qkv, n_q: int, n_k: int, top_p, fraction: float, cold_iters: int, warm_iters: int,
+                  seed_q: int = 0, seed_k: int = 1, problem: int = 0) -> DenoiseResult:
+    """One head of one layer over the steps of a run; ``steps_qkv`` lists the
+    (q, k, v) of every step and ``top_p`` is a number or a function of the step."""
+    steps = len(steps_qkv)
+    res = DenoiseResult(outs=[], modes=[], layers=[])
+    cache = None
+    for s, (q, k, v) in enumerate(steps_qkv):
+        if is_dense_step(s, steps, fraction):
+            d = np.asarray(q).shape[1]
+            out, _ = softmax_attention_rows(q, k, v, 1.0 / math.sqrt(d))
+            res.outs.append(out)
+            res.modes.append("dense")
+            res.layers.append(None)
+            continue
+        p = top_p(s) if callable(top_p) else top_p
+        if cache is None:
+            r = layer(q, k, v, n_q, n_k, cold_iters, p, seed_q, seed_k, problem)
+            res.modes.append("cold")
+        else:
+            r = layer(q, k, v, n_q, n_k, warm_iters, p, seed_q, seed_k, problem,
+                      init_q=cache[0], init_k=cache[1])
+            res.modes.append("warm")
+        cache = (r.km_q.centroids, r.km_k.centroids)
+        res.outs.append(r.out)
+        res.layers.append(r)
+    return res

@@ -299,3 +299,50 @@ def test_layer_tiny_config_end_to_end():
     assert rel_l2(got, ref.out) <= 1e-4
     assert np.max(np.abs(got - ref.out)) <= 1e-3
     assert int(layer.pairs[0]) == ref.pairs
+
+
+# ====================================================================== denoising run
+def test_denoise_driver_vs_oracle():
+    """The driver along a drifting tiny-config sequence (fp32): one dense step,
+    then a cold step and warm steps from the centroid cache, each step against
+    the oracle's reference run of the same layer."""
+    from sparse_attention_video_head_amd.driver import DenoiseDriver
+    cfg = synth.CONFIGS["tiny"]
+    steps, frac, top_p = 5, 0.2, 0.9
+    seq = list(synth.denoise_sequence(cfg, heads=[0], steps=steps))
+    drv = DenoiseDriver(1, cfg.n_tokens, cfg.head_dim, torch.float32, cfg.n_q, cfg.n_k, steps, top_p=top_p,
+                        dense_fraction=frac, cold_iters=cfg.iters, warm_iters=2, seed=3, device=DEV)
+    seed_q, seed_k = drv.seeds(0)
+    ref = oracle.denoise_layer([tuple(np64(x[c][0]) for c in "qkv") for x in seq], cfg.n_q, cfg.n_k,
+                               float(np.float32(top_p)), frac, cfg.iters, 2, seed_q, seed_k, problem=0)
+    assert ref.modes == ["dense", "cold", "warm", "warm", "warm"]
+    for s, x in enumerate(seq):
+        out = drv(0, s, *(x[c].to(DEV) for c in "qkv")).clone()
+        torch.cuda.synchronize()
+        assert drv.last_mode == ref.modes[s], f"step {s}"
+        got = np64(out[0])
+        assert rel_l2(got, ref.outs[s]) <= 1e-4, f"step {s}"
+        assert np.max(np.abs(got - ref.outs[s])) <= 1e-3, f"step {s}"
+        if ref.layers[s] is not None:
+            assert np.mean(drv.engine.labels_q[0].cpu().numpy() == ref.layers[s].km_q.labels) >= 0.999
+            assert np.mean(drv.engine.labels_k[0].cpu().numpy() == ref.layers[s].km_k.labels) >= 0.999
+
+
+def test_denoise_driver_layers_keep_separate_caches():
+    """Two layers interleaved step by step give the same outputs as two
+    drivers that each see one layer."""
+    from sparse_attention_video_head_amd.driver import DenoiseDriver
+    cfg = synth.CONFIGS["tiny"]
+    steps = 4
+    seqs = [list(synth.denoise_sequence(cfg, heads=[h], steps=steps)) for h in (0, 1)]
+    mk = lambda: DenoiseDriver(1, cfg.n_tokens, cfg.head_dim, torch.float32, cfg.n_q, cfg.n_k, steps,
+                               top_p=0.9, dense_fraction=0.25, cold_iters=3, warm_iters=2, seed=1, device=DEV)
+    both, single = mk(), [mk(), mk()]
+    for s in range(steps):
+        for layer in (0, 1):
+            x = [seqs[layer][s][c].to(DEV) for c in "qkv"]
+            a = both(layer, s, *x).clone()
+            b = single[layer](layer, s, *x).clone()
+            torch.cuda.synchronize()
+            assert torch.equal(a, b), f"layer {layer} step {s}"
+    assert sorted(both.cache) == [0, 1]
