@@ -94,6 +94,9 @@ def parse():
                     help="the denoising run through the driver (dense warm-up, cold, warm) against dense "
                          "attention on every step")
     ap.add_argument("--dense-fraction", type=float, default=0.1, help="--driver: leading dense share of the steps")
+    ap.add_argument("--recall", action="store_true",
+                    help="identification study: softmax mass recalled vs density, semantic clusters vs fixed "
+                         "128-token blocks")
     return ap.parse_args()
 
 
@@ -486,6 +489,61 @@ def driver_run(args):
     print(json.dumps(res), flush=True)
 
 
+RECALL_TOP_P = (0.05, 0.1, 0.2, 0.3, 0.5, 0.7, 0.8, 0.9, 0.95, 0.98, 0.99, 0.995, 0.998, 0.999, 0.9999)
+
+
+def recall_run(args):
+    """Identification accuracy at the layer's shape: for a sweep of top-p, the
+    density and the mean share of each query row's exact softmax mass that
+    the selection keeps, for the method's semantic clusters and for fixed
+    128-token blocks with mean-pooled representatives."""
+    import numpy as np
+    import torch
+    from sparse_attention_video_head_amd import binding as B
+    from sparse_attention_video_head_amd import synth
+    from sparse_attention_video_head_amd.study import IdentificationStudy
+
+    cfg = synth.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    data = synth.make_layer(cfg)
+    log(f"libsvg2 {B.version()}; recall study {cfg.name}: bh={cfg.bh} N={cfg.n_tokens}; inputs {time.time() - t0:.1f}s")
+    q, k, v = (data[c].to(dev) for c in "qkv")
+    st = IdentificationStudy(cfg.bh, cfg.n_tokens, cfg.head_dim, cfg.torch_dtype, cfg.n_q, cfg.n_k, block=128,
+                             device=dev)
+    seeds = dict(seed_q=(cfg.seed << 8) | 0, seed_k=(cfg.seed << 8) | 1)
+    N2 = cfg.bh * float(cfg.n_tokens) ** 2
+    t1 = time.time()
+    curves = {}
+    for name, rows in (("semantic", st.semantic(q, k, v, RECALL_TOP_P, iters=cfg.iters, **seeds)),
+                       ("positional_128", st.positional(q, k, v, RECALL_TOP_P))):
+        pts = [{"top_p": r["top_p"], "density": round(float(r["pairs"].sum().item()) / N2, 5),
+                "recall": round(float(r["recall"].mean().item()), 5)} for r in rows]
+        curves[name] = pts
+        for pt in pts:
+            log(f"{name:15s} p={pt['top_p']:<7} density {pt['density']:.4f} recall {pt['recall']:.4f}")
+    torch.cuda.synchronize()
+    elapsed = time.time() - t1
+
+    def at(name, dens):
+        pts = sorted((p["density"], p["recall"]) for p in curves[name])
+        xs, ys = [p[0] for p in pts], [p[1] for p in pts]
+        return round(float(np.interp(dens, xs, ys)), 5) if xs[0] <= dens <= xs[-1] else None
+
+    res = {
+        "metric": "share of the exact softmax mass recalled at 25% density, semantic clusters (fixed 128-token "
+                  "blocks beside it)",
+        "value": at("semantic", 0.25), "unit": "fraction", "n_gpus": 1, "higher_is_better": True,
+        "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": f"{cfg.name}-identification", "heads": cfg.bh, "n_tokens": cfg.n_tokens,
+                   "head_dim": cfg.head_dim, "n_q": cfg.n_q, "n_k": cfg.n_k, "kmeans_iters": cfg.iters,
+                   "block": 128},
+        "recall_at_density": {name: {f"{d:.2f}": at(name, d) for d in (0.05, 0.10, 0.25, 0.50)} for name in curves},
+        "curves": curves, "sweep_s": round(elapsed, 2),
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -500,6 +558,9 @@ def main():
         return
     if args.driver:
         driver_run(args)
+        return
+    if args.recall:
+        recall_run(args)
         return
 
     import numpy as np

@@ -18,6 +18,8 @@
  *                      [Method, stage (4); Key claims, §4.3 / Fig. 7(b)]
  *   svg2_unpermute     the inverse permutation of the output rows
  *                      [Method, stage (2)]
+ * and, beside the path, two analysis calls (cluster means of given labels,
+ * and the attention mass a selection recalls) for the identification study.
  *
  * Conventions shared by every call
  *   - Tensor arguments are DEVICE pointers allocated by the caller, 16-byte
@@ -209,6 +211,45 @@ int svg2_unpermute(const void* src, int32_t dtype, int32_t bh, int32_t n_tokens,
                    int32_t head_dim, const int32_t* perm, void* dst, int32_t heads,
                    int64_t dst_b_stride, int64_t dst_h_stride, int64_t dst_token_stride,
                    hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Analysis calls beside the path (the identification-accuracy study:
+ * [Key claims, §3.1 / Fig. 3; §3.2, Figs. 3-4; §5.3]).
+ *
+ * svg2_cluster_means - the Lloyd update on its own: per problem, the count
+ * and the mean row of every label [Method, stage (1)].  With labels
+ * t / block it gives the mean-pooled representatives of fixed position-based
+ * blocks, the block representation whose mismatch with in-block semantics
+ * the pages name as the first cause of misidentified critical tokens.
+ *
+ *   x               [bh, n_tokens, head_dim] dtype, contiguous.
+ *   labels          [bh, n_tokens] int32 in [0, n_clusters) (out of range:
+ *                   clamped; memory stays safe, the result is unspecified).
+ *   means           out [bh, n_clusters, head_dim] fp32: the fp64 mean of
+ *                   each label's rows, rounded to fp32.  A label with no row
+ *                   keeps its previous value.
+ *   counts          out [bh, n_clusters] int32.
+ * ---------------------------------------------------------------------- */
+size_t svg2_cluster_means_workspace_size(int32_t bh, int32_t n_tokens, int32_t head_dim,
+                                         int32_t n_clusters);
+int svg2_cluster_means(const void* x, int32_t dtype, int32_t bh, int32_t n_tokens, int32_t head_dim,
+                       const int32_t* labels, int32_t n_clusters, float* means, int32_t* counts,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * svg2_recall_mass - the share of each query row's exact softmax mass that
+ * a selection keeps, averaged over the rows of each problem:
+ *     mean_r exp(lse_sel[r] - lse_all[r])
+ * where lse_sel is the log-sum-exp over the selected keys and lse_all over
+ * every key (both from svg2_varblock_attn, rows in the same order).  Rows
+ * with lse_all = -inf (no key) are skipped; lse_sel = -inf counts as 0.
+ * The sum runs in fp64 in a fixed order.
+ *
+ *   lse_sel, lse_all  [bh, n_tokens] fp32.
+ *   mean_recall       out [bh] fp64 (NaN for a problem with no valid row).
+ * ---------------------------------------------------------------------- */
+int svg2_recall_mass(const float* lse_sel, const float* lse_all, int32_t bh, int32_t n_tokens,
+                     double* mean_recall, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -484,3 +484,54 @@ def denoise_layer(steps_qkv, n_q: int, n_k: int, top_p, fraction: float, cold_it
         res.outs.append(r.out)
         res.layers.append(r)
     return res
+
+
+# --------------------------------------------------------------------------
+# Identification accuracy, beside the path  [wiki: Key claims, §3.1 / Fig. 3;
+# §3.2, Figs. 3-4; §5.3]
+# reading: the recall of query row r under a selection is the share of r's
+# exact softmax mass that falls on the keys the selection gives r,
+#   sum_{u selected} exp(s_ru) / sum_u exp(s_ru),  s_ru = scale q_r . k_u.
+# Position-based blocks: fixed blocks of `block` consecutive tokens of the
+# original order (the last one may be shorter), each represented by the mean
+# of its rows and scored and selected exactly as the semantic clusters are
+# (the same size-weighted estimate and top-p).
+# --------------------------------------------------------------------------
+def position_blocks(n_tokens: int, block: int) -> np.ndarray:
+    """Label of every token: its fixed block, t // block."""
+    return np.arange(n_tokens) // block
+
+
+def recall_rows(q, k, zq, zk, lists, scale: float) -> np.ndarray:
+    """Per query row, the share of its softmax mass on its selected keys."""
+    s = scale * (np.asarray(q, dtype=np.float64) @ np.asarray(k, dtype=np.float64).T)
+    e = np.exp(s - np.max(s, axis=1, keepdims=True))
+    total = np.sum(e, axis=1)
+    rec = np.zeros(s.shape[0])
+    for i, sel in enumerate(lists):
+        rows = np.nonzero(zq == i)[0]
+        if len(rows) == 0:
+            continue
+        keys = np.isin(zk, sel)
+        rec[rows] = np.sum(e[np.ix_(rows, keys)], axis=1) / total[rows]
+    return rec
+
+
+@dataclass
+class BlockSelection:
+    zq: np.ndarray
+    zk: np.ndarray
+    selection: Selection
+    pairs: int
+
+
+def positional_selection(q, k, block: int, top_p: float) -> BlockSelection:
+    """Fixed position-based blocks with mean-pooled representatives, scored
+    and selected like the semantic clusters (fp32 means, as the GPU keeps)."""
+    N, d = np.asarray(q).shape
+    z = position_blocks(N, block)
+    n = int(z[-1]) + 1
+    cq, nq = update(q, z, np.zeros((n, d)))
+    ck, nk = update(k, z, np.zeros((n, d)))
+    sel = select_topp(centroid_probs(cq, ck, nk, 1.0 / math.sqrt(d)), nk, top_p)
+    return BlockSelection(zq=z, zk=z, selection=sel, pairs=pair_count(sel.lists, nq, nk))

@@ -29,6 +29,7 @@ EXPORTED = [
     "svg2_select_topp_workspace_size", "svg2_select_topp",
     "svg2_varblock_attn_workspace_size", "svg2_varblock_attn",
     "svg2_unpermute",
+    "svg2_cluster_means_workspace_size", "svg2_cluster_means", "svg2_recall_mass",
 ]
 
 
@@ -76,6 +77,13 @@ def lib() -> ctypes.CDLL:
     L.svg2_unpermute.restype = ctypes.c_int
     L.svg2_unpermute.argtypes = [_c_p, _c_int, _c_int, _c_int, _c_int, _c_p, _c_p, _c_int, _c_i64, _c_i64,
                                  _c_i64, _c_p]
+    L.svg2_cluster_means_workspace_size.restype = _c_sz
+    L.svg2_cluster_means_workspace_size.argtypes = [_c_int] * 4
+    L.svg2_cluster_means.restype = ctypes.c_int
+    L.svg2_cluster_means.argtypes = [_c_p, _c_int, _c_int, _c_int, _c_int, _c_p, _c_int, _c_p, _c_p, _c_p, _c_sz,
+                                     _c_p]
+    L.svg2_recall_mass.restype = ctypes.c_int
+    L.svg2_recall_mass.argtypes = [_c_p, _c_p, _c_int, _c_int, _c_p, _c_p]
     _lib = L
     return L
 
@@ -241,10 +249,11 @@ def select_topp(q_centroids: torch.Tensor, q_counts: torch.Tensor, k_centroids: 
 # ---------------------------------------------------------------- attention
 def varblock_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_offsets: torch.Tensor,
                   k_offsets: torch.Tensor, sel_count: torch.Tensor, sel_idx: torch.Tensor,
-                  scale: Optional[float] = None, lse: bool = False, out: Optional[torch.Tensor] = None,
+                  scale: Optional[float] = None, lse=False, out: Optional[torch.Tensor] = None,
                   workspace: Optional[torch.Tensor] = None):
     """Variable-block sparse attention on permuted contiguous [bh, N, d]
-    tensors.  Returns (out [bh,N,d], lse [bh,N] fp32 or None)."""
+    tensors.  Returns (out [bh,N,d], lse [bh,N] fp32 or None); ``lse`` is a
+    flag or a contiguous fp32 [bh, N] tensor to write it into."""
     _need_cuda(q, k, v, q_offsets, k_offsets, sel_count, sel_idx)
     for t in (q, k, v):
         if t.dim() != 3 or not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype:
@@ -262,7 +271,13 @@ def varblock_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_offsets: 
     dev = q.device
     if out is None:
         out = torch.empty_like(q)
-    ls = torch.empty(bh, N, dtype=torch.float32, device=dev) if lse else None
+    if isinstance(lse, torch.Tensor):
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (bh, N) or not lse.is_contiguous():
+            raise Svg2Error("lse must be a contiguous fp32 [bh, N] tensor")
+        _need_cuda(lse)
+        ls = lse
+    else:
+        ls = torch.empty(bh, N, dtype=torch.float32, device=dev) if lse else None
     L = lib()
     ws_n = L.svg2_varblock_attn_workspace_size(bh, N, n_q, n_k, d)
     ws = _workspace(ws_n, dev, workspace)
@@ -291,4 +306,49 @@ def unpermute(src: torch.Tensor, perm: torch.Tensor, out: Optional[torch.Tensor]
     s = lib().svg2_unpermute(_ptr(src), _dtype_code(src), bh, N, d, _ptr(perm), _ptr(out), heads, sb, sh, st,
                              _stream(src.device))
     _check(s, "svg2_unpermute")
+    return out
+
+
+# ------------------------------------------------------- identification study
+def cluster_means(x: torch.Tensor, labels: torch.Tensor, n_clusters: int, means: Optional[torch.Tensor] = None,
+                  counts: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Count and fp32 mean row of every label of each problem (the Lloyd update
+    alone).  Returns (means [bh, n, d] fp32, counts [bh, n] int32); a label with
+    no row keeps the value ``means`` held."""
+    _need_cuda(x, labels, means, counts)
+    if x.dim() != 3 or not x.is_contiguous():
+        raise Svg2Error("x must be a contiguous [bh, N, d] tensor")
+    bh, N, d = x.shape
+    if labels.dtype != torch.int32 or tuple(labels.shape) != (bh, N) or not labels.is_contiguous():
+        raise Svg2Error("labels must be contiguous int32 [bh, N]")
+    dev = x.device
+    if means is None:
+        means = torch.zeros(bh, n_clusters, d, dtype=torch.float32, device=dev)
+    if counts is None:
+        counts = torch.empty(bh, n_clusters, dtype=torch.int32, device=dev)
+    if (tuple(means.shape) != (bh, n_clusters, d) or means.dtype != torch.float32 or not means.is_contiguous()
+            or tuple(counts.shape) != (bh, n_clusters) or counts.dtype != torch.int32 or not counts.is_contiguous()):
+        raise Svg2Error("means [bh, n, d] fp32 and counts [bh, n] int32, contiguous, expected")
+    L = lib()
+    ws_n = L.svg2_cluster_means_workspace_size(bh, N, d, n_clusters)
+    ws = _workspace(ws_n, dev, workspace)
+    st = L.svg2_cluster_means(_ptr(x), _dtype_code(x), bh, N, d, _ptr(labels), n_clusters, _ptr(means),
+                              _ptr(counts), _ptr(ws), ws_n, _stream(dev))
+    _check(st, "svg2_cluster_means")
+    return means, counts
+
+
+def recall_mass(lse_sel: torch.Tensor, lse_all: torch.Tensor, out: Optional[torch.Tensor] = None):
+    """Per problem, the mean over rows of exp(lse_sel - lse_all): the share of
+    each row's softmax mass that a selection keeps.  Returns [bh] fp64."""
+    _need_cuda(lse_sel, lse_all, out)
+    for t in (lse_sel, lse_all):
+        if t.dtype != torch.float32 or t.dim() != 2 or not t.is_contiguous() or t.shape != lse_sel.shape:
+            raise Svg2Error("lse_sel and lse_all must be contiguous fp32 [bh, N] tensors of one shape")
+    bh, N = lse_sel.shape
+    if out is None:
+        out = torch.empty(bh, dtype=torch.float64, device=lse_sel.device)
+    L = lib()
+    st = L.svg2_recall_mass(_ptr(lse_sel), _ptr(lse_all), bh, N, _ptr(out), _stream(lse_sel.device))
+    _check(st, "svg2_recall_mass")
     return out

@@ -291,4 +291,47 @@ int svg2_unpermute(const void* src, int32_t dtype, int32_t bh, int32_t n_tokens,
                                         dst_h_stride, dst_token_stride, perm, stream));
 }
 
+// ------------------------------------------------------- identification study
+size_t svg2_cluster_means_workspace_size(int32_t bh, int32_t n_tokens, int32_t head_dim, int32_t n_clusters) {
+  if (!shape_ok(bh, n_tokens, n_clusters) || !dim_ok(head_dim)) return 0;
+  Carve c(nullptr);
+  c.take<int32_t>((size_t)bh * sort_chunks(n_tokens) * n_clusters);
+  c.take<int32_t>((size_t)bh * n_tokens);
+  c.take<int32_t>((size_t)bh * (n_clusters + 1));
+  c.take<double>((size_t)bh * (n_clusters + mean_chunks(n_tokens)) * head_dim);
+  return c.off;
+}
+
+int svg2_cluster_means(const void* x, int32_t dtype, int32_t bh, int32_t n_tokens, int32_t head_dim,
+                       const int32_t* labels, int32_t n_clusters, float* means, int32_t* counts,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!dtype_ok(dtype)) return SVG2_ERR_INVALID_ARG;
+  if (!shape_ok(bh, n_tokens, n_clusters)) return SVG2_ERR_INVALID_ARG;
+  if (!dim_ok(head_dim)) return SVG2_ERR_UNSUPPORTED;
+  if (!x || !labels || !means || !counts || !aligned(x, 16) || !aligned(labels, 4) || !aligned(means, 4) ||
+      !aligned(counts, 4))
+    return SVG2_ERR_INVALID_ARG;
+  const size_t need = svg2_cluster_means_workspace_size(bh, n_tokens, head_dim, n_clusters);
+  if (workspace_bytes < need || !workspace) return SVG2_ERR_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return SVG2_ERR_INVALID_ARG;
+  Carve c(workspace);
+  int32_t* hist = c.take<int32_t>((size_t)bh * sort_chunks(n_tokens) * n_clusters);
+  int32_t* perm = c.take<int32_t>((size_t)bh * n_tokens);
+  int32_t* offsets = c.take<int32_t>((size_t)bh * (n_clusters + 1));
+  double* partial = c.take<double>((size_t)bh * (n_clusters + mean_chunks(n_tokens)) * head_dim);
+  int st = hip_status(launch_counting_sort(labels, bh, n_tokens, n_clusters, hist, perm, offsets, counts, stream));
+  if (st) return st;
+  return hip_status(launch_centroid_mean(x, dtype == SVG2_BF16, bh, n_tokens, head_dim, n_clusters, perm, offsets,
+                                         partial, means, stream));
+}
+
+int svg2_recall_mass(const float* lse_sel, const float* lse_all, int32_t bh, int32_t n_tokens,
+                     double* mean_recall, hipStream_t stream) {
+  if (bh < 1 || n_tokens < 1 || n_tokens > kMaxTokens) return SVG2_ERR_INVALID_ARG;
+  if (!lse_sel || !lse_all || !mean_recall || !aligned(lse_sel, 4) || !aligned(lse_all, 4) ||
+      !aligned(mean_recall, 8))
+    return SVG2_ERR_INVALID_ARG;
+  return hip_status(launch_recall_mass(lse_sel, lse_all, bh, n_tokens, mean_recall, stream));
+}
+
 }  // extern "C"

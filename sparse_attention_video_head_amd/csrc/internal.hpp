@@ -65,4 +65,9 @@ hipError_t launch_varblock_attn(const void* q, const void* k, const void* v, boo
                                 float scale, void* out, float* lse, int32_t* tiles_ws,
                                 int32_t* item_count_ws, int32_t* items_ws, hipStream_t s);
 
+// --------------------------------------------------------------- recall.hip
+// mean_recall[p] = mean over rows with lse_all > -inf of exp(lse_sel - lse_all).
+hipError_t launch_recall_mass(const float* lse_sel, const float* lse_all, int bh, int N, double* mean_recall,
+                              hipStream_t s);
+
 }  // namespace svg2

@@ -144,3 +144,38 @@ def test_binding_refuses_cpu_tensors():
         B.kmeans(torch.zeros(1, 8, 64), 2, 1)
     with pytest.raises(B.Svg2Error):
         B.unpermute(torch.zeros(1, 8, 64), torch.zeros(1, 8, dtype=torch.int32))
+
+
+def _means(**kw):
+    a = dict(x=FAKE, dtype=1, bh=2, N=500, d=128, lab=FAKE, n=8, means=FAKE, cnt=FAKE, ws=FAKE, wsn=1 << 30)
+    a.update(kw)
+    return B.lib().svg2_cluster_means(a["x"], a["dtype"], a["bh"], a["N"], a["d"], a["lab"], a["n"], a["means"],
+                                      a["cnt"], a["ws"], a["wsn"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=5), INVALID), (dict(bh=0), INVALID), (dict(n=0), INVALID), (dict(n=501), INVALID),
+    (dict(d=96), UNSUPPORTED), (dict(x=None), INVALID), (dict(x=MISALIGNED), INVALID), (dict(lab=None), INVALID),
+    (dict(means=None), INVALID), (dict(cnt=None), INVALID), (dict(cnt=FAKE + 2), INVALID), (dict(wsn=16), WORKSPACE),
+    (dict(ws=None), WORKSPACE),
+])
+def test_cluster_means_validation(kw, code):
+    assert _means(**kw) == code
+
+
+def test_cluster_means_size_query():
+    L = B.lib()
+    assert L.svg2_cluster_means_workspace_size(1, 10, 96, 4) == 0
+    assert L.svg2_cluster_means_workspace_size(1, 10, 128, 11) == 0
+    # the per-chunk partial sums dominate: bh (n + ceil(N / 512)) d doubles
+    assert L.svg2_cluster_means_workspace_size(24, 118800, 128, 929) >= 24 * (929 + 233) * 128 * 8
+
+
+def test_recall_mass_validation():
+    L = B.lib()
+    assert L.svg2_recall_mass(FAKE, FAKE, 0, 10, FAKE, None) == INVALID
+    assert L.svg2_recall_mass(FAKE, FAKE, 1, 0, FAKE, None) == INVALID
+    assert L.svg2_recall_mass(FAKE, FAKE, 1, 1 << 25, FAKE, None) == INVALID
+    assert L.svg2_recall_mass(None, FAKE, 1, 10, FAKE, None) == INVALID
+    assert L.svg2_recall_mass(FAKE, FAKE + 2, 1, 10, FAKE, None) == INVALID
+    assert L.svg2_recall_mass(FAKE, FAKE, 1, 10, FAKE + 4, None) == INVALID

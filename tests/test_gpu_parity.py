@@ -346,3 +346,64 @@ def test_denoise_driver_layers_keep_separate_caches():
             torch.cuda.synchronize()
             assert torch.equal(a, b), f"layer {layer} step {s}"
     assert sorted(both.cache) == [0, 1]
+
+
+# ====================================================================== identification study
+@pytest.mark.parametrize("dt,d", [("bf16", 128), ("f32", 64)])
+def test_cluster_means_vs_oracle(dt, d):
+    bh, N, n = 2, 3000, 37
+    x, _, _ = mixture(bh, N, d, comps=10, seed=21, dtype=dtype_of(dt))
+    rng = np.random.default_rng(4)
+    lab = rng.integers(0, n, (bh, N)).astype(np.int32)
+    lab[lab == 5] = 6                                   # label 5 has no row
+    prev = torch.full((bh, n, d), 7.0, dtype=torch.float32, device=DEV)
+    means, counts = B.cluster_means(x.to(DEV), torch.from_numpy(lab).to(DEV), n, means=prev)
+    torch.cuda.synchronize()
+    for h in range(bh):
+        C, cnt = oracle.update(np64(x[h]), lab[h].astype(np.int64), np.full((n, d), 7.0))
+        np.testing.assert_array_equal(counts[h].cpu().numpy(), cnt)
+        got = means[h].cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(got - C) <= 1e-6 * np.maximum(1.0, np.abs(C)))
+        assert np.all(got[5] == 7.0)
+
+
+def test_recall_mass_vs_definition():
+    rng = np.random.default_rng(8)
+    bh, N = 3, 5000
+    a = rng.standard_normal((bh, N))
+    b = a + np.abs(rng.standard_normal((bh, N)))        # lse over all keys >= over the selected ones
+    a[0, :10] = -np.inf                                  # rows that keep nothing
+    b[1, :7] = -np.inf                                   # rows with no key: skipped
+    a[1, :7] = -np.inf
+    a32, b32 = a.astype(np.float32), b.astype(np.float32)
+    got = B.recall_mass(torch.from_numpy(a32).to(DEV), torch.from_numpy(b32).to(DEV)).cpu().numpy()
+    for h in range(bh):
+        ok = np.isfinite(b32[h])
+        expect = np.mean(np.exp(a32[h][ok].astype(np.float64) - b32[h][ok].astype(np.float64)))
+        assert abs(got[h] - expect) <= 1e-12 * max(1.0, expect)
+
+
+def test_identification_study_vs_oracle():
+    """Tiny fp32 config: mean recall of the semantic path and of fixed
+    128-token blocks at p = 0.9 against the oracle's definitions."""
+    from sparse_attention_video_head_amd.study import IdentificationStudy
+    cfg = synth.CONFIGS["tiny"]
+    data = synth.make_layer(cfg)
+    q, k, v = (data[c].to(DEV) for c in "qkv")
+    st = IdentificationStudy(cfg.bh, cfg.n_tokens, cfg.head_dim, torch.float32, cfg.n_q, cfg.n_k, block=128)
+    p = 0.9
+    sem = st.semantic(q, k, v, [p], iters=cfg.iters, seed_q=100, seed_k=200)[0]
+    pos = st.positional(q, k, v, [p])[0]
+    torch.cuda.synchronize()
+    qn, kn, vn = (np64(data[c][0]) for c in "qkv")
+    s = 1 / math.sqrt(cfg.head_dim)
+    pf = float(np.float32(p))
+    ref = oracle.layer(qn, kn, vn, cfg.n_q, cfg.n_k, cfg.iters, pf, seed_q=100, seed_k=200)
+    assert np.mean(st.layer.labels_q[0].cpu().numpy() == ref.km_q.labels) >= 0.999
+    rec = np.mean(oracle.recall_rows(qn, kn, ref.km_q.labels, ref.km_k.labels, ref.selection.lists, s))
+    assert abs(float(sem["recall"][0]) - rec) <= 1e-3
+    assert int(sem["pairs"][0]) == ref.pairs
+    b = oracle.positional_selection(qn, kn, 128, pf)
+    rec_b = np.mean(oracle.recall_rows(qn, kn, b.zq, b.zk, b.selection.lists, s))
+    assert abs(float(pos["recall"][0]) - rec_b) <= 1e-5
+    assert int(pos["pairs"][0]) == b.pairs
