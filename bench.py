@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 METRIC = "sparse-attn effective TFLOP/s + layer latency at 118k tokens; k-means iters/s"
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz)
 PEAK_F32_TFLOPS = 157.3
+PEAK_FP8_TFLOPS = 5033.2       # MI355X dense fp8 MFMA
 
 
 PEAK_CLOCK_MHZ = 2400.0         # the clock the published peaks assume
@@ -94,6 +95,8 @@ def parse():
                     help="the denoising run through the driver (dense warm-up, cold, warm) against dense "
                          "attention on every step")
     ap.add_argument("--dense-fraction", type=float, default=0.1, help="--driver: leading dense share of the steps")
+    ap.add_argument("--fp8", action="store_true",
+                    help="the layer step with FP8 (E4M3) attention; the bf16 step is the default")
     ap.add_argument("--recall", action="store_true",
                     help="identification study: softmax mass recalled vs density, semantic clusters vs fixed "
                          "128-token blocks")
@@ -578,7 +581,8 @@ def main():
     log(f"generated inputs in {time.time() - t0:.1f}s")
     q, k, v = (data[x].to(dev) for x in "qkv")
     host = data
-    layer = SVG2Layer(cfg.bh, cfg.n_tokens, cfg.head_dim, cfg.torch_dtype, cfg.n_q, cfg.n_k, device=dev)
+    layer = SVG2Layer(cfg.bh, cfg.n_tokens, cfg.head_dim, cfg.torch_dtype, cfg.n_q, cfg.n_k, device=dev,
+                      fp8_attention=args.fp8)
     seeds = dict(seed_q=(cfg.seed << 8) | 0, seed_k=(cfg.seed << 8) | 1)
 
     # ---- top-p: config value, or bisected on the cold-start clustering
@@ -689,7 +693,7 @@ def main():
     attn_flops = 4.0 * cfg.head_dim * cold_pairs
     attn_ms = float(cold_stage[3])
     attn_tflops = attn_flops / (attn_ms * 1e-3) / 1e12
-    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    peak = PEAK_FP8_TFLOPS if args.fp8 else (PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS)
     value = attn_flops / (cold_ms * 1e-3) / 1e12
     dense_flops = 4.0 * cfg.head_dim * cfg.bh * float(cfg.n_tokens) ** 2
 
@@ -712,9 +716,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": cfg.dtype,
+        "dtype": "fp8" if args.fp8 else cfg.dtype,
         "data": "synthetic",
-        "config": {"workload": f"{cfg.name}-layer", "heads": cfg.bh, "n_tokens": cfg.n_tokens,
+        "config": {"workload": f"{cfg.name}-layer" + ("-fp8-attention" if args.fp8 else ""), "heads": cfg.bh, "n_tokens": cfg.n_tokens,
                    "head_dim": cfg.head_dim, "n_q": cfg.n_q, "n_k": cfg.n_k, "kmeans_iters": cfg.iters,
                    "start": "cold (k-means++)", "top_p": round(top_p, 6), "density": round(density, 5)},
         "layer_ms_cold": round(cold_ms, 3),
@@ -742,9 +746,10 @@ def main():
         "padding_ratio_this_kernel": round(pad_own, 4),
         "permute_gbps": round(permute_bytes / (cold_stage[1] * 1e-3) / 1e9, 1),
         "unpermute_gbps": round(unpermute_bytes / (cold_stage[4] * 1e-3) / 1e9, 1),
-        "roofline": {"bound": "mfma", "kernel": "k_attn_bf16" if cfg.dtype == "bf16" else "k_attn_f32",
+        "roofline": {"bound": "mfma",
+                     "kernel": "k_attn_fp8" if args.fp8 else ("k_attn_bf16" if cfg.dtype == "bf16" else "k_attn_f32"),
                      "achieved": round(attn_tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(attn_tflops / peak, 4), "traffic": traffic,
+                     "frac": round(attn_tflops / peak, 4), "traffic": None if args.fp8 else traffic,
                      "flops_per_launch": attn_flops},
         # shader clock over the timed steps, and the peak scaled to its median
         "gpu_clock_mhz": gpu_clock,

@@ -18,6 +18,7 @@
  *                      [Method, stage (4); Key claims, §4.3 / Fig. 7(b)]
  *   svg2_unpermute     the inverse permutation of the output rows
  *                      [Method, stage (2)]
+ * an FP8 variant of the attention (svg2_quantize_fp8, svg2_varblock_attn_fp8),
  * and, beside the path, two analysis calls (cluster means of given labels,
  * and the attention mass a selection recalls) for the identification study.
  *
@@ -211,6 +212,41 @@ int svg2_unpermute(const void* src, int32_t dtype, int32_t bh, int32_t n_tokens,
                    int32_t head_dim, const int32_t* perm, void* dst, int32_t heads,
                    int64_t dst_b_stride, int64_t dst_h_stride, int64_t dst_token_stride,
                    hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * FP8 attention (the project README's open-source plan, "Support FP8
+ * attention"): E4M3 copies of the permuted Q', K', V' with one scale per
+ * problem and tensor, then the variable-block attention on them.
+ *
+ * svg2_quantize_fp8 - x8 = E4M3(x * r_p) with r_p = 448 / max|x_p| and the
+ * dequantization scale[p] = max|x_p| / 448 (both correctly rounded fp32; 1
+ * for an all-zero problem).  The product is taken in fp32 and clamped to
+ * +-448, the conversion rounds to nearest even (OCP E4M3: bias 7, largest
+ * finite 448, subnormals kept).
+ *
+ *   x               [bh, n_tokens, head_dim] bf16, contiguous.
+ *   x8              out [bh, n_tokens, head_dim] E4M3 bytes.
+ *   scale           out [bh] fp32.
+ *   workspace       svg2_quantize_fp8_workspace_size(bh) bytes.
+ * ---------------------------------------------------------------------- */
+size_t svg2_quantize_fp8_workspace_size(int32_t bh);
+int svg2_quantize_fp8(const void* x, int32_t bh, int32_t n_tokens, int32_t head_dim, void* x8, float* scale,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* svg2_varblock_attn_fp8 - svg2_varblock_attn on E4M3 inputs, head_dim 128
+ * only [Method, stage (4)]: S = (q8 . k8) * q_scale * k_scale on the fp8
+ * matrix cores (fp32 accumulation), softmax in fp32, probabilities rounded
+ * to E4M3 before the P.V product (they are at most 2^8), O = (P v8) *
+ * v_scale / row sum (the row sum adds the fp32 probabilities), stored bf16.
+ * Arguments as for svg2_varblock_attn, plus the three [bh] fp32 scales; the
+ * workspace is svg2_varblock_attn_workspace_size's.  Head_dim other than 128
+ * returns SVG2_ERR_UNSUPPORTED. */
+int svg2_varblock_attn_fp8(const void* q8, const void* k8, const void* v8, const float* q_scale,
+                           const float* k_scale, const float* v_scale, int32_t bh, int32_t n_tokens,
+                           int32_t head_dim, const int32_t* q_offsets, int32_t n_q,
+                           const int32_t* k_offsets, int32_t n_k, const int32_t* sel_count,
+                           const int32_t* sel_idx, float scale, void* out, float* lse, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Analysis calls beside the path (the identification-accuracy study:

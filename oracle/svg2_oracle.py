@@ -535,3 +535,56 @@ def positional_selection(q, k, block: int, top_p: float) -> BlockSelection:
     ck, nk = update(k, z, np.zeros((n, d)))
     sel = select_topp(centroid_probs(cq, ck, nk, 1.0 / math.sqrt(d)), nk, top_p)
     return BlockSelection(zq=z, zk=z, selection=sel, pairs=pair_count(sel.lists, nq, nk))
+
+
+# --------------------------------------------------------------------------
+# FP8 attention (the open-source plan's "Support FP8 attention" [README]).
+# reading: the pages name FP8 but no format or scaling.  OCP FP8 E4M3 (1 sign,
+# 4 exponent bits with bias 7, 3 mantissa bits, subnormals, largest finite
+# value 448, no infinities) with one scale per problem and tensor:
+# scale = max|x| / 448 for the dequantization, r = 448 / max|x| (both
+# correctly rounded to fp32) and x8 = round-to-nearest-even(x * r) on the E4M3
+# grid, the product taken in fp32 and clamped to +-448.
+# --------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def e4m3_grid() -> np.ndarray:
+    """Every non-negative finite E4M3 value, ascending (code order)."""
+    vals = []
+    for e in range(16):
+        for m in range(8):
+            if e == 15 and m == 7:          # the NaN code
+                continue
+            vals.append(m / 8.0 * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    return np.array(vals)
+
+
+def e4m3_round(x: np.ndarray) -> np.ndarray:
+    """x (|x| <= 448) to the nearest E4M3 value; ties go to the even code."""
+    g = e4m3_grid()
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    i = np.clip(np.searchsorted(g, a), 1, len(g) - 1)
+    lo, hi = g[i - 1], g[i]
+    pick_hi = (a - lo > hi - a) | ((a - lo == hi - a) & (i % 2 == 0))
+    r = np.where(pick_hi, hi, lo)
+    r = np.where(a <= 0.0, 0.0, r)
+    return np.copysign(r, x)
+
+
+def fp8_scale(x) -> float:
+    """Per-tensor scale of one problem: max|x| / 448 in fp32 (1 if x is all zero)."""
+    amax = float(np.max(np.abs(np.asarray(x, dtype=np.float64))))
+    return float(np.float32(amax / E4M3_MAX)) if amax > 0 else 1.0
+
+
+def fp8_ratio(x) -> float:
+    """Quantization factor of one problem: 448 / max|x| in fp32 (1 if all zero)."""
+    amax = float(np.max(np.abs(np.asarray(x, dtype=np.float64))))
+    return float(np.float32(E4M3_MAX / amax)) if amax > 0 else 1.0
+
+
+def fp8_quantize(x) -> np.ndarray:
+    """The E4M3 values of x * fp8_ratio(x) (the product taken in fp32)."""
+    q = (np.asarray(x, dtype=np.float32) * np.float32(fp8_ratio(x))).astype(np.float64)
+    return e4m3_round(np.clip(q, -E4M3_MAX, E4M3_MAX))

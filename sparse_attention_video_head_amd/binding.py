@@ -30,6 +30,7 @@ EXPORTED = [
     "svg2_varblock_attn_workspace_size", "svg2_varblock_attn",
     "svg2_unpermute",
     "svg2_cluster_means_workspace_size", "svg2_cluster_means", "svg2_recall_mass",
+    "svg2_quantize_fp8_workspace_size", "svg2_quantize_fp8", "svg2_varblock_attn_fp8",
 ]
 
 
@@ -84,6 +85,13 @@ def lib() -> ctypes.CDLL:
                                      _c_p]
     L.svg2_recall_mass.restype = ctypes.c_int
     L.svg2_recall_mass.argtypes = [_c_p, _c_p, _c_int, _c_int, _c_p, _c_p]
+    L.svg2_quantize_fp8_workspace_size.restype = _c_sz
+    L.svg2_quantize_fp8_workspace_size.argtypes = [_c_int]
+    L.svg2_quantize_fp8.restype = ctypes.c_int
+    L.svg2_quantize_fp8.argtypes = [_c_p, _c_int, _c_int, _c_int, _c_p, _c_p, _c_p, _c_sz, _c_p]
+    L.svg2_varblock_attn_fp8.restype = ctypes.c_int
+    L.svg2_varblock_attn_fp8.argtypes = [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_p, _c_int,
+                                         _c_p, _c_int, _c_p, _c_p, ctypes.c_float, _c_p, _c_p, _c_p, _c_sz, _c_p]
     _lib = L
     return L
 
@@ -352,3 +360,63 @@ def recall_mass(lse_sel: torch.Tensor, lse_all: torch.Tensor, out: Optional[torc
     st = L.svg2_recall_mass(_ptr(lse_sel), _ptr(lse_all), bh, N, _ptr(out), _stream(lse_sel.device))
     _check(st, "svg2_recall_mass")
     return out
+
+
+# ------------------------------------------------------------------ fp8 attention
+def quantize_fp8(x: torch.Tensor, x8: Optional[torch.Tensor] = None, scale: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None):
+    """E4M3 copy of a contiguous bf16 [bh, N, d] tensor with one fp32 scale per
+    problem (max|x| / 448).  Returns (x8 uint8 [bh, N, d], scale [bh] fp32)."""
+    _need_cuda(x, x8, scale)
+    if x.dim() != 3 or not x.is_contiguous() or x.dtype != torch.bfloat16:
+        raise Svg2Error("x must be a contiguous bf16 [bh, N, d] tensor")
+    bh, N, d = x.shape
+    dev = x.device
+    if x8 is None:
+        x8 = torch.empty(bh, N, d, dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = torch.empty(bh, dtype=torch.float32, device=dev)
+    if (tuple(x8.shape) != (bh, N, d) or x8.dtype != torch.uint8 or not x8.is_contiguous()
+            or tuple(scale.shape) != (bh,) or scale.dtype != torch.float32):
+        raise Svg2Error("x8 uint8 [bh, N, d] and scale fp32 [bh], contiguous, expected")
+    L = lib()
+    ws_n = L.svg2_quantize_fp8_workspace_size(bh)
+    ws = _workspace(ws_n, dev, workspace)
+    st = L.svg2_quantize_fp8(_ptr(x), bh, N, d, _ptr(x8), _ptr(scale), _ptr(ws), ws_n, _stream(dev))
+    _check(st, "svg2_quantize_fp8")
+    return x8, scale
+
+
+def varblock_attn_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, q_scale: torch.Tensor,
+                      k_scale: torch.Tensor, v_scale: torch.Tensor, q_offsets: torch.Tensor, k_offsets: torch.Tensor,
+                      sel_count: torch.Tensor, sel_idx: torch.Tensor, scale: Optional[float] = None, lse=False,
+                      out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """svg2_varblock_attn on E4M3 inputs (uint8 [bh, N, 128] with [bh] fp32
+    scales).  Returns (out bf16 [bh, N, 128], lse or None)."""
+    _need_cuda(q8, k8, v8, q_scale, k_scale, v_scale, q_offsets, k_offsets, sel_count, sel_idx)
+    for t in (q8, k8, v8):
+        if t.dim() != 3 or not t.is_contiguous() or t.shape != q8.shape or t.dtype != torch.uint8:
+            raise Svg2Error("q8, k8, v8 must be contiguous uint8 [bh, N, d] tensors of one shape")
+    bh, N, d = q8.shape
+    for t in (q_scale, k_scale, v_scale):
+        if t.dtype != torch.float32 or tuple(t.shape) != (bh,) or not t.is_contiguous():
+            raise Svg2Error("scales must be contiguous fp32 [bh]")
+    n_q = q_offsets.shape[1] - 1
+    n_k = k_offsets.shape[1] - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dev = q8.device
+    if out is None:
+        out = torch.empty(bh, N, d, dtype=torch.bfloat16, device=dev)
+    if isinstance(lse, torch.Tensor):
+        ls = lse
+    else:
+        ls = torch.empty(bh, N, dtype=torch.float32, device=dev) if lse else None
+    L = lib()
+    ws_n = L.svg2_varblock_attn_workspace_size(bh, N, n_q, n_k, d)
+    ws = _workspace(ws_n, dev, workspace)
+    st = L.svg2_varblock_attn_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), bh, N,
+                                  d, _ptr(q_offsets), n_q, _ptr(k_offsets), n_k, _ptr(sel_count), _ptr(sel_idx),
+                                  ctypes.c_float(scale), _ptr(out), _ptr(ls), _ptr(ws), ws_n, _stream(dev))
+    _check(st, "svg2_varblock_attn_fp8")
+    return out, ls

@@ -291,6 +291,55 @@ int svg2_unpermute(const void* src, int32_t dtype, int32_t bh, int32_t n_tokens,
                                         dst_h_stride, dst_token_stride, perm, stream));
 }
 
+// ------------------------------------------------------------------ fp8 attention
+size_t svg2_quantize_fp8_workspace_size(int32_t bh) {
+  if (bh < 1) return 0;
+  Carve c(nullptr);
+  c.take<uint32_t>((size_t)bh);
+  return c.off;
+}
+
+int svg2_quantize_fp8(const void* x, int32_t bh, int32_t n_tokens, int32_t head_dim, void* x8, float* scale,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (bh < 1 || n_tokens < 1 || n_tokens > kMaxTokens) return SVG2_ERR_INVALID_ARG;
+  if (!dim_ok(head_dim)) return SVG2_ERR_UNSUPPORTED;
+  if (!x || !x8 || !scale || !aligned(x, 16) || !aligned(x8, 16) || !aligned(scale, 4)) return SVG2_ERR_INVALID_ARG;
+  const size_t need = svg2_quantize_fp8_workspace_size(bh);
+  if (workspace_bytes < need || !workspace) return SVG2_ERR_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return SVG2_ERR_INVALID_ARG;
+  return hip_status(launch_quantize_fp8(x, bh, n_tokens, head_dim, static_cast<uint8_t*>(x8), scale,
+                                        static_cast<uint32_t*>(workspace), stream));
+}
+
+int svg2_varblock_attn_fp8(const void* q8, const void* k8, const void* v8, const float* q_scale,
+                           const float* k_scale, const float* v_scale, int32_t bh, int32_t n_tokens,
+                           int32_t head_dim, const int32_t* q_offsets, int32_t n_q,
+                           const int32_t* k_offsets, int32_t n_k, const int32_t* sel_count,
+                           const int32_t* sel_idx, float scale, void* out, float* lse, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  if (bh < 1 || n_tokens < 1 || n_tokens > kMaxTokens) return SVG2_ERR_INVALID_ARG;
+  if (n_q < 1 || n_q > kMaxClusters || n_k < 1 || n_k > kMaxClusters) return SVG2_ERR_INVALID_ARG;
+  if (head_dim != 128) return SVG2_ERR_UNSUPPORTED;
+  if (!(isfinite(scale) && scale > 0.f)) return SVG2_ERR_INVALID_ARG;
+  if (!q8 || !k8 || !v8 || !out || !aligned(q8, 16) || !aligned(k8, 16) || !aligned(v8, 16) || !aligned(out, 16))
+    return SVG2_ERR_INVALID_ARG;
+  if (!q_scale || !k_scale || !v_scale || !aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(v_scale, 4))
+    return SVG2_ERR_INVALID_ARG;
+  if (!q_offsets || !k_offsets || !sel_count || !sel_idx || !aligned(q_offsets, 4) ||
+      !aligned(k_offsets, 4) || !aligned(sel_count, 4) || !aligned(sel_idx, 4) || (lse && !aligned(lse, 4)))
+    return SVG2_ERR_INVALID_ARG;
+  const size_t need = svg2_varblock_attn_workspace_size(bh, n_tokens, n_q, n_k, head_dim);
+  if (workspace_bytes < need || !workspace) return SVG2_ERR_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return SVG2_ERR_INVALID_ARG;
+  Carve c(workspace);
+  int32_t* tiles = c.take<int32_t>((size_t)bh * n_q);
+  int32_t* item_count = c.take<int32_t>((size_t)bh);
+  int32_t* items = c.take<int32_t>((size_t)bh * attn_max_items(n_tokens, n_q, attn_block_rows(true)));
+  return hip_status(launch_varblock_attn_fp8(q8, k8, v8, q_scale, k_scale, v_scale, bh, n_tokens, q_offsets, n_q,
+                                             k_offsets, n_k, sel_count, sel_idx, scale, out, lse, tiles, item_count,
+                                             items, stream));
+}
+
 // ------------------------------------------------------- identification study
 size_t svg2_cluster_means_workspace_size(int32_t bh, int32_t n_tokens, int32_t head_dim, int32_t n_clusters) {
   if (!shape_ok(bh, n_tokens, n_clusters) || !dim_ok(head_dim)) return 0;

@@ -65,6 +65,21 @@ hipError_t launch_varblock_attn(const void* q, const void* k, const void* v, boo
                                 float scale, void* out, float* lse, int32_t* tiles_ws,
                                 int32_t* item_count_ws, int32_t* items_ws, hipStream_t s);
 
+// FP8 (E4M3) Q, K, V with per-problem scales, head_dim 128, bf16 output; the
+// same workspace as launch_varblock_attn (row block kAttnBM).
+hipError_t launch_varblock_attn_fp8(const void* q, const void* k, const void* v, const float* q_scale,
+                                    const float* k_scale, const float* v_scale, int bh, int N,
+                                    const int32_t* q_off, int n_q, const int32_t* k_off, int n_k,
+                                    const int32_t* sel_count, const int32_t* sel_idx, float scale, void* out,
+                                    float* lse, int32_t* tiles_ws, int32_t* item_count_ws, int32_t* items_ws,
+                                    hipStream_t s);
+
+// ---------------------------------------------------------------- quant.hip
+// x8 = E4M3(x / scale), scale[p] = max|x_p| / 448 (1 if all zero); x bf16
+// [bh, N, d]; amax_ws: bh words.
+hipError_t launch_quantize_fp8(const void* x, int bh, int N, int d, uint8_t* x8, float* scale, uint32_t* amax_ws,
+                               hipStream_t s);
+
 // --------------------------------------------------------------- recall.hip
 // mean_recall[p] = mean over rows with lse_all > -inf of exp(lse_sel - lse_all).
 hipError_t launch_recall_mass(const float* lse_sel, const float* lse_all, int bh, int N, double* mean_recall,

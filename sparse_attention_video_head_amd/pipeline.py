@@ -21,7 +21,7 @@ from . import binding as B
 
 class SVG2Layer:
     def __init__(self, bh: int, n_tokens: int, head_dim: int, dtype: torch.dtype, n_q: int, n_k: int,
-                 device="cuda", two_streams: bool = True):
+                 device="cuda", two_streams: bool = True, fp8_attention: bool = False):
         self.bh, self.N, self.d, self.dtype = bh, n_tokens, head_dim, dtype
         self.n_q, self.n_k = n_q, n_k
         self.scale = 1.0 / math.sqrt(head_dim)
@@ -55,6 +55,14 @@ class SVG2Layer:
         self.dense_sel = torch.zeros(bh, 1, 1, dtype=torch.int32, device=dev)
         self.ws_dense = u8(L.svg2_varblock_attn_workspace_size(bh, n_tokens, 1, 1, head_dim))
         self.side = torch.cuda.Stream(device=dev) if two_streams else None
+        # FP8 attention: E4M3 copies of Q', K', V' with per-problem scales
+        self.fp8 = fp8_attention
+        if fp8_attention:
+            if dtype != torch.bfloat16 or head_dim != 128:
+                raise ValueError("FP8 attention takes bf16 inputs with head_dim 128")
+            self.q8, self.k8, self.v8 = (e(bh, n_tokens, head_dim, dt=torch.uint8) for _ in range(3))
+            self.s8 = e(3, bh, dt=torch.float32)
+            self.ws_q8 = u8(L.svg2_quantize_fp8_workspace_size(bh))
 
     # ------------------------------------------------------------ steps
     def kmeans(self, q, k, iters: int, warm: bool, seed_q: int, seed_k: int):
@@ -104,6 +112,14 @@ class SVG2Layer:
                       workspace=self.ws_sel)
 
     def attend(self):
+        if self.fp8:
+            for x, x8, sc in ((self.qp, self.q8, self.s8[0]), (self.kp, self.k8, self.s8[1]),
+                              (self.vp, self.v8, self.s8[2])):
+                B.quantize_fp8(x, x8, sc, workspace=self.ws_q8)
+            B.varblock_attn_fp8(self.q8, self.k8, self.v8, self.s8[0], self.s8[1], self.s8[2], self.off_q,
+                                self.off_k, self.sel_count, self.sel_idx, scale=self.scale, out=self.op,
+                                workspace=self.ws_attn)
+            return
         B.varblock_attn(self.qp, self.kp, self.vp, self.off_q, self.off_k, self.sel_count, self.sel_idx,
                         scale=self.scale, out=self.op, workspace=self.ws_attn)
 

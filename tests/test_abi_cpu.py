@@ -179,3 +179,29 @@ def test_recall_mass_validation():
     assert L.svg2_recall_mass(None, FAKE, 1, 10, FAKE, None) == INVALID
     assert L.svg2_recall_mass(FAKE, FAKE + 2, 1, 10, FAKE, None) == INVALID
     assert L.svg2_recall_mass(FAKE, FAKE, 1, 10, FAKE + 4, None) == INVALID
+
+
+def test_fp8_validation():
+    L = B.lib()
+    ws = FAKE
+    assert L.svg2_quantize_fp8_workspace_size(0) == 0
+    assert L.svg2_quantize_fp8(FAKE, 0, 10, 128, FAKE, FAKE, ws, 1 << 20, None) == INVALID
+    assert L.svg2_quantize_fp8(FAKE, 1, 10, 96, FAKE, FAKE, ws, 1 << 20, None) == UNSUPPORTED
+    assert L.svg2_quantize_fp8(None, 1, 10, 128, FAKE, FAKE, ws, 1 << 20, None) == INVALID
+    assert L.svg2_quantize_fp8(FAKE, 1, 10, 128, FAKE + 8, FAKE, ws, 1 << 20, None) == INVALID
+    assert L.svg2_quantize_fp8(FAKE, 4, 10, 128, FAKE, FAKE, ws, 4, None) == WORKSPACE
+
+    def attn(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, sq=FAKE, sk=FAKE, sv=FAKE, bh=2, N=300, d=128, qo=FAKE, nq=5, ko=FAKE, nk=7,
+                 sc=FAKE, si=FAKE, scale=0.088, out=FAKE, lse=None, ws=FAKE, wsn=1 << 30)
+        a.update(kw)
+        return L.svg2_varblock_attn_fp8(a["q"], a["k"], a["v"], a["sq"], a["sk"], a["sv"], a["bh"], a["N"], a["d"],
+                                        a["qo"], a["nq"], a["ko"], a["nk"], a["sc"], a["si"], ctypes.c_float(a["scale"]),
+                                        a["out"], a["lse"], a["ws"], a["wsn"], None)
+    assert attn(d=64) == UNSUPPORTED
+    assert attn(bh=0) == INVALID
+    assert attn(nq=0) == INVALID
+    assert attn(sv=None) == INVALID
+    assert attn(k=MISALIGNED) == INVALID
+    assert attn(scale=-1.0) == INVALID
+    assert attn(wsn=8) == WORKSPACE
