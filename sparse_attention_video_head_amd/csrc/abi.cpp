@@ -87,6 +87,22 @@ bool strides_ok(int32_t heads, int32_t bh, int64_t sb, int64_t sh, int64_t st, i
   return sb % q == 0 && sh % q == 0 && st % q == 0;
 }
 
+// Attention work lists; the fp32 kernel uses the smaller row block, hence the
+// larger per-head item list.
+AttnWs carve_attn(Carve& c, int bh, int N, int n_q) {
+  const int bm = attn_block_rows(false) < attn_block_rows(true) ? attn_block_rows(false) : attn_block_rows(true);
+  const size_t mx = (size_t)attn_max_items(N, n_q, attn_block_rows(true));
+  AttnWs w;
+  w.tiles = c.take<int32_t>((size_t)bh * n_q);
+  w.item_count = c.take<int32_t>((size_t)bh);
+  w.items = c.take<int32_t>((size_t)bh * attn_max_items(N, n_q, bm));
+  w.xitems = c.take<int32_t>((size_t)bh * kAttnXcds * mx);
+  w.xcount = c.take<int32_t>((size_t)bh * kAttnXcds);
+  w.queue = c.take<int32_t>(2 * kAttnXcds);
+  w.flat = c.take<int32_t>((size_t)kAttnXcds * bh * mx * 2);
+  return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -239,12 +255,8 @@ size_t svg2_varblock_attn_workspace_size(int32_t bh, int32_t n_tokens, int32_t n
   if (bh < 1 || n_tokens < 1 || n_tokens > kMaxTokens || n_q < 1 || n_q > kMaxClusters || n_k < 1 ||
       n_k > kMaxClusters || !dim_ok(head_dim))
     return 0;
-  // the fp32 kernel uses the smaller row block, hence the larger item list
-  const int bm = attn_block_rows(false) < attn_block_rows(true) ? attn_block_rows(false) : attn_block_rows(true);
   Carve c(nullptr);
-  c.take<int32_t>((size_t)bh * n_q);
-  c.take<int32_t>((size_t)bh);
-  c.take<int32_t>((size_t)bh * attn_max_items(n_tokens, n_q, bm));
+  carve_attn(c, bh, n_tokens, n_q);
   return c.off;
 }
 
@@ -267,13 +279,9 @@ int svg2_varblock_attn(const void* q, const void* k, const void* v, int32_t dtyp
   if (workspace_bytes < need || !workspace) return SVG2_ERR_WORKSPACE;
   if (!aligned(workspace, kAlign)) return SVG2_ERR_INVALID_ARG;
   Carve c(workspace);
-  int32_t* tiles = c.take<int32_t>((size_t)bh * n_q);
-  int32_t* item_count = c.take<int32_t>((size_t)bh);
-  const bool bf16 = dtype == SVG2_BF16;
-  int32_t* items = c.take<int32_t>((size_t)bh * attn_max_items(n_tokens, n_q, attn_block_rows(bf16)));
-  return hip_status(launch_varblock_attn(q, k, v, bf16, bh, n_tokens, head_dim, q_offsets, n_q, k_offsets,
-                                         n_k, sel_count, sel_idx, scale, out, lse, tiles, item_count,
-                                         items, stream));
+  const AttnWs ws = carve_attn(c, bh, n_tokens, n_q);
+  return hip_status(launch_varblock_attn(q, k, v, dtype == SVG2_BF16, bh, n_tokens, head_dim, q_offsets, n_q,
+                                         k_offsets, n_k, sel_count, sel_idx, scale, out, lse, ws, stream));
 }
 
 // ------------------------------------------------------------------ unpermute
@@ -332,12 +340,9 @@ int svg2_varblock_attn_fp8(const void* q8, const void* k8, const void* v8, const
   if (workspace_bytes < need || !workspace) return SVG2_ERR_WORKSPACE;
   if (!aligned(workspace, kAlign)) return SVG2_ERR_INVALID_ARG;
   Carve c(workspace);
-  int32_t* tiles = c.take<int32_t>((size_t)bh * n_q);
-  int32_t* item_count = c.take<int32_t>((size_t)bh);
-  int32_t* items = c.take<int32_t>((size_t)bh * attn_max_items(n_tokens, n_q, attn_block_rows(true)));
+  const AttnWs ws = carve_attn(c, bh, n_tokens, n_q);
   return hip_status(launch_varblock_attn_fp8(q8, k8, v8, q_scale, k_scale, v_scale, bh, n_tokens, q_offsets, n_q,
-                                             k_offsets, n_k, sel_count, sel_idx, scale, out, lse, tiles, item_count,
-                                             items, stream));
+                                             k_offsets, n_k, sel_count, sel_idx, scale, out, lse, ws, stream));
 }
 
 // ------------------------------------------------------- identification study

@@ -63,25 +63,15 @@ __global__ __launch_bounds__(256) void k_attn_lengths(const int32_t* __restrict_
   if (lane == 0) tiles[(size_t)p * n_q + i] = (int32_t)min((keys + tile - 1) / tile, (long long)kSortTilesMax);
 }
 
-// One work-group per problem: the list of (cluster, slab) items, clusters in
-// decreasing order of key tiles (ties: lower cluster index first).  The order
-// comes from a bitonic sort in LDS of (tiles << 12 | 4095 - cluster).
-__global__ __launch_bounds__(1024) void k_attn_plan(const int32_t* __restrict__ q_off, int n_q, int N,
-                                                    int bm, int max_items,
-                                                    const int32_t* __restrict__ tiles,
-                                                    int32_t* __restrict__ item_count,
-                                                    int32_t* __restrict__ items) {
-  __shared__ int32_t scratch[17];
-  __shared__ uint32_t order[kMaxClusters];
-  const int p = blockIdx.x;
-  const int32_t* qo = q_off + (size_t)p * (n_q + 1);
+// Clusters of problem p in decreasing order of key tiles (ties: lower cluster
+// index first): a bitonic sort in LDS of (tiles << 12 | 4095 - cluster); the
+// padding entries (0) end up past n_q because every real entry is positive.
+__device__ __forceinline__ void sort_clusters(uint32_t* order, const int32_t* tiles_p, int n_q) {
   int P = 64;
   while (P < n_q) P <<= 1;
   for (int i = threadIdx.x; i < P; i += blockDim.x)
-    order[i] = i < n_q ? ((uint32_t)tiles[(size_t)p * n_q + i] << 12) | (uint32_t)(kMaxClusters - 1 - i) : 0u;
+    order[i] = i < n_q ? ((uint32_t)tiles_p[i] << 12) | (uint32_t)(kMaxClusters - 1 - i) : 0u;
   __syncthreads();
-  // descending bitonic sort; the padding entries (0) end up past n_q because
-  // every real entry with i < 4095 is positive
   for (int k = 2; k <= P; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
       for (int t = threadIdx.x; t < P / 2; t += blockDim.x) {
@@ -97,6 +87,20 @@ __global__ __launch_bounds__(1024) void k_attn_plan(const int32_t* __restrict__ 
       __syncthreads();
     }
   }
+}
+
+// One work-group per problem: the list of (cluster, slab) items, clusters in
+// decreasing order of key tiles.
+__global__ __launch_bounds__(1024) void k_attn_plan(const int32_t* __restrict__ q_off, int n_q, int N,
+                                                    int bm, int max_items,
+                                                    const int32_t* __restrict__ tiles,
+                                                    int32_t* __restrict__ item_count,
+                                                    int32_t* __restrict__ items) {
+  __shared__ int32_t scratch[17];
+  __shared__ uint32_t order[kMaxClusters];
+  const int p = blockIdx.x;
+  const int32_t* qo = q_off + (size_t)p * (n_q + 1);
+  sort_clusters(order, tiles + (size_t)p * n_q, n_q);
   int nb[4], cl[4];
   int local = 0;
 #pragma unroll
@@ -119,6 +123,73 @@ __global__ __launch_bounds__(1024) void k_attn_plan(const int32_t* __restrict__ 
   for (int e = 0; e < 4; ++e)
     for (int r = 0; r < nb[e] && base < max_items; ++r, ++base) it[base] = cl[e] | (r << 12);
   if (threadIdx.x == 0) item_count[p] = min(total, max_items);
+}
+
+// Per-XCD work lists.  Each XCD has its own L2, and the slabs of one Q-cluster
+// read the same key list, so a Q-cluster's slabs go to one XCD, where they run
+// side by side and share that list through the L2.  Work of an item in tiles:
+// its key tiles plus a fixed cost for its start (Q rows, the first tiles'
+// latency) and end.
+constexpr int kItemOverheadTiles = 4;
+
+// One work-group per problem: clusters longest first, each to the least
+// loaded XCD so far (all its slabs), the items kept in that order per XCD.
+__global__ __launch_bounds__(1024) void k_attn_plan_xcd(const int32_t* __restrict__ q_off, int n_q, int N,
+                                                        int bm, int max_items,
+                                                        const int32_t* __restrict__ tiles,
+                                                        int32_t* __restrict__ xcount,
+                                                        int32_t* __restrict__ xitems) {
+  __shared__ uint32_t order[kMaxClusters];
+  __shared__ long long s_load[kAttnXcds];
+  __shared__ int s_cnt[kAttnXcds];
+  const int p = blockIdx.x;
+  const int32_t* qo = q_off + (size_t)p * (n_q + 1);
+  sort_clusters(order, tiles + (size_t)p * n_q, n_q);
+  if (threadIdx.x == 0) {
+    for (int x = 0; x < kAttnXcds; ++x) {
+      s_load[x] = 0;
+      s_cnt[x] = 0;
+    }
+    int32_t* out = xitems + (size_t)p * kAttnXcds * max_items;
+    for (int s = 0; s < n_q; ++s) {
+      const int i = kMaxClusters - 1 - (int)(order[s] & (kMaxClusters - 1));
+      const int t = (int)(order[s] >> 12);
+      const int a = clampi(qo[i], 0, N), b = clampi(qo[i + 1], a, N);
+      const int nb = (b - a + bm - 1) / bm;
+      if (nb == 0) continue;
+      int x = 0;
+      for (int y = 1; y < kAttnXcds; ++y)
+        if (s_load[y] < s_load[x]) x = y;
+      s_load[x] += (long long)nb * (t + kItemOverheadTiles);
+      for (int r = 0; r < nb && s_cnt[x] < max_items; ++r) out[(size_t)x * max_items + s_cnt[x]++] = i | (r << 12);
+    }
+    for (int x = 0; x < kAttnXcds; ++x) xcount[p * kAttnXcds + x] = s_cnt[x];
+  }
+}
+
+// One work-group per XCD: that XCD's queue, the problems' lists in problem
+// order as (problem, item) pairs, so that all XCDs work through the problems
+// together (one problem's K and V stay in the last-level cache); resets the
+// queue's counter and sets its item total.
+__global__ __launch_bounds__(256) void k_attn_flatten(const int32_t* __restrict__ xcount,
+                                                      const int32_t* __restrict__ xitems, int bh, int max_items,
+                                                      int32_t* __restrict__ flat, int32_t* __restrict__ queue) {
+  const int x = blockIdx.x;
+  int32_t* f = flat + (size_t)x * bh * max_items * 2;
+  int off = 0;
+  for (int p = 0; p < bh; ++p) {
+    const int c = xcount[p * kAttnXcds + x];
+    const int32_t* src = xitems + ((size_t)p * kAttnXcds + x) * max_items;
+    for (int k = threadIdx.x; k < c; k += blockDim.x) {
+      f[2 * (size_t)(off + k)] = p;
+      f[2 * (size_t)(off + k) + 1] = src[k];
+    }
+    off += c;
+  }
+  if (threadIdx.x == 0) {
+    queue[x] = 0;
+    queue[kAttnXcds + x] = off;
+  }
 }
 
 // Walks the concatenated key ranges of the selected clusters; all threads of a
@@ -322,26 +393,86 @@ struct LdsCursor {
     }
     return filled;
   }
+  // The next tile of `tile` rows, for a lane that loads tile rows row[q]:
+  // when the tile is one run of consecutive keys inside one range, *first is
+  // its first key (rkey[] is left alone), else *first = -1 and rkey[q] is the
+  // key of row row[q], or -1 past the end of the list.  Returns the number of
+  // keys in the tile.  The range walk is uniform (scalar); per range piece a
+  // lane spends two vector ops per row.
+  template <int NR>
+  __device__ __forceinline__ int fill_rows(int tile, const int (&row)[NR], int (&rkey)[NR], int* first) {
+    open();
+    if (rem >= tile) {
+      *first = pos;
+      pos += tile;
+      rem -= tile;
+      return tile;
+    }
+    *first = -1;
+    int c[NR];                                   // key - row of the piece holding each row
+#pragma unroll
+    for (int q = 0; q < NR; ++q) c[q] = 0;
+    int filled = 0;
+    while (filled < tile) {
+      open();
+      if (rem == 0) break;
+      const int take = min(rem, tile - filled);
+      const int cj = pos - filled;
+#pragma unroll
+      for (int q = 0; q < NR; ++q) c[q] = row[q] >= filled ? cj : c[q];
+      filled += take;
+      pos += take;
+      rem -= take;
+    }
+#pragma unroll
+    for (int q = 0; q < NR; ++q) rkey[q] = row[q] < filled ? row[q] + c[q] : -1;
+    return filled;
+  }
 };
 
 // One tile = 32 rows of K (or V).  Each wave fills 8 rows with direct-to-LDS
-// loads of 16 bytes per lane (lane -> row RPI q + lane/CPR, slot lane%CPR of
-// the row); rows past the key list load key 0 (never weighted: their scores
-// are masked to -inf).  `lane_off[q]` is the lane's swizzled byte offset
-// inside its row; one head's rows span less than 4 GiB (N <= 2^24), so the
-// address is the uniform head base plus a 32-bit per-lane offset.
-template <int D>
-__device__ __forceinline__ void dma_rows(const uint16_t* src, lds_u16_t* dst, const int (&key)[4],
-                                         const uint32_t (&lane_off)[4], int wave) {
-  constexpr int CPR = D / 8;
-  constexpr int RPI = kWave / CPR;                  // rows per instruction (4 at D=128)
-  constexpr int INS = 8 / RPI;                      // instructions per 8 rows
-#pragma unroll
-  for (int q = 0; q < INS; ++q) {
-    const uint32_t off = (uint32_t)max(key[q], 0) * (uint32_t)(D * 2) + lane_off[q];
-    const void* g = (const void*)((const char*)src + off);
-    __builtin_amdgcn_global_load_lds(g, (lds_void_t*)(dst + (8 * wave + RPI * q) * D), 16, 0, 0);
-  }
+// buffer loads of 16 bytes per lane: lane -> row RPI q + lane/CPR of the
+// wave's 8, 16-byte slot lane%CPR of the row (swizzled); the hardware writes
+// lane i's 16 bytes at m0 + 16 i.  The buffer descriptor spans one head's rows
+// (at most 2^32 bytes: N <= 2^24, D <= 128), the byte offset is 32-bit.
+//
+// The loads are inline assembly.  As compiler-visible loads into LDS, a
+// global load would make the compiler wait for every LDS read in flight
+// wherever it waits for one, and either kind makes it wait for the loads
+// themselves before reads of buffers it cannot tell apart.  The kernel orders
+// these loads itself: an explicit vmcnt wait for the tile, then a barrier.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4_t head_rsrc(const void* base, int N, int D) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  const uint64_t bytes = (uint64_t)N * (uint64_t)D * 2u;
+  i32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));   // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(bytes > 0xffffffffu ? 0xffffffffu : bytes));
+  r[3] = 0x00020000;                                                               // raw 32-bit data
+  return r;
+}
+
+// 16 bytes per lane from buffer offset voff + soff to LDS byte address
+// lds + 16 * lane (lds and soff uniform).  m0 carries the LDS address; it is
+// saved and restored around the load (the compiler keeps m0 for itself), and
+// the load waits one cycle after m0 is written.
+__device__ __forceinline__ void lds_dma16(i32x4_t rsrc, uint32_t lds, uint32_t voff, uint32_t soff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %[sv], m0\n\t"
+      "s_mov_b32 m0, %[lds]\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %[vo], %[rs], %[so] offen lds\n\t"
+      "s_mov_b32 m0, %[sv]"
+      : [sv] "=&s"(saved)
+      : [lds] "s"(lds), [vo] "v"(voff), [rs] "s"(rsrc), [so] "s"(soff)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
 }
 
 // Per wave and 32-key tile the work is two matrix-core phases, S^T = K Q^T
@@ -349,278 +480,327 @@ __device__ __forceinline__ void dma_rows(const uint16_t* src, lds_u16_t* dst, co
 // between them on the vector ALU.  Three work-groups share a CU (52 KB of LDS
 // and at most 168 registers each), so every SIMD holds three waves and the
 // matrix core of one overlaps the softmax of another.  K and V tiles go
-// through rings of 3 LDS buffers (tile j in slot j % 3) and are loaded 2
-// tiles ahead:
-//   iteration t:  load K, V of tile t+2 -> slot (t+2) % 3
-//                 S[t] = K[t] Q^T;  softmax;  O += V[t]^T P[t]^T
-//                 wait for the loads of tiles <= t+1, barrier
+// through a ring of 3 LDS slots (tile j in slot j % 3), loaded 2 tiles ahead:
+//   step t:  load K, V of tile t+2 -> slot (t+2) % 3
+//            S[t] = K[t] Q^T;  softmax;  O += V[t]^T P[t]^T
+//            wait for the loads of tiles <= t+1, barrier
+// The SIMD issues one instruction per cycle for its waves, and an MFMA takes
+// half of its matrix-core time in issue cycles, so the vector work beside the
+// MFMAs bounds the kernel: per step it is kept to the softmax itself (operand
+// addresses are per-lane constants with the slot in the instructions'
+// immediate offsets; a tile inside one key range is loaded with a scalar row
+// offset).
+// The grid is persistent (three work-groups per CU); each work-group takes
+// items from its XCD's queue (a Q-cluster's slabs on one XCD, clusters longest
+// first, problems in order) until every queue is empty.
 template <int D>
 __global__ __launch_bounds__(256, 3) void k_attn_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     int N, const int32_t* __restrict__ q_off, int n_q, const int32_t* __restrict__ k_off, int n_k,
     const int32_t* __restrict__ sel_count, const int32_t* __restrict__ sel_idx, float scale_log2,
-    uint16_t* __restrict__ O, float* __restrict__ lse, const int32_t* __restrict__ item_count,
-    const int32_t* __restrict__ items, int max_items, int bh) {
+    uint16_t* __restrict__ O, float* __restrict__ lse, const int32_t* __restrict__ flat,
+    int32_t* __restrict__ queue, size_t cap) {
   constexpr int BN = kAttnBN;
   constexpr int KS = D / 16;           // 16-wide k-steps of Q.K
   constexpr int DT = D / 32;           // 32-row tiles of O^T
   constexpr int CPR = D / 8;
   constexpr int RPI = kWave / CPR;
   constexpr int INS = 8 / RPI;
+  constexpr int ROWB = D * 2;          // bytes per K or V row
+  constexpr int SLOT = 2 * BN * ROWB;  // bytes per ring slot: K tile, then V tile
   static_assert(BN == 32 && INS >= 1 && INS <= 4, "tile geometry");
-  // s_waitcnt immediates: vmcnt = the loads of one tile, or 0; expcnt and
-  // lgkmcnt left at their maxima (not waited for)
+  // s_waitcnt immediates: vmcnt = the loads of one tile; expcnt and lgkmcnt
+  // left at their maxima (not waited for)
   constexpr int kWaitTile = 0xF70 | (2 * INS);
-  constexpr int kWaitAll = 0xF70;
-  // ring slot j: K tile at [0, BN*D), V tile at [BN*D, 2*BN*D); one array per
-  // slot keeps the number of distinct LDS objects that the loads write small
-  // enough for the compiler to track each of them separately
-  __shared__ __attribute__((aligned(16))) uint16_t sT0[2 * BN * D], sT1[2 * BN * D], sT2[2 * BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t sT[3 * 2 * BN * D];
   __shared__ int s_rs[kRangeChunk], s_rl[kRangeChunk];
+  __shared__ int s_job[2];
 
-  const int total = max_items * bh;
-  const int jx = (int)(blockIdx.x / kXcds), xx = (int)(blockIdx.x % kXcds);
-  const int logical = ((jx / kXcdChunk) * kXcds + xx) * kXcdChunk + jx % kXcdChunk;
-  if (logical >= total) return;
-  const int p = logical / max_items, slot = logical % max_items;
-  if (slot >= item_count[p]) return;
-  const int item = items[(size_t)p * max_items + slot];
-  const int ci = item & 0xfff, rb = item >> 12;
-  const int32_t* qo = q_off + (size_t)p * (n_q + 1);
-  const int qa = clampi(qo[ci], 0, N), qb = clampi(qo[ci + 1], qa, N);
-  const int tid = threadIdx.x, lane = tid & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int col = lane & 31, half = lane >> 5;
-  const int row0 = qa + rb * kAttnBM + wave * 32;
-  const bool active = row0 < qb;                 // this wave has query rows
-  const int row = row0 + col;
-  const bool row_ok = row < qb;
-  const size_t base = (size_t)p * N * D;
-  const uint16_t* Kp = K + base;
-  const uint16_t* Vp = V + base;
-
-  bf16x8_t qf[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    u32x4_t v = {0u, 0u, 0u, 0u};
-    if (row_ok) v = *reinterpret_cast<const u32x4_t*>(Q + base + (size_t)row * D + ks * 16 + half * 8);
-    qf[ks] = __builtin_bit_cast(bf16x8_t, v);
-  }
-
-  // this lane's tile rows (one per direct-to-LDS load)
-  int slot_of[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) slot_of[q] = q < INS ? 8 * wave + RPI * q + lane / CPR : -1;
-
-  LdsCursor cur;
-  cur.init(sel_idx + ((size_t)p * n_q + ci) * n_k, k_off + (size_t)p * (n_k + 1),
-           clampi(sel_count[(size_t)p * n_q + ci], 0, n_k), n_k, N, s_rs, s_rl);
-
-  float m_ref = -__builtin_inff();
-  float l_part = 0.f;                            // this lane's share of the row sum
-  f32x16_t o[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
-
-  // per-lane LDS offsets (elements) of the operand reads
-  //   K (S^T = K Q^T): row col, chunk 2 ks + half
-  //   V^T (transposing read): rows 4 half + (lane%16)/4 (+ 16 kk, + 8),
-  //   columns dt*32 + 16 ((lane/16)%2) + 4 (lane%4); the swizzle depends on
-  //   the row only through row % 4, which the added rows keep
-  int koff[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) koff[ks] = col * D + TileGeom<D>::k_chunk(col, 2 * ks + half) * 8;
-  const int vr = (lane & 15) >> 2;
-  const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  int voff[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    const int r = 4 * half + vr, c0 = dt * 32 + vcol;
-    voff[dt] = r * D + TileGeom<D>::v_chunk(r, c0 >> 3) * 8 + (c0 & 7);
-  }
-  // byte offsets of this lane's 16-byte slot within its tile row, swizzled
-  uint32_t kl_off[4], vl_off[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r = 8 * wave + RPI * q + lane / CPR;
-    kl_off[q] = (uint32_t)TileGeom<D>::k_chunk(r, lane % CPR) * 16u;
-    vl_off[q] = (uint32_t)TileGeom<D>::v_chunk(r, lane % CPR) * 16u;
-  }
-
-  // S^T for the 32 keys of a K tile; lane holds query `col` and keys
-  // (i/4)*8 + half*4 + i%4
-  // The K fragments are read kAhead k-steps ahead of their MFMA, so the LDS
-  // latency overlaps the matrix core instead of sitting before every step.
-  // The scheduling groups pin that order (mask 0x100: LDS reads, 0x008: MFMA);
-  // left alone, the scheduler pairs each read with its MFMA and waits on it.
-  auto scores = [&](const lds_u16_t* kb, f32x16_t& s) __attribute__((always_inline)) {
-    constexpr int kAhead = KS < 2 ? KS : 2;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = 0.f;
-    bf16x8_t a[KS];
-#pragma unroll
-    for (int ks = 0; ks < kAhead; ++ks) a[ks] = *(const __attribute__((address_space(3))) bf16x8_t*)(kb + koff[ks]);
-    __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (ks + kAhead < KS)
-        a[ks + kAhead] = *(const __attribute__((address_space(3))) bf16x8_t*)(kb + koff[ks + kAhead]);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qf[ks], s, 0, 0, 0);
-      if (ks + kAhead < KS) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      } else {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  // Work items come from the queue of the XCD this work-group runs on (hardware
+  // register XCC_ID), then, once it is empty, from the other XCDs' queues.
+  const int xcc = __builtin_amdgcn_s_getreg((3 << 11) | 20) & (kAttnXcds - 1);
+  for (int qx = 0; qx < kAttnXcds; ++qx) {
+    const int x = (xcc + qx) & (kAttnXcds - 1);
+    const int total_x = queue[kAttnXcds + x];
+    for (;;) {
+      __syncthreads();                               // the previous item is done with LDS
+      if (threadIdx.x == 0) {
+        const int j = atomicAdd(&queue[x], 1);
+        int pj = -1, ij = 0;
+        if (j < total_x) {
+          pj = flat[2 * ((size_t)x * cap + j)];
+          ij = flat[2 * ((size_t)x * cap + j) + 1];
+        }
+        s_job[0] = pj;
+        s_job[1] = ij;
       }
-    }
-  };
-  // Scores, softmax and O^T += V^T P^T of one tile (K from `kb`, V from `vb`).
-  auto step = [&](const lds_u16_t* kb, const lds_u16_t* vb, int filled) __attribute__((always_inline)) {
-    f32x16_t sc;
-    scores(kb, sc);
-    if (filled < BN) {
-      // key of score i: (i/4)*8 + 4*half + i%4; compared against the list end
-      // shifted by this lane's half, so every compare takes an inline constant
-      const int lim = filled - 4 * half;
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if ((i >> 2) * 8 + (i & 3) >= lim) sc[i] = -__builtin_inff();
-    }
-    float mx = sc[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
-    {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
-    }
-    if (mx > m_ref + kLazyTau) {
-      const float alpha = __builtin_amdgcn_exp2f(m_ref - mx);
-      l_part *= alpha;
-#pragma unroll
+      __syncthreads();
+      const int p = s_job[0];
+      if (p < 0) break;
+      const int item = s_job[1];
+      const int ci = item & 0xfff, rb = item >> 12;
+      const int32_t* qo = q_off + (size_t)p * (n_q + 1);
+      const int qa = clampi(qo[ci], 0, N), qb = clampi(qo[ci + 1], qa, N);
+      const int tid = threadIdx.x, lane = tid & (kWave - 1);
+      const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+      const int col = lane & 31, half = lane >> 5;
+      const int row0 = qa + rb * kAttnBM + wave * 32;
+      const bool active = row0 < qb;                 // this wave has query rows
+      const int row = row0 + col;
+      const bool row_ok = row < qb;
+      const size_t base = (size_t)p * N * D;
+      const i32x4_t Kr = head_rsrc(K + base, N, D);
+      const i32x4_t Vr = head_rsrc(V + base, N, D);
+
+      bf16x8_t qf[KS];
+    #pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (row_ok) v = *reinterpret_cast<const u32x4_t*>(Q + base + (size_t)row * D + ks * 16 + half * 8);
+        qf[ks] = __builtin_bit_cast(bf16x8_t, v);
+      }
+
+      // this lane's tile rows (one per direct-to-LDS load)
+      int trow[INS];
+    #pragma unroll
+      for (int q = 0; q < INS; ++q) trow[q] = 8 * wave + RPI * q + lane / CPR;
+
+      LdsCursor cur;
+      cur.init(sel_idx + ((size_t)p * n_q + ci) * n_k, k_off + (size_t)p * (n_k + 1),
+               clampi(sel_count[(size_t)p * n_q + ci], 0, n_k), n_k, N, s_rs, s_rl);
+      // The Q rows have landed by now; saying so here, before any tile load is in
+      // flight, keeps the compiler from waiting for every load (the tile loads
+      // included) at the first use of Q in each step.
+      __builtin_amdgcn_s_waitcnt(0xF70);
+
+      float m_ref = -__builtin_inff();
+      float l_part = 0.f;                            // this lane's share of the row sum
+      f32x16_t o[DT];
+    #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
-      m_ref = mx;
-    }
-    const float neg = -m_ref;
-    u32x4_t pw[2];
-#pragma unroll
-    for (int i = 0; i < 16; i += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[i], scale_log2, neg));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[i + 1], scale_log2, neg));
-      l_part += p0 + p1;
-      pw[i >> 3][(i & 7) >> 1] = pack_bf16x2(p0, p1);
-    }
-    // V^T fragments: two transposing reads per MFMA, issued kAhead MFMAs early
-    constexpr int NV = 2 * DT;
-    constexpr int kAhead = NV < 2 ? NV : 2;
-    auto vread = [&](int j) __attribute__((always_inline)) {
-      const int kk = j / DT, dt = j % DT;
-      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb + (voff[dt] + 16 * kk * D)));
-      const s16x4_t hi =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vb + (voff[dt] + (16 * kk + 8) * D)));
-      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    bf16x8_t va[NV];
-#pragma unroll
-    for (int j = 0; j < kAhead; ++j) va[j] = vread(j);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      if (j + kAhead < NV) va[j + kAhead] = vread(j + kAhead);
-      const int kk = j / DT, dt = j % DT;
-      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j], __builtin_bit_cast(bf16x8_t, pw[kk]), o[dt], 0, 0, 0);
-      if (j + kAhead < NV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    }
-  };
+    #pragma unroll
+        for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
 
-  lds_u16_t* k0 = to_lds(sT0);
-  lds_u16_t* k1 = to_lds(sT1);
-  lds_u16_t* k2 = to_lds(sT2);
-  lds_u16_t* v0 = k0 + BN * D;
-  lds_u16_t* v1 = k1 + BN * D;
-  lds_u16_t* v2 = k2 + BN * D;
-
-  // keys of tiles t, t+1 (0: no such tile)
-  int key[4];
-  int f0 = cur.fill<4>(BN, slot_of, key);
-  if (f0 > 0) {
-    dma_rows<D>(Kp, k0, key, kl_off, wave);
-    dma_rows<D>(Vp, v0, key, vl_off, wave);
-  }
-  int f1 = f0 > 0 ? cur.fill<4>(BN, slot_of, key) : 0;
-  if (f1 > 0) {
-    dma_rows<D>(Kp, k1, key, kl_off, wave);
-    dma_rows<D>(Vp, v1, key, vl_off, wave);
-    __builtin_amdgcn_s_waitcnt(kWaitTile);       // tile 0 has landed
-  } else {
-    __builtin_amdgcn_s_waitcnt(kWaitAll);
-  }
-  lds_barrier();
-
-  // The loads are issued even past the end of the key list (all slots then
-  // read key 0 and the tile is never used): an unconditional load keeps the
-  // compiler's per-buffer tracking of them intact, so it adds no waits of its
-  // own before the LDS reads.  At the loop head that tracking is lost and the
-  // compiler waits for every load before the first LDS read, so the first
-  // tile of each trip issues its loads after its compute (`late`).
-  auto iter = [&](auto late, const lds_u16_t* kc, const lds_u16_t* vc, lds_u16_t* kd, lds_u16_t* vd)
-      __attribute__((always_inline)) -> bool {
-    int f2 = 0;
-    if (f1 > 0) {
-      f2 = cur.fill<4>(BN, slot_of, key);
-    } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) key[q] = -1;
-    }
-    if constexpr (!decltype(late)::value) {
-      dma_rows<D>(Kp, kd, key, kl_off, wave);
-      dma_rows<D>(Vp, vd, key, vl_off, wave);
-    }
-    if (active) step(kc, vc, f0);
-    if constexpr (decltype(late)::value) {
-      dma_rows<D>(Kp, kd, key, kl_off, wave);
-      dma_rows<D>(Vp, vd, key, vl_off, wave);
-    }
-    __builtin_amdgcn_s_waitcnt(kWaitTile);       // tiles <= t+1 have landed
-    lds_barrier();
-    f0 = f1;
-    f1 = f2;
-    return f0 > 0;
-  };
-  // three tiles per trip so that every LDS buffer is a distinct static array
-  if (f0 > 0) {
-    constexpr std::true_type late{};
-    constexpr std::false_type early{};
-    while (iter(late, k0, v0, k2, v2) && iter(early, k1, v1, k0, v0) && iter(early, k2, v2, k1, v1)) {
-    }
-  }
-
-  // lanes i and i+32 hold the two halves of query col's keys
-  float l_tot;
-  {
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part), __float_as_uint(l_part), false, false);
-    l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-  }
-  if (row_ok) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* orow = O + base + (size_t)row * D;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        uint2 w;
-        w.x = pack_bf16x2(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv);
-        w.y = pack_bf16x2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv);
-        *reinterpret_cast<uint2*>(orow + dt * 32 + g * 8 + half * 4) = w;
+      // LDS byte addresses (slot 0) of the operand reads; the asm statements hide
+      // their range from the compiler, which would otherwise turn the slot's add
+      // into a vector op per read instead of the reads' immediate offset
+      //   K (S^T = K Q^T): row col, chunk 2 ks + half
+      //   V^T (transposing read): rows 4 half + (lane%16)/4 (+ 16 kk, + 8),
+      //   columns dt*32 + 16 ((lane/16)%2) + 4 (lane%4); the swizzle depends on
+      //   the row only through row % 4, which the added rows keep
+      const uint32_t lds0 = lds_addr(sT);
+      uint32_t kaddr[KS];
+    #pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        kaddr[ks] = lds0 + (uint32_t)(col * ROWB + TileGeom<D>::k_chunk(col, 2 * ks + half) * 16);
+        asm volatile("" : "+v"(kaddr[ks]));
       }
-    if (lse && half == 0)
-      lse[(size_t)p * N + row] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * 0.69314718055994531f
-                                            : -__builtin_inff();
-  }
+      const int vr = (lane & 15) >> 2;
+      const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+      uint32_t vaddr[DT];
+    #pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int r = 4 * half + vr, c0 = dt * 32 + vcol;
+        vaddr[dt] = lds0 + (uint32_t)(BN * ROWB + r * ROWB + TileGeom<D>::v_chunk(r, c0 >> 3) * 16 + (c0 & 7) * 2);
+        asm volatile("" : "+v"(vaddr[dt]));
+      }
+      // this lane's source offsets for its tile rows: within the tile (a run of
+      // consecutive keys from a scalar first key), and the swizzled 16-byte slot
+      // within the row (a tile assembled from several key ranges)
+      uint32_t kl_off[INS], vl_off[INS], krun[INS], vrun[INS];
+    #pragma unroll
+      for (int q = 0; q < INS; ++q) {
+        const int r = 8 * wave + RPI * q + lane / CPR;
+        kl_off[q] = (uint32_t)TileGeom<D>::k_chunk(r, lane % CPR) * 16u;
+        vl_off[q] = (uint32_t)TileGeom<D>::v_chunk(r, lane % CPR) * 16u;
+        krun[q] = (uint32_t)r * ROWB + kl_off[q];
+        vrun[q] = (uint32_t)r * ROWB + vl_off[q];
+      }
+      // Loads of one tile into ring slot `s` (compile-time): 2 INS instructions
+      // per wave on every path, so that the vmcnt waits count the same loads.
+      auto load_tile = [&](int s, int first, const int (&key)[INS]) __attribute__((always_inline)) {
+        const uint32_t kdst = lds0 + (uint32_t)(s * SLOT + 8 * wave * ROWB);
+        if (first >= 0) {
+          const uint32_t so = (uint32_t)__builtin_amdgcn_readfirstlane(first * ROWB);   // uniform by construction
+    #pragma unroll
+          for (int q = 0; q < INS; ++q) {
+            lds_dma16(Kr, kdst + (uint32_t)(RPI * q * ROWB), krun[q], so);
+            lds_dma16(Vr, kdst + (uint32_t)(BN * ROWB + RPI * q * ROWB), vrun[q], so);
+          }
+        } else {
+    #pragma unroll
+          for (int q = 0; q < INS; ++q) {
+            const uint32_t ro = (uint32_t)max(key[q], 0) * ROWB;
+            lds_dma16(Kr, kdst + (uint32_t)(RPI * q * ROWB), ro + kl_off[q], 0u);
+            lds_dma16(Vr, kdst + (uint32_t)(BN * ROWB + RPI * q * ROWB), ro + vl_off[q], 0u);
+          }
+        }
+      };
+      auto kread = [&](int s, int ks) __attribute__((always_inline)) {
+        return *(const __attribute__((address_space(3))) bf16x8_t*)(uintptr_t)(kaddr[ks] + (uint32_t)(s * SLOT));
+      };
+      auto vread = [&](int s, int j) __attribute__((always_inline)) {
+        const int kk = j / DT, dt = j % DT;
+        const uint32_t a = vaddr[dt] + (uint32_t)(s * SLOT + 16 * kk * ROWB);
+        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)a);
+        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)(a + 8 * ROWB));
+        return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+
+      // S^T for the 32 keys of the K tile in slot s; lane holds query `col` and
+      // keys (i/4)*8 + half*4 + i%4.  The K fragments are read kAhead k-steps
+      // ahead of their MFMA, so the LDS latency overlaps the matrix core instead
+      // of sitting before every step.  The scheduling groups pin that order (mask
+      // 0x100: LDS reads, 0x008: MFMA); left alone, the scheduler pairs each read
+      // with its MFMA and waits on it.
+      auto scores = [&](int s, f32x16_t& sc) __attribute__((always_inline)) {
+        constexpr int kAhead = KS < 2 ? KS : 2;
+    #pragma unroll
+        for (int i = 0; i < 16; ++i) sc[i] = 0.f;
+        bf16x8_t a[KS];
+    #pragma unroll
+        for (int ks = 0; ks < kAhead; ++ks) a[ks] = kread(s, ks);
+        __builtin_amdgcn_s_setprio(1);
+        __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+    #pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          if (ks + kAhead < KS) a[ks + kAhead] = kread(s, ks + kAhead);
+          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qf[ks], sc, 0, 0, 0);
+          if (ks + kAhead < KS) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          } else {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          }
+        }
+      };
+      // Scores, softmax and O^T += V^T P^T of the tile in slot s.
+      auto step = [&](int s, int filled) __attribute__((always_inline)) {
+        f32x16_t sc;
+        scores(s, sc);
+        __builtin_amdgcn_s_setprio(0);
+        if (filled < BN) {
+          // key of score i: (i/4)*8 + 4*half + i%4; compared against the list end
+          // shifted by this lane's half, so every compare takes an inline constant
+          const int lim = filled - 4 * half;
+    #pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if ((i >> 2) * 8 + (i & 3) >= lim) sc[i] = -__builtin_inff();
+        }
+        float mx = sc[0];
+    #pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+        {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+          mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
+        }
+        if (mx > m_ref + kLazyTau) {
+          const float alpha = __builtin_amdgcn_exp2f(m_ref - mx);
+          l_part *= alpha;
+    #pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+    #pragma unroll
+            for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+          m_ref = mx;
+        }
+        const float neg = -m_ref;
+        u32x4_t pw[2];
+    #pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[i], scale_log2, neg));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[i + 1], scale_log2, neg));
+          l_part += p0 + p1;
+          pw[i >> 3][(i & 7) >> 1] = pack_bf16x2(p0, p1);
+        }
+        // V^T fragments: two transposing reads per MFMA, issued kAhead MFMAs early
+        constexpr int NV = 2 * DT;
+        constexpr int kAhead = NV < 2 ? NV : 2;
+        bf16x8_t va[NV];
+    #pragma unroll
+        for (int j = 0; j < kAhead; ++j) va[j] = vread(s, j);
+        __builtin_amdgcn_s_setprio(1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
+    #pragma unroll
+        for (int j = 0; j < NV; ++j) {
+          if (j + kAhead < NV) va[j + kAhead] = vread(s, j + kAhead);
+          const int kk = j / DT, dt = j % DT;
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j], __builtin_bit_cast(bf16x8_t, pw[kk]), o[dt], 0, 0, 0);
+          if (j + kAhead < NV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_s_setprio(0);
+      };
+
+      // tiles 0 and 1 -> slots 0 and 1.  The loads are issued even past the end
+      // of the key list (all rows then read key 0 and the tile is never used), so
+      // that every step has the same loads in flight.
+      int key[INS];
+      int first;
+      int f0 = cur.fill_rows<INS>(BN, trow, key, &first);
+      load_tile(0, first, key);
+      int f1 = 0;
+      if (f0 > 0) {
+        f1 = cur.fill_rows<INS>(BN, trow, key, &first);
+      } else {
+        first = -1;
+    #pragma unroll
+        for (int q = 0; q < INS; ++q) key[q] = -1;
+      }
+      load_tile(1, first, key);
+      __builtin_amdgcn_s_waitcnt(kWaitTile);         // tile 0 has landed
+      lds_barrier();
+
+      // step t (tile t in slot s = t % 3, compile-time): load tile t+2 into slot
+      // (s+2) % 3, compute tile t, wait for tile t+1, barrier
+      auto iter = [&](auto sc_) __attribute__((always_inline)) -> bool {
+        constexpr int s = decltype(sc_)::value;
+        int f2 = 0;
+        if (f1 > 0) {
+          f2 = cur.fill_rows<INS>(BN, trow, key, &first);
+        } else {
+          first = -1;
+    #pragma unroll
+          for (int q = 0; q < INS; ++q) key[q] = -1;
+        }
+        load_tile((s + 2) % 3, first, key);
+        if (active) step(s, f0);
+        __builtin_amdgcn_s_waitcnt(kWaitTile);       // tiles <= t+1 have landed
+        lds_barrier();
+        f0 = f1;
+        f1 = f2;
+        return f0 > 0;
+      };
+      if (f0 > 0) {
+        while (iter(std::integral_constant<int, 0>{}) && iter(std::integral_constant<int, 1>{}) &&
+               iter(std::integral_constant<int, 2>{})) {
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xF70);             // no tile load outlives the loop
+
+      // lanes i and i+32 hold the two halves of query col's keys
+      float l_tot;
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part), __float_as_uint(l_part), false, false);
+        l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      }
+      if (row_ok) {
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        uint16_t* orow = O + base + (size_t)row * D;
+    #pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+    #pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            uint2 w;
+            w.x = pack_bf16x2(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv);
+            w.y = pack_bf16x2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv);
+            *reinterpret_cast<uint2*>(orow + dt * 32 + g * 8 + half * 4) = w;
+          }
+        if (lse && half == 0)
+          lse[(size_t)p * N + row] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * 0.69314718055994531f
+                                                : -__builtin_inff();
+      }
+    }  // items of queue x
+  }  // queues
 }
 
 // ---------------------------------------------------------------- fp8
@@ -978,36 +1158,49 @@ __global__ __launch_bounds__(128) void k_attn_f32(
   }
 }
 
+// Resident work-groups of the bf16 kernel: three per CU, a multiple of the
+// XCD count.
+static int attn_persistent_grid() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                               hipSuccess || cus < 1)
+    cus = 256;
+  const int g = cus * 3 / kAttnXcds * kAttnXcds;
+  return g < kAttnXcds ? kAttnXcds : g;
+}
+
 hipError_t launch_varblock_attn(const void* q, const void* k, const void* v, bool bf16, int bh,
                                 int N, int d, const int32_t* q_off, int n_q, const int32_t* k_off,
                                 int n_k, const int32_t* sel_count, const int32_t* sel_idx,
-                                float scale, void* out, float* lse, int32_t* tiles_ws,
-                                int32_t* item_count_ws, int32_t* items_ws, hipStream_t s) {
+                                float scale, void* out, float* lse, const AttnWs& ws, hipStream_t s) {
   const int bm = attn_block_rows(bf16);
   const int max_items = attn_max_items(N, n_q, bm);
   hipLaunchKernelGGL(k_attn_lengths, dim3((n_q + 3) / 4, bh), dim3(256), 0, s, k_off, n_k, N, sel_count,
-                     sel_idx, n_q, bf16 ? kAttnBN : 32, tiles_ws);
-  hipLaunchKernelGGL(k_attn_plan, dim3(bh), dim3(1024), 0, s, q_off, n_q, N, bm, max_items, tiles_ws,
-                     item_count_ws, items_ws);
-  const dim3 grid(max_items, bh);
-  const int total = max_items * bh;
-  constexpr int span = kXcds * kXcdChunk;
-  const dim3 grid_x((total + span - 1) / span * span);
+                     sel_idx, n_q, bf16 ? kAttnBN : 32, ws.tiles);
   if (bf16) {
+    hipLaunchKernelGGL(k_attn_plan_xcd, dim3(bh), dim3(1024), 0, s, q_off, n_q, N, bm, max_items, ws.tiles,
+                       ws.xcount, ws.xitems);
+    hipLaunchKernelGGL(k_attn_flatten, dim3(kAttnXcds), dim3(256), 0, s, ws.xcount, ws.xitems, bh, max_items,
+                       ws.flat, ws.queue);
     const float sl2 = scale * 1.4426950408889634f;
+    const size_t cap = (size_t)bh * max_items;
+    const dim3 grid_p(attn_persistent_grid());
 #define SVG2_ATTN(D)                                                                                  \
-  hipLaunchKernelGGL(k_attn_bf16<D>, grid_x, dim3(256), 0, s, static_cast<const uint16_t*>(q),        \
+  hipLaunchKernelGGL(k_attn_bf16<D>, grid_p, dim3(256), 0, s, static_cast<const uint16_t*>(q),        \
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), N, q_off, n_q, \
-                     k_off, n_k, sel_count, sel_idx, sl2, static_cast<uint16_t*>(out), lse,          \
-                     item_count_ws, items_ws, max_items, bh)
+                     k_off, n_k, sel_count, sel_idx, sl2, static_cast<uint16_t*>(out), lse, ws.flat,   \
+                     ws.queue, cap)
     if (d == 128) SVG2_ATTN(128); else SVG2_ATTN(64);
 #undef SVG2_ATTN
   } else {
+    hipLaunchKernelGGL(k_attn_plan, dim3(bh), dim3(1024), 0, s, q_off, n_q, N, bm, max_items, ws.tiles,
+                       ws.item_count, ws.items);
+    const dim3 grid(max_items, bh);
 #define SVG2_ATTN(D)                                                                                   \
   hipLaunchKernelGGL(k_attn_f32<D>, grid, dim3(128), 0, s, static_cast<const float*>(q),               \
                      static_cast<const float*>(k), static_cast<const float*>(v), N, q_off, n_q, k_off, \
-                     n_k, sel_count, sel_idx, scale, static_cast<float*>(out), lse, item_count_ws,    \
-                     items_ws, max_items)
+                     n_k, sel_count, sel_idx, scale, static_cast<float*>(out), lse, ws.item_count,    \
+                     ws.items, max_items)
     if (d == 128) SVG2_ATTN(128); else SVG2_ATTN(64);
 #undef SVG2_ATTN
   }
@@ -1018,9 +1211,11 @@ hipError_t launch_varblock_attn_fp8(const void* q, const void* k, const void* v,
                                     const float* k_scale, const float* v_scale, int bh, int N,
                                     const int32_t* q_off, int n_q, const int32_t* k_off, int n_k,
                                     const int32_t* sel_count, const int32_t* sel_idx, float scale, void* out,
-                                    float* lse, int32_t* tiles_ws, int32_t* item_count_ws, int32_t* items_ws,
-                                    hipStream_t s) {
+                                    float* lse, const AttnWs& ws, hipStream_t s) {
   const int max_items = attn_max_items(N, n_q, kAttnBM);
+  int32_t* tiles_ws = ws.tiles;
+  int32_t* item_count_ws = ws.item_count;
+  int32_t* items_ws = ws.items;
   hipLaunchKernelGGL(k_attn_lengths, dim3((n_q + 3) / 4, bh), dim3(256), 0, s, k_off, n_k, N, sel_count, sel_idx,
                      n_q, kAttnF8BN, tiles_ws);
   hipLaunchKernelGGL(k_attn_plan, dim3(bh), dim3(1024), 0, s, q_off, n_q, N, kAttnBM, max_items, tiles_ws,

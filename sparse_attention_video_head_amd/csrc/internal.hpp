@@ -58,12 +58,24 @@ hipError_t launch_select_topp(const float* cq, const int32_t* q_counts, int n_q,
 // ----------------------------------------------------------------- attn.hip
 int attn_block_rows(bool bf16);
 inline int attn_max_items(int N, int n_q, int bm) { return (N + bm - 1) / bm + n_q; }
-// workspace: tiles [bh, n_q], item_count [bh], items [bh, attn_max_items] (all int32)
+// Attention work lists, carved from the caller's workspace (all int32).  The
+// bf16 kernel takes its items from per-XCD queues: xitems/xcount hold each
+// head's items per XCD, flat the queue of each XCD (heads in order, pairs of
+// (head, item)), queue each XCD's next-item counter and item total.
+constexpr int kAttnXcds = 8;
+struct AttnWs {
+  int32_t* tiles;        // [bh, n_q] key tiles per Q-cluster
+  int32_t* item_count;   // [bh] items per head
+  int32_t* items;        // [bh, attn_max_items(N, n_q, smallest row block)]
+  int32_t* xitems;       // [bh, kAttnXcds, attn_max_items(N, n_q, 128)]
+  int32_t* xcount;       // [bh, kAttnXcds]
+  int32_t* queue;        // [2 kAttnXcds]
+  int32_t* flat;         // [kAttnXcds, bh * attn_max_items(N, n_q, 128), 2]
+};
 hipError_t launch_varblock_attn(const void* q, const void* k, const void* v, bool bf16, int bh,
                                 int N, int d, const int32_t* q_off, int n_q, const int32_t* k_off,
                                 int n_k, const int32_t* sel_count, const int32_t* sel_idx,
-                                float scale, void* out, float* lse, int32_t* tiles_ws,
-                                int32_t* item_count_ws, int32_t* items_ws, hipStream_t s);
+                                float scale, void* out, float* lse, const AttnWs& ws, hipStream_t s);
 
 // FP8 (E4M3) Q, K, V with per-problem scales, head_dim 128, bf16 output; the
 // same workspace as launch_varblock_attn (row block kAttnBM).
@@ -71,8 +83,7 @@ hipError_t launch_varblock_attn_fp8(const void* q, const void* k, const void* v,
                                     const float* k_scale, const float* v_scale, int bh, int N,
                                     const int32_t* q_off, int n_q, const int32_t* k_off, int n_k,
                                     const int32_t* sel_count, const int32_t* sel_idx, float scale, void* out,
-                                    float* lse, int32_t* tiles_ws, int32_t* item_count_ws, int32_t* items_ws,
-                                    hipStream_t s);
+                                    float* lse, const AttnWs& ws, hipStream_t s);
 
 // ---------------------------------------------------------------- quant.hip
 // x8 = E4M3(x / scale), scale[p] = max|x_p| / 448 (1 if all zero); x bf16
