@@ -134,36 +134,79 @@ constexpr int kItemOverheadTiles = 4;
 
 // One work-group per problem: clusters longest first, each to the least
 // loaded XCD so far (all its slabs), the items kept in that order per XCD.
+// The greedy pass is sequential (one wave, in registers); the slab counts
+// before it and the item writes after it are parallel.
 __global__ __launch_bounds__(1024) void k_attn_plan_xcd(const int32_t* __restrict__ q_off, int n_q, int N,
                                                         int bm, int max_items,
                                                         const int32_t* __restrict__ tiles,
                                                         int32_t* __restrict__ xcount,
                                                         int32_t* __restrict__ xitems) {
   __shared__ uint32_t order[kMaxClusters];
-  __shared__ long long s_load[kAttnXcds];
-  __shared__ int s_cnt[kAttnXcds];
+  __shared__ int s_nb[kMaxClusters];            // slabs of sorted cluster s, then its XCD and first slot
   const int p = blockIdx.x;
   const int32_t* qo = q_off + (size_t)p * (n_q + 1);
   sort_clusters(order, tiles + (size_t)p * n_q, n_q);
-  if (threadIdx.x == 0) {
-    for (int x = 0; x < kAttnXcds; ++x) {
-      s_load[x] = 0;
-      s_cnt[x] = 0;
+  for (int s = threadIdx.x; s < n_q; s += blockDim.x) {
+    const int i = kMaxClusters - 1 - (int)(order[s] & (kMaxClusters - 1));
+    const int a = clampi(qo[i], 0, N), b = clampi(qo[i + 1], a, N);
+    s_nb[s] = (b - a + bm - 1) / bm;
+  }
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    // wave 0: the greedy pass over 64 clusters at a time, their slab and tile
+    // counts read from the lanes; the XCD loads and counts stay in registers
+    const int lane = threadIdx.x;
+    long long load[kAttnXcds];
+    int cnt[kAttnXcds];
+#pragma unroll
+    for (int y = 0; y < kAttnXcds; ++y) {
+      load[y] = 0;
+      cnt[y] = 0;
     }
-    int32_t* out = xitems + (size_t)p * kAttnXcds * max_items;
-    for (int s = 0; s < n_q; ++s) {
-      const int i = kMaxClusters - 1 - (int)(order[s] & (kMaxClusters - 1));
-      const int t = (int)(order[s] >> 12);
-      const int a = clampi(qo[i], 0, N), b = clampi(qo[i + 1], a, N);
-      const int nb = (b - a + bm - 1) / bm;
-      if (nb == 0) continue;
-      int x = 0;
-      for (int y = 1; y < kAttnXcds; ++y)
-        if (s_load[y] < s_load[x]) x = y;
-      s_load[x] += (long long)nb * (t + kItemOverheadTiles);
-      for (int r = 0; r < nb && s_cnt[x] < max_items; ++r) out[(size_t)x * max_items + s_cnt[x]++] = i | (r << 12);
+    for (int s0 = 0; s0 < n_q; s0 += kWave) {
+      const int sl = s0 + lane;
+      const int nb_l = sl < n_q ? s_nb[sl] : 0;
+      const int t_l = sl < n_q ? (int)(order[sl] >> 12) : 0;
+      int code_l = -1;
+      const int m = min(kWave, n_q - s0);
+      for (int j = 0; j < m; ++j) {
+        const int nb = __builtin_amdgcn_readlane(nb_l, j);
+        const int t = __builtin_amdgcn_readlane(t_l, j);
+        int x = 0;
+        long long lx = load[0];
+#pragma unroll
+        for (int y = 1; y < kAttnXcds; ++y)
+          if (load[y] < lx) {
+            lx = load[y];
+            x = y;
+          }
+        int first = 0;
+#pragma unroll
+        for (int y = 0; y < kAttnXcds; ++y)
+          if (y == x) {
+            first = cnt[y];
+            if (nb > 0) load[y] += (long long)nb * (t + kItemOverheadTiles);
+            cnt[y] = min(first + nb, max_items);
+          }
+        if (lane == j) code_l = nb > 0 ? (x << 24) | first : -1;   // first < max_items < 2^24
+      }
+      if (sl < n_q) s_nb[sl] = code_l;
     }
-    for (int x = 0; x < kAttnXcds; ++x) xcount[p * kAttnXcds + x] = s_cnt[x];
+    if (lane == 0) {
+#pragma unroll
+      for (int y = 0; y < kAttnXcds; ++y) xcount[p * kAttnXcds + y] = cnt[y];
+    }
+  }
+  __syncthreads();
+  int32_t* out = xitems + (size_t)p * kAttnXcds * max_items;
+  for (int s = threadIdx.x; s < n_q; s += blockDim.x) {
+    const int code = s_nb[s];
+    if (code < 0) continue;
+    const int i = kMaxClusters - 1 - (int)(order[s] & (kMaxClusters - 1));
+    const int a = clampi(qo[i], 0, N), b = clampi(qo[i + 1], a, N);
+    const int nb = (b - a + bm - 1) / bm;
+    const int x = code >> 24, first = code & 0xffffff;
+    for (int r = 0; r < nb && first + r < max_items; ++r) out[(size_t)x * max_items + first + r] = i | (r << 12);
   }
 }
 
@@ -553,7 +596,7 @@ __global__ __launch_bounds__(256, 3) void k_attn_bf16(
       const i32x4_t Vr = head_rsrc(V + base, N, D);
 
       bf16x8_t qf[KS];
-    #pragma unroll
+#pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         u32x4_t v = {0u, 0u, 0u, 0u};
         if (row_ok) v = *reinterpret_cast<const u32x4_t*>(Q + base + (size_t)row * D + ks * 16 + half * 8);
@@ -562,7 +605,7 @@ __global__ __launch_bounds__(256, 3) void k_attn_bf16(
 
       // this lane's tile rows (one per direct-to-LDS load)
       int trow[INS];
-    #pragma unroll
+#pragma unroll
       for (int q = 0; q < INS; ++q) trow[q] = 8 * wave + RPI * q + lane / CPR;
 
       LdsCursor cur;
@@ -576,9 +619,9 @@ __global__ __launch_bounds__(256, 3) void k_attn_bf16(
       float m_ref = -__builtin_inff();
       float l_part = 0.f;                            // this lane's share of the row sum
       f32x16_t o[DT];
-    #pragma unroll
+#pragma unroll
       for (int dt = 0; dt < DT; ++dt)
-    #pragma unroll
+#pragma unroll
         for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
 
       // LDS byte addresses (slot 0) of the operand reads; the asm statements hide
@@ -590,7 +633,7 @@ __global__ __launch_bounds__(256, 3) void k_attn_bf16(
       //   the row only through row % 4, which the added rows keep
       const uint32_t lds0 = lds_addr(sT);
       uint32_t kaddr[KS];
-    #pragma unroll
+#pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         kaddr[ks] = lds0 + (uint32_t)(col * ROWB + TileGeom<D>::k_chunk(col, 2 * ks + half) * 16);
         asm volatile("" : "+v"(kaddr[ks]));
@@ -598,7 +641,7 @@ __global__ __launch_bounds__(256, 3) void k_attn_bf16(
       const int vr = (lane & 15) >> 2;
       const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
       uint32_t vaddr[DT];
-    #pragma unroll
+#pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const int r = 4 * half + vr, c0 = dt * 32 + vcol;
         vaddr[dt] = lds0 + (uint32_t)(BN * ROWB + r * ROWB + TileGeom<D>::v_chunk(r, c0 >> 3) * 16 + (c0 & 7) * 2);
@@ -608,7 +651,7 @@ __global__ __launch_bounds__(256, 3) void k_attn_bf16(
       // consecutive keys from a scalar first key), and the swizzled 16-byte slot
       // within the row (a tile assembled from several key ranges)
       uint32_t kl_off[INS], vl_off[INS], krun[INS], vrun[INS];
-    #pragma unroll
+#pragma unroll
       for (int q = 0; q < INS; ++q) {
         const int r = 8 * wave + RPI * q + lane / CPR;
         kl_off[q] = (uint32_t)TileGeom<D>::k_chunk(r, lane % CPR) * 16u;
@@ -622,13 +665,13 @@ __global__ __launch_bounds__(256, 3) void k_attn_bf16(
         const uint32_t kdst = lds0 + (uint32_t)(s * SLOT + 8 * wave * ROWB);
         if (first >= 0) {
           const uint32_t so = (uint32_t)__builtin_amdgcn_readfirstlane(first * ROWB);   // uniform by construction
-    #pragma unroll
+#pragma unroll
           for (int q = 0; q < INS; ++q) {
             lds_dma16(Kr, kdst + (uint32_t)(RPI * q * ROWB), krun[q], so);
             lds_dma16(Vr, kdst + (uint32_t)(BN * ROWB + RPI * q * ROWB), vrun[q], so);
           }
         } else {
-    #pragma unroll
+#pragma unroll
           for (int q = 0; q < INS; ++q) {
             const uint32_t ro = (uint32_t)max(key[q], 0) * ROWB;
             lds_dma16(Kr, kdst + (uint32_t)(RPI * q * ROWB), ro + kl_off[q], 0u);
@@ -655,14 +698,17 @@ __global__ __launch_bounds__(256, 3) void k_attn_bf16(
       // with its MFMA and waits on it.
       auto scores = [&](int s, f32x16_t& sc) __attribute__((always_inline)) {
         constexpr int kAhead = KS < 2 ? KS : 2;
-    #pragma unroll
+#pragma unroll
         for (int i = 0; i < 16; ++i) sc[i] = 0.f;
         bf16x8_t a[KS];
-    #pragma unroll
+#pragma unroll
         for (int ks = 0; ks < kAhead; ++ks) a[ks] = kread(s, ks);
+        // raised issue priority while the wave feeds the matrix core, so that
+        // the other waves' softmax work fills in around its MFMAs (lowered
+        // again after each MFMA run)
         __builtin_amdgcn_s_setprio(1);
         __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
-    #pragma unroll
+#pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           if (ks + kAhead < KS) a[ks + kAhead] = kread(s, ks + kAhead);
           sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qf[ks], sc, 0, 0, 0);
@@ -683,12 +729,12 @@ __global__ __launch_bounds__(256, 3) void k_attn_bf16(
           // key of score i: (i/4)*8 + 4*half + i%4; compared against the list end
           // shifted by this lane's half, so every compare takes an inline constant
           const int lim = filled - 4 * half;
-    #pragma unroll
+#pragma unroll
           for (int i = 0; i < 16; ++i)
             if ((i >> 2) * 8 + (i & 3) >= lim) sc[i] = -__builtin_inff();
         }
         float mx = sc[0];
-    #pragma unroll
+#pragma unroll
         for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
         {
           const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
@@ -697,15 +743,15 @@ __global__ __launch_bounds__(256, 3) void k_attn_bf16(
         if (mx > m_ref + kLazyTau) {
           const float alpha = __builtin_amdgcn_exp2f(m_ref - mx);
           l_part *= alpha;
-    #pragma unroll
+#pragma unroll
           for (int dt = 0; dt < DT; ++dt)
-    #pragma unroll
+#pragma unroll
             for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
           m_ref = mx;
         }
         const float neg = -m_ref;
         u32x4_t pw[2];
-    #pragma unroll
+#pragma unroll
         for (int i = 0; i < 16; i += 2) {
           const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[i], scale_log2, neg));
           const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[i + 1], scale_log2, neg));
@@ -716,11 +762,11 @@ __global__ __launch_bounds__(256, 3) void k_attn_bf16(
         constexpr int NV = 2 * DT;
         constexpr int kAhead = NV < 2 ? NV : 2;
         bf16x8_t va[NV];
-    #pragma unroll
+#pragma unroll
         for (int j = 0; j < kAhead; ++j) va[j] = vread(s, j);
         __builtin_amdgcn_s_setprio(1);
         __builtin_amdgcn_sched_group_barrier(0x100, 2 * kAhead, 0);
-    #pragma unroll
+#pragma unroll
         for (int j = 0; j < NV; ++j) {
           if (j + kAhead < NV) va[j + kAhead] = vread(s, j + kAhead);
           const int kk = j / DT, dt = j % DT;
@@ -743,7 +789,7 @@ __global__ __launch_bounds__(256, 3) void k_attn_bf16(
         f1 = cur.fill_rows<INS>(BN, trow, key, &first);
       } else {
         first = -1;
-    #pragma unroll
+#pragma unroll
         for (int q = 0; q < INS; ++q) key[q] = -1;
       }
       load_tile(1, first, key);
@@ -759,7 +805,7 @@ __global__ __launch_bounds__(256, 3) void k_attn_bf16(
           f2 = cur.fill_rows<INS>(BN, trow, key, &first);
         } else {
           first = -1;
-    #pragma unroll
+#pragma unroll
           for (int q = 0; q < INS; ++q) key[q] = -1;
         }
         load_tile((s + 2) % 3, first, key);
@@ -786,9 +832,9 @@ __global__ __launch_bounds__(256, 3) void k_attn_bf16(
       if (row_ok) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         uint16_t* orow = O + base + (size_t)row * D;
-    #pragma unroll
+#pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-    #pragma unroll
+#pragma unroll
           for (int g = 0; g < 4; ++g) {
             uint2 w;
             w.x = pack_bf16x2(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv);
