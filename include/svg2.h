@@ -199,6 +199,30 @@ int svg2_varblock_attn(const void* q, const void* k, const void* v, int32_t dtyp
                        hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * svg2_varblock_attn_unpermute - svg2_varblock_attn with the inverse
+ * permutation fused into its output stores  [Method, stages (2) and (4)]:
+ * the same values as svg2_varblock_attn into a buffer followed by
+ * svg2_unpermute of that buffer, without the pass over it.
+ *
+ *   Output row r of problem p (permuted order) goes to token t = perm[p, r]:
+ *   element e at dst + (p / heads) * dst_b_stride + (p % heads) *
+ *   dst_h_stride + t * dst_token_stride + e (strides in elements, multiples of
+ *   16 bytes; heads divides bh); lse, if not NULL, [bh, n_tokens] fp32 at
+ *   p * n_tokens + t.  perm is [bh, n_tokens] int32, a permutation of
+ *   0..n_tokens-1 (a row whose index is out of range is not written).
+ *   The other arguments and the workspace are those of svg2_varblock_attn.
+ * ---------------------------------------------------------------------- */
+int svg2_varblock_attn_unpermute(const void* q, const void* k, const void* v, int32_t dtype,
+                                 int32_t bh, int32_t n_tokens, int32_t head_dim,
+                                 const int32_t* q_offsets, int32_t n_q,
+                                 const int32_t* k_offsets, int32_t n_k,
+                                 const int32_t* sel_count, const int32_t* sel_idx, float scale,
+                                 const int32_t* perm, void* dst, int32_t heads,
+                                 int64_t dst_b_stride, int64_t dst_h_stride,
+                                 int64_t dst_token_stride, float* lse, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * svg2_unpermute - scatter rows back to the original token order:
  * dst row perm[i] = src row i  [Method, stage (2)].
  *

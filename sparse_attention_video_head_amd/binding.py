@@ -27,7 +27,7 @@ EXPORTED = [
     "svg2_kmeans_workspace_size", "svg2_kmeans",
     "svg2_permute_workspace_size", "svg2_permute",
     "svg2_select_topp_workspace_size", "svg2_select_topp",
-    "svg2_varblock_attn_workspace_size", "svg2_varblock_attn",
+    "svg2_varblock_attn_workspace_size", "svg2_varblock_attn", "svg2_varblock_attn_unpermute",
     "svg2_unpermute",
     "svg2_cluster_means_workspace_size", "svg2_cluster_means", "svg2_recall_mass",
     "svg2_quantize_fp8_workspace_size", "svg2_quantize_fp8", "svg2_varblock_attn_fp8",
@@ -75,6 +75,10 @@ def lib() -> ctypes.CDLL:
     L.svg2_varblock_attn.restype = ctypes.c_int
     L.svg2_varblock_attn.argtypes = [_c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_p, _c_int, _c_p,
                                      _c_int, _c_p, _c_p, ctypes.c_float, _c_p, _c_p, _c_p, _c_sz, _c_p]
+    L.svg2_varblock_attn_unpermute.restype = ctypes.c_int
+    L.svg2_varblock_attn_unpermute.argtypes = [_c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_p, _c_int,
+                                               _c_p, _c_int, _c_p, _c_p, ctypes.c_float, _c_p, _c_p, _c_int,
+                                               _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_sz, _c_p]
     L.svg2_unpermute.restype = ctypes.c_int
     L.svg2_unpermute.argtypes = [_c_p, _c_int, _c_int, _c_int, _c_int, _c_p, _c_p, _c_int, _c_i64, _c_i64,
                                  _c_i64, _c_p]
@@ -293,6 +297,54 @@ def varblock_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_offsets: 
                              _ptr(k_offsets), n_k, _ptr(sel_count), _ptr(sel_idx), ctypes.c_float(scale),
                              _ptr(out), _ptr(ls), _ptr(ws), ws_n, _stream(dev))
     _check(s, "svg2_varblock_attn")
+    return out, ls
+
+
+def varblock_attn_unpermute(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_offsets: torch.Tensor,
+                            k_offsets: torch.Tensor, sel_count: torch.Tensor, sel_idx: torch.Tensor,
+                            perm: torch.Tensor, scale: Optional[float] = None, lse=False,
+                            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """varblock_attn with the inverse permutation fused into its stores: out
+    row perm[i] = attention output row i (original token order).  ``out`` may be
+    a strided [bh,N,d] or [B,H,N,d] view (default: new contiguous tensor);
+    ``lse`` (flag or fp32 [bh, N] tensor) is in the original order too."""
+    _need_cuda(q, k, v, q_offsets, k_offsets, sel_count, sel_idx, perm, out)
+    for t in (q, k, v):
+        if t.dim() != 3 or not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype:
+            raise Svg2Error("q, k, v must be contiguous [bh, N, d] tensors of one dtype")
+    bh, N, d = q.shape
+    n_q = q_offsets.shape[1] - 1
+    n_k = k_offsets.shape[1] - 1
+    for t in (q_offsets, k_offsets, sel_count, sel_idx, perm):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise Svg2Error("offsets, lists and perm must be contiguous int32")
+    if tuple(sel_count.shape) != (bh, n_q) or tuple(sel_idx.shape) != (bh, n_q, n_k):
+        raise Svg2Error("sel_count [bh, n_q] and sel_idx [bh, n_q, n_k] expected")
+    if tuple(perm.shape) != (bh, N):
+        raise Svg2Error("perm must be [bh, N]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    obh, oN, od, heads, sb, sh, st = _strided_view(out)
+    if (obh, oN, od) != (bh, N, d) or out.dtype != q.dtype:
+        raise Svg2Error("out does not match q")
+    if isinstance(lse, torch.Tensor):
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (bh, N) or not lse.is_contiguous():
+            raise Svg2Error("lse must be a contiguous fp32 [bh, N] tensor")
+        _need_cuda(lse)
+        ls = lse
+    else:
+        ls = torch.empty(bh, N, dtype=torch.float32, device=dev) if lse else None
+    L = lib()
+    ws_n = L.svg2_varblock_attn_workspace_size(bh, N, n_q, n_k, d)
+    ws = _workspace(ws_n, dev, workspace)
+    s = L.svg2_varblock_attn_unpermute(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), bh, N, d, _ptr(q_offsets), n_q,
+                                       _ptr(k_offsets), n_k, _ptr(sel_count), _ptr(sel_idx), ctypes.c_float(scale),
+                                       _ptr(perm), _ptr(out), heads, sb, sh, st, _ptr(ls), _ptr(ws), ws_n,
+                                       _stream(dev))
+    _check(s, "svg2_varblock_attn_unpermute")
     return out, ls
 
 

@@ -281,7 +281,38 @@ int svg2_varblock_attn(const void* q, const void* k, const void* v, int32_t dtyp
   Carve c(workspace);
   const AttnWs ws = carve_attn(c, bh, n_tokens, n_q);
   return hip_status(launch_varblock_attn(q, k, v, dtype == SVG2_BF16, bh, n_tokens, head_dim, q_offsets, n_q,
-                                         k_offsets, n_k, sel_count, sel_idx, scale, out, lse, ws, stream));
+                                         k_offsets, n_k, sel_count, sel_idx, scale, out, lse,
+                                         contiguous_out(n_tokens, head_dim), ws, stream));
+}
+
+int svg2_varblock_attn_unpermute(const void* q, const void* k, const void* v, int32_t dtype, int32_t bh,
+                                 int32_t n_tokens, int32_t head_dim, const int32_t* q_offsets, int32_t n_q,
+                                 const int32_t* k_offsets, int32_t n_k, const int32_t* sel_count,
+                                 const int32_t* sel_idx, float scale, const int32_t* perm, void* dst,
+                                 int32_t heads, int64_t dst_b_stride, int64_t dst_h_stride,
+                                 int64_t dst_token_stride, float* lse, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  if (!dtype_ok(dtype)) return SVG2_ERR_INVALID_ARG;
+  if (bh < 1 || n_tokens < 1 || n_tokens > kMaxTokens) return SVG2_ERR_INVALID_ARG;
+  if (n_q < 1 || n_q > kMaxClusters || n_k < 1 || n_k > kMaxClusters) return SVG2_ERR_INVALID_ARG;
+  if (!dim_ok(head_dim)) return SVG2_ERR_UNSUPPORTED;
+  if (!(isfinite(scale) && scale > 0.f)) return SVG2_ERR_INVALID_ARG;
+  if (!q || !k || !v || !dst || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dst, 16))
+    return SVG2_ERR_INVALID_ARG;
+  if (!q_offsets || !k_offsets || !sel_count || !sel_idx || !perm || !aligned(q_offsets, 4) ||
+      !aligned(k_offsets, 4) || !aligned(sel_count, 4) || !aligned(sel_idx, 4) || !aligned(perm, 4) ||
+      (lse && !aligned(lse, 4)))
+    return SVG2_ERR_INVALID_ARG;
+  if (!strides_ok(heads, bh, dst_b_stride, dst_h_stride, dst_token_stride, esize(dtype)))
+    return SVG2_ERR_INVALID_ARG;
+  const size_t need = svg2_varblock_attn_workspace_size(bh, n_tokens, n_q, n_k, head_dim);
+  if (workspace_bytes < need || !workspace) return SVG2_ERR_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return SVG2_ERR_INVALID_ARG;
+  Carve c(workspace);
+  const AttnWs ws = carve_attn(c, bh, n_tokens, n_q);
+  const OutMap om{perm, heads, dst_b_stride, dst_h_stride, dst_token_stride};
+  return hip_status(launch_varblock_attn(q, k, v, dtype == SVG2_BF16, bh, n_tokens, head_dim, q_offsets, n_q,
+                                         k_offsets, n_k, sel_count, sel_idx, scale, dst, lse, om, ws, stream));
 }
 
 // ------------------------------------------------------------------ unpermute

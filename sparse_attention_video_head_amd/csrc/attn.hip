@@ -541,7 +541,7 @@ __global__ __launch_bounds__(256, 3) void k_attn_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     int N, const int32_t* __restrict__ q_off, int n_q, const int32_t* __restrict__ k_off, int n_k,
     const int32_t* __restrict__ sel_count, const int32_t* __restrict__ sel_idx, float scale_log2,
-    uint16_t* __restrict__ O, float* __restrict__ lse, const int32_t* __restrict__ flat,
+    uint16_t* __restrict__ O, float* __restrict__ lse, OutMap om, const int32_t* __restrict__ flat,
     int32_t* __restrict__ queue, size_t cap) {
   constexpr int BN = kAttnBN;
   constexpr int KS = D / 16;           // 16-wide k-steps of Q.K
@@ -829,9 +829,10 @@ __global__ __launch_bounds__(256, 3) void k_attn_bf16(
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part), __float_as_uint(l_part), false, false);
         l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
       }
-      if (row_ok) {
+      const int tout = row_ok ? (om.perm ? om.perm[(size_t)p * N + row] : row) : -1;
+      if (row_ok && (unsigned)tout < (unsigned)N) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        uint16_t* orow = O + base + (size_t)row * D;
+        uint16_t* orow = O + (p / om.heads) * om.bs + (p % om.heads) * om.hs + (int64_t)tout * om.ts;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -842,8 +843,8 @@ __global__ __launch_bounds__(256, 3) void k_attn_bf16(
             *reinterpret_cast<uint2*>(orow + dt * 32 + g * 8 + half * 4) = w;
           }
         if (lse && half == 0)
-          lse[(size_t)p * N + row] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * 0.69314718055994531f
-                                                : -__builtin_inff();
+          lse[(size_t)p * N + tout] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * 0.69314718055994531f
+                                                 : -__builtin_inff();
       }
     }  // items of queue x
   }  // queues
@@ -1136,7 +1137,7 @@ __global__ __launch_bounds__(128) void k_attn_f32(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V, int N,
     const int32_t* __restrict__ q_off, int n_q, const int32_t* __restrict__ k_off, int n_k,
     const int32_t* __restrict__ sel_count, const int32_t* __restrict__ sel_idx, float scale,
-    float* __restrict__ O, float* __restrict__ lse, const int32_t* __restrict__ item_count,
+    float* __restrict__ O, float* __restrict__ lse, OutMap om, const int32_t* __restrict__ item_count,
     const int32_t* __restrict__ items, int max_items) {
   constexpr int BN = 32;
   constexpr int H = D / 2;
@@ -1196,11 +1197,13 @@ __global__ __launch_bounds__(128) void k_attn_f32(
       m_run = m_new;
     }
   }
-  if (row_ok) {
+  const int trow = row_ok ? (om.perm ? om.perm[(size_t)p * N + row] : row) : -1;
+  if (row_ok && (unsigned)trow < (unsigned)N) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    float* orow = O + (p / om.heads) * om.bs + (p % om.heads) * om.hs + (int64_t)trow * om.ts;
 #pragma unroll
-    for (int e = 0; e < H; ++e) O[base + (size_t)row * D + hh * H + e] = o[e] * inv;
-    if (lse && hh == 0) lse[(size_t)p * N + row] = l_run > 0.f ? m_run + logf(l_run) : -__builtin_inff();
+    for (int e = 0; e < H; ++e) orow[hh * H + e] = o[e] * inv;
+    if (lse && hh == 0) lse[(size_t)p * N + trow] = l_run > 0.f ? m_run + logf(l_run) : -__builtin_inff();
   }
 }
 
@@ -1218,7 +1221,8 @@ static int attn_persistent_grid() {
 hipError_t launch_varblock_attn(const void* q, const void* k, const void* v, bool bf16, int bh,
                                 int N, int d, const int32_t* q_off, int n_q, const int32_t* k_off,
                                 int n_k, const int32_t* sel_count, const int32_t* sel_idx,
-                                float scale, void* out, float* lse, const AttnWs& ws, hipStream_t s) {
+                                float scale, void* out, float* lse, const OutMap& om, const AttnWs& ws,
+                                hipStream_t s) {
   const int bm = attn_block_rows(bf16);
   const int max_items = attn_max_items(N, n_q, bm);
   hipLaunchKernelGGL(k_attn_lengths, dim3((n_q + 3) / 4, bh), dim3(256), 0, s, k_off, n_k, N, sel_count,
@@ -1234,7 +1238,7 @@ hipError_t launch_varblock_attn(const void* q, const void* k, const void* v, boo
 #define SVG2_ATTN(D)                                                                                  \
   hipLaunchKernelGGL(k_attn_bf16<D>, grid_p, dim3(256), 0, s, static_cast<const uint16_t*>(q),        \
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), N, q_off, n_q, \
-                     k_off, n_k, sel_count, sel_idx, sl2, static_cast<uint16_t*>(out), lse, ws.flat,   \
+                     k_off, n_k, sel_count, sel_idx, sl2, static_cast<uint16_t*>(out), lse, om, ws.flat, \
                      ws.queue, cap)
     if (d == 128) SVG2_ATTN(128); else SVG2_ATTN(64);
 #undef SVG2_ATTN
@@ -1245,7 +1249,7 @@ hipError_t launch_varblock_attn(const void* q, const void* k, const void* v, boo
 #define SVG2_ATTN(D)                                                                                   \
   hipLaunchKernelGGL(k_attn_f32<D>, grid, dim3(128), 0, s, static_cast<const float*>(q),               \
                      static_cast<const float*>(k), static_cast<const float*>(v), N, q_off, n_q, k_off, \
-                     n_k, sel_count, sel_idx, scale, static_cast<float*>(out), lse, ws.item_count,    \
+                     n_k, sel_count, sel_idx, scale, static_cast<float*>(out), lse, om, ws.item_count, \
                      ws.items, max_items)
     if (d == 128) SVG2_ATTN(128); else SVG2_ATTN(64);
 #undef SVG2_ATTN

@@ -72,10 +72,21 @@ struct AttnWs {
   int32_t* queue;        // [2 kAttnXcds]
   int32_t* flat;         // [kAttnXcds, bh * attn_max_items(N, n_q, 128), 2]
 };
+// Where the attention writes output row r of problem p: row t = perm[p, r]
+// (r itself when perm is null) at element offset (p / heads) * bs +
+// (p % heads) * hs + t * ts; lse at p * N + t.  A row with t outside
+// [0, N) is not written.
+struct OutMap {
+  const int32_t* perm;
+  int heads;
+  int64_t bs, hs, ts;
+};
+inline OutMap contiguous_out(int N, int d) { return OutMap{nullptr, 1, (int64_t)N * d, 0, d}; }
 hipError_t launch_varblock_attn(const void* q, const void* k, const void* v, bool bf16, int bh,
                                 int N, int d, const int32_t* q_off, int n_q, const int32_t* k_off,
                                 int n_k, const int32_t* sel_count, const int32_t* sel_idx,
-                                float scale, void* out, float* lse, const AttnWs& ws, hipStream_t s);
+                                float scale, void* out, float* lse, const OutMap& om, const AttnWs& ws,
+                                hipStream_t s);
 
 // FP8 (E4M3) Q, K, V with per-problem scales, head_dim 128, bf16 output; the
 // same workspace as launch_varblock_attn (row block kAttnBM).

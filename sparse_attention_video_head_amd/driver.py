@@ -90,8 +90,7 @@ class DenoiseDriver:
         e.kmeans(q, k, iters, mode == "warm", seed_q, seed_k)
         e.permute(q, k, v)
         e.select(self.p_at(step))
-        e.attend()
-        return e.unpermute(out)
+        return e.attend_unpermute(out)
 
     def reset(self):
         """Forget every cached centroid (a new generation starts cold)."""

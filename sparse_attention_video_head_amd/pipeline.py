@@ -126,6 +126,17 @@ class SVG2Layer:
     def unpermute(self, out: Optional[torch.Tensor] = None):
         return B.unpermute(self.op, self.perm_q, out=self.out if out is None else out)
 
+    def attend_unpermute(self, out: Optional[torch.Tensor] = None):
+        """Attention with the inverse permutation fused into its stores (one
+        pass less over the output); FP8 attention keeps the separate pass."""
+        dst = self.out if out is None else out
+        if self.fp8:
+            self.attend()
+            return self.unpermute(dst)
+        B.varblock_attn_unpermute(self.qp, self.kp, self.vp, self.off_q, self.off_k, self.sel_count, self.sel_idx,
+                                  self.perm_q, scale=self.scale, out=dst, workspace=self.ws_attn)
+        return dst
+
     # ------------------------------------------------------------ layer
     def run(self, q, k, v, top_p: float, iters: int = 5, warm: bool = False, seed_q: int = 0,
             seed_k: int = 1, out: Optional[torch.Tensor] = None):
@@ -133,8 +144,7 @@ class SVG2Layer:
         self.kmeans(q, k, iters, warm, seed_q, seed_k)
         self.permute(q, k, v)
         self.select(top_p)
-        self.attend()
-        return self.unpermute(out)
+        return self.attend_unpermute(out)
 
     def dense(self, q, k, v, out: Optional[torch.Tensor] = None):
         """This library's own dense attention (one block, every key selected)."""

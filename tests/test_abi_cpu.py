@@ -129,6 +129,28 @@ def test_attn_validation(kw, code):
     assert _attn(**kw) == code
 
 
+def _attn_unperm(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=1, bh=2, N=1000, d=128, qo=FAKE, nq=8, ko=FAKE, nk=9, sc=FAKE,
+             si=FAKE, scale=0.088, perm=FAKE, out=FAKE, heads=1, sb=128000, sh=0, st=128, lse=None, ws=FAKE,
+             wsn=1 << 30)
+    a.update(kw)
+    return B.lib().svg2_varblock_attn_unpermute(
+        a["q"], a["k"], a["v"], a["dtype"], a["bh"], a["N"], a["d"], a["qo"], a["nq"], a["ko"], a["nk"], a["sc"],
+        a["si"], ctypes.c_float(a["scale"]), a["perm"], a["out"], a["heads"], a["sb"], a["sh"], a["st"], a["lse"],
+        a["ws"], a["wsn"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(perm=None), INVALID), (dict(perm=FAKE + 2), INVALID), (dict(out=None), INVALID),
+    (dict(heads=3), INVALID), (dict(st=130), INVALID), (dict(sb=-8), INVALID), (dict(dtype=2), INVALID),
+    (dict(N=1 << 25), INVALID), (dict(nk=5000), INVALID), (dict(scale=0.0), INVALID), (dict(d=96), UNSUPPORTED),
+    (dict(lse=FAKE + 2), INVALID), (dict(wsn=16), WORKSPACE),
+])
+def test_attn_unpermute_validation(kw, code):
+    """The fused call validates like the attention and unpermute calls, before any HIP call."""
+    assert _attn_unperm(**kw) == code
+
+
 def test_unpermute_validation():
     L = B.lib()
     assert L.svg2_unpermute(None, 1, 1, 10, 128, FAKE, FAKE, 1, 1280, 0, 128, None) == INVALID

@@ -194,6 +194,49 @@ def test_varblock_attn_vs_oracle(dt, d, N, n_q, n_k, top_p):
         assert np.all(gl[~fin] == -np.inf) and np.all(got[~fin] == 0)
 
 
+@pytest.mark.parametrize("dt,d,layout", [("bf16", 128, "contiguous"), ("bf16", 128, "bnhd"), ("f32", 64, "bnhd"),
+                                         ("bf16", 64, "contiguous")])
+def test_varblock_attn_unpermute_vs_oracle(dt, d, layout):
+    """The fused call writes row i of the attention to token perm[i] (and its
+    lse there): against the oracle's block attention scattered the same way,
+    and bit-identical to the attention followed by the separate un-permute."""
+    Bsz, H, N, n_q, n_k = 2, 2, 2100, 15, 40
+    bh = Bsz * H
+    q, k, v, qo, ko, cnt, idx, lists, qo_np, ko_np = _attn_case(dt, d, bh, N, n_q, n_k, 0.85, seed=404,
+                                                               empty_rows=True)
+    rng = np.random.default_rng(9)
+    perm_np = np.stack([rng.permutation(N) for _ in range(bh)]).astype(np.int32)
+    perm = torch.from_numpy(perm_np).to(DEV)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    if layout == "bnhd":
+        buf = torch.full((Bsz, N, H, d), 7.0, dtype=qd.dtype, device=DEV)
+        out, lse = B.varblock_attn_unpermute(qd, kd, vd, qo, ko, cnt, idx, perm, lse=True, out=buf.transpose(1, 2))
+        got_all = buf.transpose(1, 2).reshape(bh, N, d)
+    else:
+        out, lse = B.varblock_attn_unpermute(qd, kd, vd, qo, ko, cnt, idx, perm, lse=True)
+        got_all = out
+    sep, sep_lse = B.varblock_attn(qd, kd, vd, qo, ko, cnt, idx, lse=True)
+    back = B.unpermute(sep, perm)
+    torch.cuda.synchronize()
+    assert torch.equal(got_all.contiguous(), back)
+    tol = (2e-2, 1e-2) if dt == "bf16" else (1e-4, 1e-4)
+    s = 1 / math.sqrt(d)
+    for h in range(bh):
+        ref, ref_lse = oracle.block_attention(np64(q[h]), np64(k[h]), np64(v[h]), qo_np[h], ko_np[h], lists[h], s)
+        exp = np.empty_like(ref)
+        exp[perm_np[h]] = ref
+        exp_lse = np.empty_like(ref_lse)
+        exp_lse[perm_np[h]] = ref_lse
+        got = np64(got_all[h])
+        assert np.max(np.abs(got - exp)) <= tol[0]
+        assert rel_l2(got, exp) <= tol[1]
+        gl = lse[h].cpu().numpy().astype(np.float64)
+        fin = np.isfinite(exp_lse)
+        np.testing.assert_allclose(gl[fin], exp_lse[fin], rtol=0, atol=2.5e-3 if dt == "bf16" else 1e-4)
+        assert np.all(gl[~fin] == -np.inf)
+        np.testing.assert_array_equal(gl, sep_lse[h].cpu().numpy()[np.argsort(perm_np[h])])
+
+
 def test_varblock_attn_dense_equals_softmax_attention():
     """n_q = n_k = 1 with every key selected is plain softmax attention."""
     bh, N, d = 2, 1100, 128
