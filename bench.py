@@ -24,6 +24,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "sparse-attn effective TFLOP/s + layer latency at 118k tokens; k-means iters/s"
+# timed stages of one layer step (the permutation rides on the last Lloyd
+# round; the inverse permutation on the attention's stores, except for FP8)
+STAGES = ["kmeans_permute", "select", "attention", "unpermute"]
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz)
 PEAK_F32_TFLOPS = 157.3
 PEAK_FP8_TFLOPS = 5033.2       # MI355X dense fp8 MFMA
@@ -613,38 +616,36 @@ def main():
     def step(warm: bool, iters: int, ev=None):
         if ev:
             ev[0].record()
-        layer.kmeans(q, k, iters, warm, **seeds)
+        # k-means of Q and K; the last Lloyd round also writes Q', K', V'
+        layer.cluster(q, k, v, iters, warm, **seeds)
         if ev:
             ev[1].record()
-        layer.permute(q, k, v)
-        if ev:
-            ev[2].record()
         layer.select(top_p)
         if ev:
-            ev[3].record()
+            ev[2].record()
         if layer.fp8:
             layer.attend()
             if ev:
-                ev[4].record()
+                ev[3].record()
             layer.unpermute()
         else:
             # the inverse permutation is fused into the attention's stores
             layer.attend_unpermute()
             if ev:
-                ev[4].record()
+                ev[3].record()
         if ev:
-            ev[5].record()
+            ev[4].record()
 
     def timed(warm: bool, iters: int, steps: int):
-        evs = [[E() for _ in range(6)] for _ in range(steps)]
+        evs = [[E() for _ in range(5)] for _ in range(steps)]
         torch.cuda.synchronize()
         w0 = time.perf_counter()
         for i in range(steps):
             step(warm, iters, evs[i])
         torch.cuda.synchronize()
         wall = (time.perf_counter() - w0) * 1e3 / steps
-        st = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(5)] for i in range(steps)])
-        tot = np.array([evs[i][0].elapsed_time(evs[i][5]) for i in range(steps)])
+        st = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)] for i in range(steps)])
+        tot = np.array([evs[i][0].elapsed_time(evs[i][4]) for i in range(steps)])
         return st.mean(0), float(tot.mean()), wall
 
     for _ in range(args.warmup):
@@ -675,20 +676,35 @@ def main():
         torch.cuda.synchronize()
         km.append(a.elapsed_time(b))
     ms_per_iter = (km[1] - km[0]) / 4.0
-    seeding_ms = cold_stage[0] - cfg.iters * ms_per_iter
+    # a cold k-means alone (no rows moved): seeding, and what the moves in
+    # the last round add
+    a, b = E(), E()
+    torch.cuda.synchronize()
+    a.record()
+    layer.kmeans(q, k, cfg.iters, False, **seeds)
+    b.record()
+    torch.cuda.synchronize()
+    kmeans_cold_ms = a.elapsed_time(b)
+    seeding_ms = kmeans_cold_ms - cfg.iters * ms_per_iter
+    fused_move_ms = float(cold_stage[0]) - kmeans_cold_ms
+    # the stand-alone permutation (sort + row gather of Q, K and V)
+    def median_ms(fn, runs=3):
+        fn()
+        ts = []
+        for _ in range(runs):
+            a, b = E(), E()
+            torch.cuda.synchronize()
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    permute_ms = median_ms(lambda: layer.permute(q, k, v))
     # the stand-alone inverse permutation (the layer fuses it into the
     # attention's stores, where it costs no pass of its own)
-    layer.unpermute()
-    ut = []
-    for _ in range(3):
-        a, b = E(), E()
-        torch.cuda.synchronize()
-        a.record()
-        layer.unpermute()
-        b.record()
-        torch.cuda.synchronize()
-        ut.append(a.elapsed_time(b))
-    unpermute_ms = float(np.median(ut))
+    unpermute_ms = median_ms(layer.unpermute)
 
     dense_ms = rel_dense = None
     if not args.no_dense:
@@ -709,7 +725,7 @@ def main():
         log(f"dense attention {dense_ms:.2f} ms; sparse vs dense rel-L2 {rel_dense:.4f}")
 
     attn_flops = 4.0 * cfg.head_dim * cold_pairs
-    attn_ms = float(cold_stage[3])
+    attn_ms = float(cold_stage[2])
     attn_tflops = attn_flops / (attn_ms * 1e-3) / 1e12
     peak = PEAK_FP8_TFLOPS if args.fp8 else (PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS)
     value = attn_flops / (cold_ms * 1e-3) / 1e12
@@ -742,27 +758,28 @@ def main():
         "layer_ms_cold": round(cold_ms, 3),
         "layer_ms_warm": round(warm_ms, 3),
         "warm_iters": args.warm_iters,
-        "stage_ms_cold": dict(zip(["kmeans", "permute", "select", "attention", "unpermute"],
-                                  [round(float(x), 4) for x in cold_stage])),
-        "stage_ms_warm": dict(zip(["kmeans", "permute", "select", "attention", "unpermute"],
-                                  [round(float(x), 4) for x in warm_stage])),
+        "stage_ms_cold": dict(zip(STAGES, [round(float(x), 4) for x in cold_stage])),
+        "stage_ms_warm": dict(zip(STAGES, [round(float(x), 4) for x in warm_stage])),
         "attn_tflops": round(attn_tflops, 2),
-        "attn_tflops_warm": round(4.0 * cfg.head_dim * warm_pairs / (float(warm_stage[3]) * 1e-3) / 1e12, 2),
+        "attn_tflops_warm": round(4.0 * cfg.head_dim * warm_pairs / (float(warm_stage[2]) * 1e-3) / 1e12, 2),
         "pairs_cold": cold_pairs,
         "pairs_warm": warm_pairs,
         "kmeans_ms_per_iter": round(ms_per_iter, 4),
         "kmeans_iters_per_s": round(1e3 / ms_per_iter, 1) if ms_per_iter > 0 else None,
         "kmeanspp_seeding_ms": round(float(seeding_ms), 3),
+        "kmeans_cold_ms": round(kmeans_cold_ms, 3),
+        "permute_in_last_round_ms": round(fused_move_ms, 3),
         "dense_ms": round(dense_ms, 3) if dense_ms else None,
         "dense_tflops": round(dense_flops / (dense_ms * 1e-3) / 1e12, 2) if dense_ms else None,
         "speedup_vs_dense_cold": round(dense_ms / cold_ms, 3) if dense_ms else None,
         "speedup_vs_dense_warm": round(dense_ms / warm_ms, 3) if dense_ms else None,
         "lloyd_round_distance_tflops": round(lloyd_flops / (ms_per_iter * 1e-3) / 1e12, 2) if ms_per_iter > 0 else None,
-        "select_share_of_dense": round(float(cold_stage[2]) / dense_ms, 5) if dense_ms else None,
+        "select_share_of_dense": round(float(cold_stage[1]) / dense_ms, 5) if dense_ms else None,
         "rel_l2_sparse_vs_dense": round(rel_dense, 5) if rel_dense is not None else None,
         "padding_ratio_fixed128_blocks": round(pad_fixed128, 4),
         "padding_ratio_this_kernel": round(pad_own, 4),
-        "permute_gbps": round(permute_bytes / (cold_stage[1] * 1e-3) / 1e9, 1),
+        "permute_ms_standalone": round(permute_ms, 4),
+        "permute_gbps": round(permute_bytes / (permute_ms * 1e-3) / 1e9, 1),
         "unpermute_gbps": round(unpermute_bytes / (unpermute_ms * 1e-3) / 1e9, 1),
         "roofline": {"bound": "mfma",
                      "kernel": "k_attn_fp8" if args.fp8 else ("k_attn_bf16" if cfg.dtype == "bf16" else "k_attn_f32"),

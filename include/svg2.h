@@ -108,6 +108,31 @@ int svg2_kmeans(const void* x, int32_t dtype, int32_t bh, int32_t n_tokens,
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * svg2_kmeans_permute - svg2_kmeans followed by the permutation of its
+ * final labels (svg2_permute), in one call: the last Lloyd round's centroid
+ * update reads every row in cluster order anyway, and stores it there too
+ * [Method, stages (1) and (2)].
+ *
+ *   x, dtype ... seed_index   as for svg2_kmeans; n_iters must be >= 1.
+ *   y               [bh, n_tokens, head_dim] dtype, contiguous, or NULL: a
+ *                   second tensor permuted the same way (V beside K).
+ *   x_perm          out [bh, n_tokens, head_dim]: row i = row perm[i] of x.
+ *   y_perm          out, the same for y; NULL exactly when y is NULL.
+ *   perm, offsets   out [bh, n_tokens] / [bh, n_clusters + 1] int32, as
+ *                   svg2_permute gives them for the returned labels.
+ *   workspace       svg2_kmeans_workspace_size bytes.
+ * Outputs must not overlap the inputs or each other.  Every output equals,
+ * bit for bit, svg2_kmeans followed by svg2_permute of its labels.
+ * ---------------------------------------------------------------------- */
+int svg2_kmeans_permute(const void* x, const void* y, int32_t dtype, int32_t bh,
+                        int32_t n_tokens, int32_t head_dim, int32_t n_clusters,
+                        int32_t n_iters, const float* init_centroids, uint64_t seed,
+                        float* centroids, int32_t* labels, int32_t* counts,
+                        float* min_dist, int32_t* seed_index, void* x_perm,
+                        void* y_perm, int32_t* perm, int32_t* offsets,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * svg2_permute - build the permutation of each problem from its cluster
  * labels and gather rows into contiguous cluster blocks; with n_tensors = 2
  * the same permutation is applied to both (K and V)  [Method, stage (2)].

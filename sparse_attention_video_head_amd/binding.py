@@ -24,7 +24,7 @@ _c_int, _c_i64, _c_u64, _c_sz, _c_p = ctypes.c_int32, ctypes.c_int64, ctypes.c_u
 
 EXPORTED = [
     "svg2_version", "svg2_status_string", "svg2_last_hip_error",
-    "svg2_kmeans_workspace_size", "svg2_kmeans",
+    "svg2_kmeans_workspace_size", "svg2_kmeans", "svg2_kmeans_permute",
     "svg2_permute_workspace_size", "svg2_permute",
     "svg2_select_topp_workspace_size", "svg2_select_topp",
     "svg2_varblock_attn_workspace_size", "svg2_varblock_attn", "svg2_varblock_attn_unpermute",
@@ -60,6 +60,9 @@ def lib() -> ctypes.CDLL:
     L.svg2_kmeans.restype = ctypes.c_int
     L.svg2_kmeans.argtypes = [_c_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_p, _c_u64,
                               _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]
+    L.svg2_kmeans_permute.restype = ctypes.c_int
+    L.svg2_kmeans_permute.argtypes = [_c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_p, _c_u64,
+                                      _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]
     L.svg2_permute_workspace_size.restype = _c_sz
     L.svg2_permute_workspace_size.argtypes = [_c_int] * 3
     L.svg2_permute.restype = ctypes.c_int
@@ -172,6 +175,49 @@ def kmeans(x: torch.Tensor, n_clusters: int, n_iters: int, init: Optional[torch.
                        _ptr(counts), _ptr(md), _ptr(si), _ptr(ws), ws_n, _stream(dev))
     _check(st, "svg2_kmeans")
     return dict(centroids=centroids, labels=labels, counts=counts, min_dist=md, seed_index=si)
+
+
+def kmeans_permute(x: torch.Tensor, n_clusters: int, n_iters: int, y: Optional[torch.Tensor] = None,
+                   init: Optional[torch.Tensor] = None, seed: int = 0, centroids: Optional[torch.Tensor] = None,
+                   labels: Optional[torch.Tensor] = None, counts: Optional[torch.Tensor] = None,
+                   x_out: Optional[torch.Tensor] = None, y_out: Optional[torch.Tensor] = None,
+                   perm: Optional[torch.Tensor] = None, offsets: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None):
+    """k-means of x [bh, N, d] (n_iters >= 1) with the rows of x, and of y when
+    given, gathered into the final clusters' order in the last round.  Returns
+    dict(centroids, labels, counts, x_perm, y_perm, perm, offsets)."""
+    _need_cuda(x, y, init)
+    if x.dim() != 3 or not x.is_contiguous():
+        raise Svg2Error("x must be a contiguous [bh, N, d] tensor")
+    bh, N, d = x.shape
+    dev = x.device
+    if y is not None and (y.shape != x.shape or y.dtype != x.dtype or not y.is_contiguous()):
+        raise Svg2Error("y must be a contiguous tensor of x's shape and dtype")
+    if init is not None and (init.dtype != torch.float32 or not init.is_contiguous()
+                             or tuple(init.shape) != (bh, n_clusters, d)):
+        raise Svg2Error("init must be a contiguous fp32 [bh, n_clusters, d] tensor")
+    e = lambda *sh, dt=torch.int32: torch.empty(*sh, dtype=dt, device=dev)
+    centroids = e(bh, n_clusters, d, dt=torch.float32) if centroids is None else centroids
+    labels = e(bh, N) if labels is None else labels
+    counts = e(bh, n_clusters) if counts is None else counts
+    x_out = torch.empty_like(x) if x_out is None else x_out
+    if y is not None and y_out is None:
+        y_out = torch.empty_like(y)
+    for o in (x_out, y_out):
+        if o is not None and (o.shape != x.shape or o.dtype != x.dtype or not o.is_contiguous()):
+            raise Svg2Error("permuted outputs must be contiguous tensors of x's shape and dtype")
+    perm = e(bh, N) if perm is None else perm
+    offsets = e(bh, n_clusters + 1) if offsets is None else offsets
+    L = lib()
+    ws_n = L.svg2_kmeans_workspace_size(bh, N, d, n_clusters)
+    ws = _workspace(ws_n, dev, workspace)
+    st = L.svg2_kmeans_permute(_ptr(x), _ptr(y), _dtype_code(x), bh, N, d, n_clusters, n_iters, _ptr(init),
+                               ctypes.c_uint64(seed & ((1 << 64) - 1)), _ptr(centroids), _ptr(labels),
+                               _ptr(counts), None, None, _ptr(x_out), _ptr(y_out), _ptr(perm), _ptr(offsets),
+                               _ptr(ws), ws_n, _stream(dev))
+    _check(st, "svg2_kmeans_permute")
+    return dict(centroids=centroids, labels=labels, counts=counts, x_perm=x_out, y_perm=y_out, perm=perm,
+                offsets=offsets)
 
 
 # ---------------------------------------------------------------- permute

@@ -103,37 +103,13 @@ AttnWs carve_attn(Carve& c, int bh, int N, int n_q) {
   return w;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* svg2_version(void) { return "svg2-mi355x 0.1.0 (gfx950)"; }
-
-const char* svg2_status_string(int status) {
-  switch (status) {
-    case SVG2_OK: return "ok";
-    case SVG2_ERR_INVALID_ARG: return "invalid argument";
-    case SVG2_ERR_UNSUPPORTED: return "unsupported shape or dtype";
-    case SVG2_ERR_WORKSPACE: return "workspace too small";
-    case SVG2_ERR_HIP: return "HIP error";
-    default: return "unknown status";
-  }
-}
-
-int svg2_last_hip_error(void) { return g_last_hip_error; }
-
-// ------------------------------------------------------------------ kmeans
-size_t svg2_kmeans_workspace_size(int32_t bh, int32_t n_tokens, int32_t head_dim, int32_t n_clusters) {
-  if (!shape_ok(bh, n_tokens, n_clusters) || !dim_ok(head_dim)) return 0;
-  Carve c(nullptr);
-  carve_kmeans(c, bh, n_tokens, head_dim, n_clusters);
-  return c.off;
-}
-
-int svg2_kmeans(const void* x, int32_t dtype, int32_t bh, int32_t n_tokens, int32_t head_dim,
-                int32_t n_clusters, int32_t n_iters, const float* init_centroids, uint64_t seed,
-                float* centroids, int32_t* labels, int32_t* counts, float* min_dist,
-                int32_t* seed_index, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// svg2_kmeans, and with x_sorted set, svg2_kmeans_permute: the last round's
+// sort writes perm / offsets and its centroid update also moves the rows.
+int kmeans_run(const void* x, int32_t dtype, int32_t bh, int32_t n_tokens, int32_t head_dim,
+               int32_t n_clusters, int32_t n_iters, const float* init_centroids, uint64_t seed,
+               float* centroids, int32_t* labels, int32_t* counts, float* min_dist, int32_t* seed_index,
+               void* x_sorted, const void* y, void* y_sorted, int32_t* perm_out, int32_t* offsets_out,
+               void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!dtype_ok(dtype)) return SVG2_ERR_INVALID_ARG;
   if (!shape_ok(bh, n_tokens, n_clusters)) return SVG2_ERR_INVALID_ARG;
   if (!dim_ok(head_dim)) return SVG2_ERR_UNSUPPORTED;
@@ -170,12 +146,70 @@ int svg2_kmeans(const void* x, int32_t dtype, int32_t bh, int32_t n_tokens, int3
     st = hip_status(launch_assign(x, bf16, bh, N, d, n, centroids, w.c_hi, w.c_lo, w.c_norm, labels,
                                   it == n_iters - 1 ? min_dist : nullptr, stream));
     if (st) return st;
-    st = hip_status(launch_counting_sort(labels, bh, N, n, w.hist, w.perm, w.offsets, counts, stream));
+    const bool last = it == n_iters - 1 && x_sorted;
+    int32_t* pm = last ? perm_out : w.perm;
+    int32_t* of = last ? offsets_out : w.offsets;
+    st = hip_status(launch_counting_sort(labels, bh, N, n, w.hist, pm, of, counts, stream));
     if (st) return st;
-    st = hip_status(launch_centroid_mean(x, bf16, bh, N, d, n, w.perm, w.offsets, w.partial, centroids, stream));
+    st = hip_status(launch_centroid_mean(x, bf16, bh, N, d, n, pm, of, w.partial, centroids, stream,
+                                         last ? x_sorted : nullptr, last ? y : nullptr,
+                                         last ? y_sorted : nullptr));
     if (st) return st;
   }
   return SVG2_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* svg2_version(void) { return "svg2-mi355x 0.1.0 (gfx950)"; }
+
+const char* svg2_status_string(int status) {
+  switch (status) {
+    case SVG2_OK: return "ok";
+    case SVG2_ERR_INVALID_ARG: return "invalid argument";
+    case SVG2_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case SVG2_ERR_WORKSPACE: return "workspace too small";
+    case SVG2_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+int svg2_last_hip_error(void) { return g_last_hip_error; }
+
+// ------------------------------------------------------------------ kmeans
+size_t svg2_kmeans_workspace_size(int32_t bh, int32_t n_tokens, int32_t head_dim, int32_t n_clusters) {
+  if (!shape_ok(bh, n_tokens, n_clusters) || !dim_ok(head_dim)) return 0;
+  Carve c(nullptr);
+  carve_kmeans(c, bh, n_tokens, head_dim, n_clusters);
+  return c.off;
+}
+
+int svg2_kmeans(const void* x, int32_t dtype, int32_t bh, int32_t n_tokens, int32_t head_dim,
+                int32_t n_clusters, int32_t n_iters, const float* init_centroids, uint64_t seed,
+                float* centroids, int32_t* labels, int32_t* counts, float* min_dist,
+                int32_t* seed_index, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return kmeans_run(x, dtype, bh, n_tokens, head_dim, n_clusters, n_iters, init_centroids, seed, centroids,
+                    labels, counts, min_dist, seed_index, nullptr, nullptr, nullptr, nullptr, nullptr, workspace,
+                    workspace_bytes, stream);
+}
+
+int svg2_kmeans_permute(const void* x, const void* y, int32_t dtype, int32_t bh, int32_t n_tokens,
+                        int32_t head_dim, int32_t n_clusters, int32_t n_iters, const float* init_centroids,
+                        uint64_t seed, float* centroids, int32_t* labels, int32_t* counts, float* min_dist,
+                        int32_t* seed_index, void* x_perm, void* y_perm, int32_t* perm, int32_t* offsets,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (n_iters < 1) return SVG2_ERR_INVALID_ARG;
+  if (!x_perm || !aligned(x_perm, 16) || !perm || !aligned(perm, 4) || !offsets || !aligned(offsets, 4))
+    return SVG2_ERR_INVALID_ARG;
+  if ((y == nullptr) != (y_perm == nullptr)) return SVG2_ERR_INVALID_ARG;
+  if (y && (!aligned(y, 16) || !aligned(y_perm, 16))) return SVG2_ERR_INVALID_ARG;
+  if (x_perm == x || (y && (y_perm == y || y_perm == x || x_perm == y || y_perm == x_perm)))
+    return SVG2_ERR_INVALID_ARG;
+  return kmeans_run(x, dtype, bh, n_tokens, head_dim, n_clusters, n_iters, init_centroids, seed, centroids,
+                    labels, counts, min_dist, seed_index, x_perm, y, y_perm, perm, offsets, workspace,
+                    workspace_bytes, stream);
 }
 
 // ------------------------------------------------------------------ permute

@@ -45,9 +45,12 @@ hipError_t launch_assign(const void* x, bool bf16, int bh, int N, int d, int n, 
 // partial_ws: bh * (n + mean_chunks(N)) * d doubles.
 constexpr int kMeanChunk = 512;              // sorted positions per partial-sum work-group
 inline int mean_chunks(int n_tokens) { return (n_tokens + kMeanChunk - 1) / kMeanChunk; }
+// x_sorted (with y / y_sorted optional): also store row perm[r] of x (of y)
+// to row r, in the same pass.
 hipError_t launch_centroid_mean(const void* x, bool bf16, int bh, int N, int d, int n,
                                 const int32_t* perm, const int32_t* offsets, double* partial_ws, float* c,
-                                hipStream_t s);
+                                hipStream_t s, void* x_sorted = nullptr, const void* y = nullptr,
+                                void* y_sorted = nullptr);
 
 // --------------------------------------------------------------- select.hip
 hipError_t launch_select_topp(const float* cq, const int32_t* q_counts, int n_q, const float* ck,

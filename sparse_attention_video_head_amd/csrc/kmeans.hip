@@ -785,11 +785,15 @@ hipError_t launch_assign(const void* x, bool bf16, int bh, int N, int d, int n, 
 // every cluster is a contiguous, increasing range of the sorted order).  A
 // second kernel adds each cluster's partials in chunk order.  Every sum runs
 // in a fixed order, so the result is the same run to run.
-template <typename T, int D>
+// MOVE: the rows read at sorted position r are also stored to row r of Xo
+// (and, when Y is given, row perm[r] of Y to row r of Yo): the permutation
+// into cluster blocks rides on the reads the update makes anyway.
+template <typename T, int D, bool MOVE>
 __global__ __launch_bounds__(256) void k_centroid_partial(const T* __restrict__ X, int N, int n,
                                                           const int32_t* __restrict__ perm,
                                                           const int32_t* __restrict__ offsets,
-                                                          double* __restrict__ partial) {
+                                                          double* __restrict__ partial, T* __restrict__ Xo,
+                                                          const T* __restrict__ Y, T* __restrict__ Yo) {
   constexpr int EPV = 16 / sizeof(T);          // elements per 16-byte vector
   constexpr int VPR = D / EPV;                 // lanes per row
   constexpr int G = 256 / VPR;                 // row groups
@@ -815,6 +819,9 @@ __global__ __launch_bounds__(256) void k_centroid_partial(const T* __restrict__ 
   __syncthreads();
   const int cv = threadIdx.x % VPR, g = threadIdx.x / VPR;
   const T* Xp = X + (size_t)p * N * D + cv * EPV;
+  T* Xq = MOVE ? Xo + (size_t)p * N * D + cv * EPV : nullptr;
+  const T* Yp = MOVE && Y ? Y + (size_t)p * N * D + cv * EPV : nullptr;
+  T* Yq = MOVE && Y ? Yo + (size_t)p * N * D + cv * EPV : nullptr;
   double* part = partial + (size_t)p * (n + chunks) * D;
   int c = s_c0, pos = j0;
   while (pos < j1 && c < n) {
@@ -823,11 +830,25 @@ __global__ __launch_bounds__(256) void k_centroid_partial(const T* __restrict__ 
 #pragma unroll
     for (int e = 0; e < EPV; ++e) acc[e] = 0.0;
     for (int i = pos + g; i < end; i += G * U) {
-      u32x4_t v[U];
+      u32x4_t v[U], w[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int r = i + u * G;
-        if (r < end) v[u] = *reinterpret_cast<const u32x4_t*>(Xp + (size_t)s_perm[r - j0] * D);
+        if (r < end) {
+          const size_t src = (size_t)s_perm[r - j0] * D;
+          v[u] = *reinterpret_cast<const u32x4_t*>(Xp + src);
+          if (MOVE && Yp) w[u] = *reinterpret_cast<const u32x4_t*>(Yp + src);
+        }
+      }
+      if constexpr (MOVE) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int r = i + u * G;
+          if (r < end) {
+            *reinterpret_cast<u32x4_t*>(Xq + (size_t)r * D) = v[u];
+            if (Yp) *reinterpret_cast<u32x4_t*>(Yq + (size_t)r * D) = w[u];
+          }
+        }
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -878,12 +899,18 @@ __global__ __launch_bounds__(D) void k_centroid_finish(int n, int chunks, const 
 
 hipError_t launch_centroid_mean(const void* x, bool bf16, int bh, int N, int d, int n,
                                 const int32_t* perm, const int32_t* offsets, double* partial_ws, float* c,
-                                hipStream_t s) {
+                                hipStream_t s, void* x_sorted, const void* y, void* y_sorted) {
   const int chunks = mean_chunks(N);
   const dim3 grid(chunks, bh);
-#define SVG2_MEAN(T, D)                                                                               \
-  hipLaunchKernelGGL((k_centroid_partial<T, D>), grid, dim3(256), 0, s, static_cast<const T*>(x), N, n, \
-                     perm, offsets, partial_ws);                                                      \
+#define SVG2_MEAN(T, D)                                                                                   \
+  if (x_sorted)                                                                                           \
+    hipLaunchKernelGGL((k_centroid_partial<T, D, true>), grid, dim3(256), 0, s, static_cast<const T*>(x), \
+                       N, n, perm, offsets, partial_ws, static_cast<T*>(x_sorted),                        \
+                       static_cast<const T*>(y), static_cast<T*>(y_sorted));                              \
+  else                                                                                                    \
+    hipLaunchKernelGGL((k_centroid_partial<T, D, false>), grid, dim3(256), 0, s,                          \
+                       static_cast<const T*>(x), N, n, perm, offsets, partial_ws, nullptr, nullptr,       \
+                       nullptr);                                                                          \
   hipLaunchKernelGGL((k_centroid_finish<D>), dim3(n, bh), dim3(D), 0, s, n, chunks, offsets, partial_ws, c)
   if (bf16) {
     if (d == 128) { SVG2_MEAN(uint16_t, 128); } else { SVG2_MEAN(uint16_t, 64); }

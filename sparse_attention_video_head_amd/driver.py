@@ -87,8 +87,7 @@ class DenoiseDriver:
         e.cq, e.ck = self.cache[layer]
         seed_q, seed_k = self.seeds(layer)
         iters = self.cold_iters if mode == "cold" else self.warm_iters
-        e.kmeans(q, k, iters, mode == "warm", seed_q, seed_k)
-        e.permute(q, k, v)
+        e.cluster(q, k, v, iters, mode == "warm", seed_q, seed_k)
         e.select(self.p_at(step))
         return e.attend_unpermute(out)
 

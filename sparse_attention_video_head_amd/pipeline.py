@@ -2,6 +2,7 @@
 ("Sparse VideoGen2" wiki summary, Method, stages (1)-(4)):
 
     k-means(Q), k-means(K)  ->  permute Q by P_Q, K and V by P_K
+    (the permutation rides on the last Lloyd round's centroid update)
     ->  centroid scores + top-p  ->  variable-block attention  ->  un-permute
 
 Buffers (outputs and workspaces) are allocated once per shape, so repeated
@@ -106,6 +107,35 @@ class SVG2Layer:
         side_k()
         main.wait_stream(self.side)
 
+    def cluster(self, q, k, v, iters: int, warm: bool, seed_q: int, seed_k: int):
+        """k-means of Q and K with the permutation fused into the last Lloyd
+        round: Q' from Q's clusters, K' and V' from K's."""
+        if iters < 1:
+            self.kmeans(q, k, iters, warm, seed_q, seed_k)
+            self.permute(q, k, v)
+            return
+
+        def side_q():
+            B.kmeans_permute(q, self.n_q, iters, init=self.cq if warm else None, seed=seed_q, centroids=self.cq,
+                             labels=self.labels_q, counts=self.counts_q, x_out=self.qp, perm=self.perm_q,
+                             offsets=self.off_q, workspace=self.ws_kq)
+
+        def side_k():
+            B.kmeans_permute(k, self.n_k, iters, y=v, init=self.ck if warm else None, seed=seed_k,
+                             centroids=self.ck, labels=self.labels_k, counts=self.counts_k, x_out=self.kp,
+                             y_out=self.vp, perm=self.perm_k, offsets=self.off_k, workspace=self.ws_kk)
+
+        if self.side is None:
+            side_q()
+            side_k()
+            return
+        main = torch.cuda.current_stream(self.dev)
+        self.side.wait_stream(main)
+        with torch.cuda.stream(self.side):
+            side_k()
+        side_q()
+        main.wait_stream(self.side)
+
     def select(self, top_p: float):
         B.select_topp(self.cq, self.counts_q, self.ck, self.counts_k, top_p, scale=self.scale,
                       sel_count=self.sel_count, sel_idx=self.sel_idx, pair_count=self.pairs,
@@ -141,8 +171,7 @@ class SVG2Layer:
     def run(self, q, k, v, top_p: float, iters: int = 5, warm: bool = False, seed_q: int = 0,
             seed_k: int = 1, out: Optional[torch.Tensor] = None):
         """Whole layer; returns the output in the original token order."""
-        self.kmeans(q, k, iters, warm, seed_q, seed_k)
-        self.permute(q, k, v)
+        self.cluster(q, k, v, iters, warm, seed_q, seed_k)
         self.select(top_p)
         return self.attend_unpermute(out)
 

@@ -151,6 +151,29 @@ def test_attn_unpermute_validation(kw, code):
     assert _attn_unperm(**kw) == code
 
 
+def _kmeans_perm(**kw):
+    a = dict(x=FAKE, y=FAKE + 4096, dtype=1, bh=2, N=1000, d=128, n=8, it=3, init=None, cent=FAKE + 8192,
+             lab=FAKE + 12288, cnt=FAKE + 16384, xp=FAKE + 20480, yp=FAKE + 24576, perm=FAKE + 28672,
+             off=FAKE + 32768, ws=FAKE + 36864, wsn=1 << 30)
+    a.update(kw)
+    return B.lib().svg2_kmeans_permute(
+        a["x"], a["y"], a["dtype"], a["bh"], a["N"], a["d"], a["n"], a["it"], a["init"], ctypes.c_uint64(7),
+        a["cent"], a["lab"], a["cnt"], None, None, a["xp"], a["yp"], a["perm"], a["off"], a["ws"], a["wsn"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(it=0), INVALID), (dict(xp=None), INVALID), (dict(xp=FAKE + 20482), INVALID), (dict(perm=None), INVALID),
+    (dict(off=None), INVALID), (dict(y=None), INVALID), (dict(yp=None), INVALID), (dict(yp=FAKE + 24578), INVALID),
+    (dict(xp=FAKE), INVALID), (dict(yp=FAKE + 4096), INVALID), (dict(yp=FAKE + 20480), INVALID),
+    (dict(lab=None), INVALID), (dict(dtype=2), INVALID), (dict(d=96), UNSUPPORTED), (dict(n=1001), INVALID),
+    (dict(it=101), INVALID), (dict(wsn=16), WORKSPACE),
+])
+def test_kmeans_permute_validation(kw, code):
+    """The fused k-means + permutation validates every argument before any HIP call:
+    n_iters >= 1, outputs present, aligned and not aliasing the inputs, y and y_perm given together."""
+    assert _kmeans_perm(**kw) == code
+
+
 def test_unpermute_validation():
     L = B.lib()
     assert L.svg2_unpermute(None, 1, 1, 10, 128, FAKE, FAKE, 1, 1280, 0, 128, None) == INVALID

@@ -303,6 +303,42 @@ def test_kmeans_chained_rounds_equal_one_call():
     assert torch.equal(one["counts"], step["counts"])
 
 
+@pytest.mark.parametrize("dt,d,N,n,iters,warm,with_y", [
+    ("bf16", 128, 5000, 40, 3, False, True), ("bf16", 128, 3001, 37, 1, True, True),
+    ("bf16", 64, 2000, 17, 2, False, False), ("f32", 64, 4097, 64, 2, True, True),
+    ("bf16", 128, 700, 700, 1, False, True), ("bf16", 128, 1000, 1, 2, True, False),
+])
+def test_kmeans_permute_equals_kmeans_then_permute(dt, d, N, n, iters, warm, with_y):
+    """The permutation fused into the last Lloyd round gives, bit for bit, what
+    k-means followed by the stand-alone permutation gives; perm / offsets are the
+    oracle's counting sort of the returned labels and the rows follow them."""
+    bh = 3
+    q, k, v = mixture(bh, N, d, comps=max(2, n // 2), seed=N + n, dtype=dtype_of(dt))
+    xd, yd = k.to(DEV), v.to(DEV)
+    init = B.kmeans(xd, n, 0, seed=5)["centroids"].clone() if warm else None
+    ref = B.kmeans(xd, n, iters, init=init, seed=3)
+    (rx, *ry), rperm, roff = B.permute(ref["labels"], n, xd, *([yd] if with_y else []))
+    got = B.kmeans_permute(xd, n, iters, y=yd if with_y else None, init=init, seed=3)
+    torch.cuda.synchronize()
+    for key in ("centroids", "labels", "counts"):
+        assert torch.equal(got[key], ref[key]), key
+    assert torch.equal(got["perm"], rperm) and torch.equal(got["offsets"], roff)
+    assert torch.equal(got["x_perm"], rx)
+    if with_y:
+        assert torch.equal(got["y_perm"], ry[0])
+    else:
+        assert got["y_perm"] is None
+    lab = got["labels"].cpu().numpy()
+    for h in range(bh):
+        p_ref, o_ref, _ = oracle.counting_sort(lab[h], n)
+        np.testing.assert_array_equal(got["perm"][h].cpu().numpy(), p_ref)
+        np.testing.assert_array_equal(got["offsets"][h].cpu().numpy(), o_ref)
+        idx = torch.from_numpy(p_ref)
+        assert torch.equal(got["x_perm"][h].cpu(), k[h][idx])
+        if with_y:
+            assert torch.equal(got["y_perm"][h].cpu(), v[h][idx])
+
+
 @pytest.mark.parametrize("dt,d,N,n,heads", [("f32", 64, 4096, 64, 1), ("bf16", 128, 16384, 250, 2),
                                            ("bf16", 128, 3000, 100, 2), ("bf16", 64, 700, 700, 1)])
 def test_kmeanspp_picks_match_oracle(dt, d, N, n, heads):
