@@ -25,8 +25,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "sparse-attn effective TFLOP/s + layer latency at 118k tokens; k-means iters/s"
 # timed stages of one layer step (the permutation rides on the last Lloyd
-# round; the inverse permutation on the attention's stores, except for FP8)
-STAGES = ["kmeans_permute", "select", "attention", "unpermute"]
+# round, the inverse permutation on the attention's stores)
+STAGES = ["kmeans_permute", "select", "attention"]
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz)
 PEAK_F32_TFLOPS = 157.3
 PEAK_FP8_TFLOPS = 5033.2       # MI355X dense fp8 MFMA
@@ -623,29 +623,22 @@ def main():
         layer.select(top_p)
         if ev:
             ev[2].record()
-        if layer.fp8:
-            layer.attend()
-            if ev:
-                ev[3].record()
-            layer.unpermute()
-        else:
-            # the inverse permutation is fused into the attention's stores
-            layer.attend_unpermute()
-            if ev:
-                ev[3].record()
+        # the inverse permutation is fused into the attention's stores (FP8:
+        # the quantization of Q', K', V' runs first, inside this stage)
+        layer.attend_unpermute()
         if ev:
-            ev[4].record()
+            ev[3].record()
 
     def timed(warm: bool, iters: int, steps: int):
-        evs = [[E() for _ in range(5)] for _ in range(steps)]
+        evs = [[E() for _ in range(4)] for _ in range(steps)]
         torch.cuda.synchronize()
         w0 = time.perf_counter()
         for i in range(steps):
             step(warm, iters, evs[i])
         torch.cuda.synchronize()
         wall = (time.perf_counter() - w0) * 1e3 / steps
-        st = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)] for i in range(steps)])
-        tot = np.array([evs[i][0].elapsed_time(evs[i][4]) for i in range(steps)])
+        st = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(3)] for i in range(steps)])
+        tot = np.array([evs[i][0].elapsed_time(evs[i][3]) for i in range(steps)])
         return st.mean(0), float(tot.mean()), wall
 
     for _ in range(args.warmup):

@@ -297,6 +297,23 @@ int svg2_varblock_attn_fp8(const void* q8, const void* k8, const void* v8, const
                            const int32_t* sel_idx, float scale, void* out, float* lse, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
 
+/* svg2_varblock_attn_fp8_unpermute - svg2_varblock_attn_fp8 with the inverse
+ * permutation fused into its output stores [Method, stages (2) and (4)]: the
+ * same values as svg2_varblock_attn_fp8 followed by svg2_unpermute (bf16).
+ * perm, dst, heads, the strides and lse as for svg2_varblock_attn_unpermute;
+ * the other arguments as for svg2_varblock_attn_fp8. */
+int svg2_varblock_attn_fp8_unpermute(const void* q8, const void* k8, const void* v8,
+                                     const float* q_scale, const float* k_scale,
+                                     const float* v_scale, int32_t bh, int32_t n_tokens,
+                                     int32_t head_dim, const int32_t* q_offsets, int32_t n_q,
+                                     const int32_t* k_offsets, int32_t n_k,
+                                     const int32_t* sel_count, const int32_t* sel_idx,
+                                     float scale, const int32_t* perm, void* dst,
+                                     int32_t heads, int64_t dst_b_stride,
+                                     int64_t dst_h_stride, int64_t dst_token_stride,
+                                     float* lse, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Analysis calls beside the path (the identification-accuracy study:
  * [Key claims, §3.1 / Fig. 3; §3.2, Figs. 3-4; §5.3]).

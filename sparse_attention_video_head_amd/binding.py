@@ -31,6 +31,7 @@ EXPORTED = [
     "svg2_unpermute",
     "svg2_cluster_means_workspace_size", "svg2_cluster_means", "svg2_recall_mass",
     "svg2_quantize_fp8_workspace_size", "svg2_quantize_fp8", "svg2_varblock_attn_fp8",
+    "svg2_varblock_attn_fp8_unpermute",
 ]
 
 
@@ -99,6 +100,10 @@ def lib() -> ctypes.CDLL:
     L.svg2_varblock_attn_fp8.restype = ctypes.c_int
     L.svg2_varblock_attn_fp8.argtypes = [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_p, _c_int,
                                          _c_p, _c_int, _c_p, _c_p, ctypes.c_float, _c_p, _c_p, _c_p, _c_sz, _c_p]
+    L.svg2_varblock_attn_fp8_unpermute.restype = ctypes.c_int
+    L.svg2_varblock_attn_fp8_unpermute.argtypes = [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_p,
+                                                   _c_int, _c_p, _c_int, _c_p, _c_p, ctypes.c_float, _c_p, _c_p,
+                                                   _c_int, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_sz, _c_p]
     _lib = L
     return L
 
@@ -517,4 +522,49 @@ def varblock_attn_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, q_sc
                                   d, _ptr(q_offsets), n_q, _ptr(k_offsets), n_k, _ptr(sel_count), _ptr(sel_idx),
                                   ctypes.c_float(scale), _ptr(out), _ptr(ls), _ptr(ws), ws_n, _stream(dev))
     _check(st, "svg2_varblock_attn_fp8")
+    return out, ls
+
+
+def varblock_attn_fp8_unpermute(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, q_scale: torch.Tensor,
+                                k_scale: torch.Tensor, v_scale: torch.Tensor, q_offsets: torch.Tensor,
+                                k_offsets: torch.Tensor, sel_count: torch.Tensor, sel_idx: torch.Tensor,
+                                perm: torch.Tensor, scale: Optional[float] = None, lse=False,
+                                out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """varblock_attn_fp8 with the inverse permutation fused into its stores:
+    out row perm[i] = attention output row i.  ``out`` is a bf16 [bh,N,d] or
+    [B,H,N,d] view; ``lse`` (flag or fp32 [bh, N] tensor) in the original order."""
+    _need_cuda(q8, k8, v8, q_scale, k_scale, v_scale, q_offsets, k_offsets, sel_count, sel_idx, perm, out)
+    for t in (q8, k8, v8):
+        if t.dim() != 3 or not t.is_contiguous() or t.shape != q8.shape or t.dtype != torch.uint8:
+            raise Svg2Error("q8, k8, v8 must be contiguous uint8 [bh, N, d] tensors of one shape")
+    bh, N, d = q8.shape
+    for t in (q_scale, k_scale, v_scale):
+        if t.dtype != torch.float32 or tuple(t.shape) != (bh,) or not t.is_contiguous():
+            raise Svg2Error("scales must be contiguous fp32 [bh]")
+    if perm.dtype != torch.int32 or not perm.is_contiguous() or tuple(perm.shape) != (bh, N):
+        raise Svg2Error("perm must be contiguous int32 [bh, N]")
+    n_q = q_offsets.shape[1] - 1
+    n_k = k_offsets.shape[1] - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dev = q8.device
+    if out is None:
+        out = torch.empty(bh, N, d, dtype=torch.bfloat16, device=dev)
+    obh, oN, od, heads, sb, sh, st = _strided_view(out)
+    if (obh, oN, od) != (bh, N, d) or out.dtype != torch.bfloat16:
+        raise Svg2Error("out must be a bf16 view of shape [bh, N, d]")
+    if isinstance(lse, torch.Tensor):
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (bh, N) or not lse.is_contiguous():
+            raise Svg2Error("lse must be a contiguous fp32 [bh, N] tensor")
+        ls = lse
+    else:
+        ls = torch.empty(bh, N, dtype=torch.float32, device=dev) if lse else None
+    L = lib()
+    ws_n = L.svg2_varblock_attn_workspace_size(bh, N, n_q, n_k, d)
+    ws = _workspace(ws_n, dev, workspace)
+    s = L.svg2_varblock_attn_fp8_unpermute(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale), _ptr(k_scale),
+                                           _ptr(v_scale), bh, N, d, _ptr(q_offsets), n_q, _ptr(k_offsets), n_k,
+                                           _ptr(sel_count), _ptr(sel_idx), ctypes.c_float(scale), _ptr(perm),
+                                           _ptr(out), heads, sb, sh, st, _ptr(ls), _ptr(ws), ws_n, _stream(dev))
+    _check(s, "svg2_varblock_attn_fp8_unpermute")
     return out, ls

@@ -159,6 +159,31 @@ int kmeans_run(const void* x, int32_t dtype, int32_t bh, int32_t n_tokens, int32
   return SVG2_OK;
 }
 
+// the FP8 attention's checks and launch; om maps output rows (identity, or
+// token perm[row] through strides)
+int attn_fp8_run(const void* q8, const void* k8, const void* v8, const float* q_scale, const float* k_scale,
+                 const float* v_scale, int32_t bh, int32_t n_tokens, int32_t head_dim, const int32_t* q_offsets,
+                 int32_t n_q, const int32_t* k_offsets, int32_t n_k, const int32_t* sel_count,
+                 const int32_t* sel_idx, float scale, void* out, float* lse, const OutMap& om, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream) {
+  if (n_q < 1 || n_q > kMaxClusters || n_k < 1 || n_k > kMaxClusters) return SVG2_ERR_INVALID_ARG;
+  if (!(isfinite(scale) && scale > 0.f)) return SVG2_ERR_INVALID_ARG;
+  if (!q8 || !k8 || !v8 || !out || !aligned(q8, 16) || !aligned(k8, 16) || !aligned(v8, 16) || !aligned(out, 16))
+    return SVG2_ERR_INVALID_ARG;
+  if (!q_scale || !k_scale || !v_scale || !aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(v_scale, 4))
+    return SVG2_ERR_INVALID_ARG;
+  if (!q_offsets || !k_offsets || !sel_count || !sel_idx || !aligned(q_offsets, 4) ||
+      !aligned(k_offsets, 4) || !aligned(sel_count, 4) || !aligned(sel_idx, 4) || (lse && !aligned(lse, 4)))
+    return SVG2_ERR_INVALID_ARG;
+  const size_t need = svg2_varblock_attn_workspace_size(bh, n_tokens, n_q, n_k, head_dim);
+  if (workspace_bytes < need || !workspace) return SVG2_ERR_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return SVG2_ERR_INVALID_ARG;
+  Carve c(workspace);
+  const AttnWs ws = carve_attn(c, bh, n_tokens, n_q);
+  return hip_status(launch_varblock_attn_fp8(q8, k8, v8, q_scale, k_scale, v_scale, bh, n_tokens, q_offsets, n_q,
+                                             k_offsets, n_k, sel_count, sel_idx, scale, out, lse, om, ws, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -391,23 +416,27 @@ int svg2_varblock_attn_fp8(const void* q8, const void* k8, const void* v8, const
                            const int32_t* sel_idx, float scale, void* out, float* lse, void* workspace,
                            size_t workspace_bytes, hipStream_t stream) {
   if (bh < 1 || n_tokens < 1 || n_tokens > kMaxTokens) return SVG2_ERR_INVALID_ARG;
-  if (n_q < 1 || n_q > kMaxClusters || n_k < 1 || n_k > kMaxClusters) return SVG2_ERR_INVALID_ARG;
   if (head_dim != 128) return SVG2_ERR_UNSUPPORTED;
-  if (!(isfinite(scale) && scale > 0.f)) return SVG2_ERR_INVALID_ARG;
-  if (!q8 || !k8 || !v8 || !out || !aligned(q8, 16) || !aligned(k8, 16) || !aligned(v8, 16) || !aligned(out, 16))
-    return SVG2_ERR_INVALID_ARG;
-  if (!q_scale || !k_scale || !v_scale || !aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(v_scale, 4))
-    return SVG2_ERR_INVALID_ARG;
-  if (!q_offsets || !k_offsets || !sel_count || !sel_idx || !aligned(q_offsets, 4) ||
-      !aligned(k_offsets, 4) || !aligned(sel_count, 4) || !aligned(sel_idx, 4) || (lse && !aligned(lse, 4)))
-    return SVG2_ERR_INVALID_ARG;
-  const size_t need = svg2_varblock_attn_workspace_size(bh, n_tokens, n_q, n_k, head_dim);
-  if (workspace_bytes < need || !workspace) return SVG2_ERR_WORKSPACE;
-  if (!aligned(workspace, kAlign)) return SVG2_ERR_INVALID_ARG;
-  Carve c(workspace);
-  const AttnWs ws = carve_attn(c, bh, n_tokens, n_q);
-  return hip_status(launch_varblock_attn_fp8(q8, k8, v8, q_scale, k_scale, v_scale, bh, n_tokens, q_offsets, n_q,
-                                             k_offsets, n_k, sel_count, sel_idx, scale, out, lse, ws, stream));
+  return attn_fp8_run(q8, k8, v8, q_scale, k_scale, v_scale, bh, n_tokens, head_dim, q_offsets, n_q, k_offsets,
+                      n_k, sel_count, sel_idx, scale, out, lse, contiguous_out(n_tokens, head_dim), workspace,
+                      workspace_bytes, stream);
+}
+
+int svg2_varblock_attn_fp8_unpermute(const void* q8, const void* k8, const void* v8, const float* q_scale,
+                                     const float* k_scale, const float* v_scale, int32_t bh, int32_t n_tokens,
+                                     int32_t head_dim, const int32_t* q_offsets, int32_t n_q,
+                                     const int32_t* k_offsets, int32_t n_k, const int32_t* sel_count,
+                                     const int32_t* sel_idx, float scale, const int32_t* perm, void* dst,
+                                     int32_t heads, int64_t dst_b_stride, int64_t dst_h_stride,
+                                     int64_t dst_token_stride, float* lse, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+  if (bh < 1 || n_tokens < 1 || n_tokens > kMaxTokens) return SVG2_ERR_INVALID_ARG;
+  if (head_dim != 128) return SVG2_ERR_UNSUPPORTED;
+  if (!perm || !aligned(perm, 4)) return SVG2_ERR_INVALID_ARG;
+  if (!strides_ok(heads, bh, dst_b_stride, dst_h_stride, dst_token_stride, 2)) return SVG2_ERR_INVALID_ARG;
+  const OutMap om{perm, heads, dst_b_stride, dst_h_stride, dst_token_stride};
+  return attn_fp8_run(q8, k8, v8, q_scale, k_scale, v_scale, bh, n_tokens, head_dim, q_offsets, n_q, k_offsets,
+                      n_k, sel_count, sel_idx, scale, dst, lse, om, workspace, workspace_bytes, stream);
 }
 
 // ------------------------------------------------------- identification study

@@ -890,7 +890,7 @@ __global__ __launch_bounds__(256, 3) void k_attn_fp8(
     int N, const int32_t* __restrict__ q_off, int n_q,
     const int32_t* __restrict__ k_off, int n_k, const int32_t* __restrict__ sel_count,
     const int32_t* __restrict__ sel_idx, float scale_log2, uint16_t* __restrict__ O, float* __restrict__ lse,
-    const int32_t* __restrict__ item_count, const int32_t* __restrict__ items, int max_items, int bh) {
+    OutMap om, const int32_t* __restrict__ item_count, const int32_t* __restrict__ items, int max_items, int bh) {
   constexpr int BN = kAttnF8BN;
   constexpr int D = kAttnF8D;
   constexpr int ROW = D;                         // bytes per tile row
@@ -1111,9 +1111,11 @@ __global__ __launch_bounds__(256, 3) void k_attn_fp8(
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part), __float_as_uint(l_part), false, false);
     l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   }
-  if (row_ok) {
+  // output row: row itself, or token perm[row] through the destination's strides
+  const int tout = row_ok ? (om.perm ? om.perm[(size_t)p * N + row] : row) : -1;
+  if (row_ok && (unsigned)tout < (unsigned)N) {
     const float inv = l_tot > 0.f ? sv / l_tot : 0.f;
-    uint16_t* orow = O + base + (size_t)row * D;
+    uint16_t* orow = O + (p / om.heads) * om.bs + (p % om.heads) * om.hs + (int64_t)tout * om.ts;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -1124,8 +1126,8 @@ __global__ __launch_bounds__(256, 3) void k_attn_fp8(
         *reinterpret_cast<uint2*>(orow + dt * 32 + g * 8 + half * 4) = w;
       }
     if (lse && half == 0)
-      lse[(size_t)p * N + row] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * 0.69314718055994531f
-                                            : -__builtin_inff();
+      lse[(size_t)p * N + tout] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * 0.69314718055994531f
+                                             : -__builtin_inff();
   }
 }
 
@@ -1261,7 +1263,7 @@ hipError_t launch_varblock_attn_fp8(const void* q, const void* k, const void* v,
                                     const float* k_scale, const float* v_scale, int bh, int N,
                                     const int32_t* q_off, int n_q, const int32_t* k_off, int n_k,
                                     const int32_t* sel_count, const int32_t* sel_idx, float scale, void* out,
-                                    float* lse, const AttnWs& ws, hipStream_t s) {
+                                    float* lse, const OutMap& om, const AttnWs& ws, hipStream_t s) {
   const int max_items = attn_max_items(N, n_q, kAttnBM);
   int32_t* tiles_ws = ws.tiles;
   int32_t* item_count_ws = ws.item_count;
@@ -1275,7 +1277,7 @@ hipError_t launch_varblock_attn_fp8(const void* q, const void* k, const void* v,
   hipLaunchKernelGGL(k_attn_fp8, dim3((total + span - 1) / span * span), dim3(256), 0, s,
                      static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(k), static_cast<const uint8_t*>(v),
                      q_scale, k_scale, v_scale, N, q_off, n_q, k_off, n_k, sel_count, sel_idx,
-                     scale * 1.4426950408889634f, static_cast<uint16_t*>(out), lse, item_count_ws, items_ws,
+                     scale * 1.4426950408889634f, static_cast<uint16_t*>(out), lse, om, item_count_ws, items_ws,
                      max_items, bh);
   return hipGetLastError();
 }

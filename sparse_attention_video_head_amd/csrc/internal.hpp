@@ -97,7 +97,7 @@ hipError_t launch_varblock_attn_fp8(const void* q, const void* k, const void* v,
                                     const float* k_scale, const float* v_scale, int bh, int N,
                                     const int32_t* q_off, int n_q, const int32_t* k_off, int n_k,
                                     const int32_t* sel_count, const int32_t* sel_idx, float scale, void* out,
-                                    float* lse, const AttnWs& ws, hipStream_t s);
+                                    float* lse, const OutMap& om, const AttnWs& ws, hipStream_t s);
 
 // ---------------------------------------------------------------- quant.hip
 // x8 = E4M3(x / scale), scale[p] = max|x_p| / 448 (1 if all zero); x bf16

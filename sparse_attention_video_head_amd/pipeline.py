@@ -141,11 +141,15 @@ class SVG2Layer:
                       sel_count=self.sel_count, sel_idx=self.sel_idx, pair_count=self.pairs,
                       workspace=self.ws_sel)
 
+    def quantize(self):
+        """E4M3 copies of Q', K', V' with per-problem scales (FP8 attention)."""
+        for x, x8, sc in ((self.qp, self.q8, self.s8[0]), (self.kp, self.k8, self.s8[1]),
+                          (self.vp, self.v8, self.s8[2])):
+            B.quantize_fp8(x, x8, sc, workspace=self.ws_q8)
+
     def attend(self):
         if self.fp8:
-            for x, x8, sc in ((self.qp, self.q8, self.s8[0]), (self.kp, self.k8, self.s8[1]),
-                              (self.vp, self.v8, self.s8[2])):
-                B.quantize_fp8(x, x8, sc, workspace=self.ws_q8)
+            self.quantize()
             B.varblock_attn_fp8(self.q8, self.k8, self.v8, self.s8[0], self.s8[1], self.s8[2], self.off_q,
                                 self.off_k, self.sel_count, self.sel_idx, scale=self.scale, out=self.op,
                                 workspace=self.ws_attn)
@@ -158,11 +162,14 @@ class SVG2Layer:
 
     def attend_unpermute(self, out: Optional[torch.Tensor] = None):
         """Attention with the inverse permutation fused into its stores (one
-        pass less over the output); FP8 attention keeps the separate pass."""
+        pass less over the output)."""
         dst = self.out if out is None else out
         if self.fp8:
-            self.attend()
-            return self.unpermute(dst)
+            self.quantize()
+            B.varblock_attn_fp8_unpermute(self.q8, self.k8, self.v8, self.s8[0], self.s8[1], self.s8[2],
+                                          self.off_q, self.off_k, self.sel_count, self.sel_idx, self.perm_q,
+                                          scale=self.scale, out=dst, workspace=self.ws_attn)
+            return dst
         B.varblock_attn_unpermute(self.qp, self.kp, self.vp, self.off_q, self.off_k, self.sel_count, self.sel_idx,
                                   self.perm_q, scale=self.scale, out=dst, workspace=self.ws_attn)
         return dst

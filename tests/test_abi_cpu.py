@@ -250,3 +250,23 @@ def test_fp8_validation():
     assert attn(k=MISALIGNED) == INVALID
     assert attn(scale=-1.0) == INVALID
     assert attn(wsn=8) == WORKSPACE
+
+    def attn_unperm(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, sq=FAKE, sk=FAKE, sv=FAKE, bh=2, N=300, d=128, qo=FAKE, nq=5, ko=FAKE, nk=7,
+                 sc=FAKE, si=FAKE, scale=0.088, perm=FAKE, out=FAKE, heads=1, sb=38400, sh=0, st=128, lse=None,
+                 ws=FAKE, wsn=1 << 30)
+        a.update(kw)
+        return L.svg2_varblock_attn_fp8_unpermute(
+            a["q"], a["k"], a["v"], a["sq"], a["sk"], a["sv"], a["bh"], a["N"], a["d"], a["qo"], a["nq"], a["ko"],
+            a["nk"], a["sc"], a["si"], ctypes.c_float(a["scale"]), a["perm"], a["out"], a["heads"], a["sb"], a["sh"],
+            a["st"], a["lse"], a["ws"], a["wsn"], None)
+    # the fused inverse permutation adds perm and the destination strides to the checks
+    assert attn_unperm(d=64) == UNSUPPORTED
+    assert attn_unperm(perm=None) == INVALID
+    assert attn_unperm(perm=FAKE + 2) == INVALID
+    assert attn_unperm(heads=3) == INVALID
+    assert attn_unperm(st=130) == INVALID
+    assert attn_unperm(out=None) == INVALID
+    assert attn_unperm(sv=None) == INVALID
+    assert attn_unperm(lse=FAKE + 2) == INVALID
+    assert attn_unperm(wsn=8) == WORKSPACE

@@ -552,6 +552,39 @@ def test_varblock_attn_fp8_vs_oracle():
         assert np.all(lse[h].cpu().numpy()[~fin] == -np.inf) and np.all(got[~fin] == 0)
 
 
+@pytest.mark.parametrize("layout", ["contiguous", "bnhd"])
+def test_varblock_attn_fp8_unpermute_equals_attn_then_unpermute(layout):
+    """The FP8 attention with the inverse permutation in its stores writes, bit
+    for bit, what the FP8 attention followed by the stand-alone un-permute
+    writes (outputs and lse); the permutation is the oracle's of random labels."""
+    bh, N, n_q, n_k, heads = 4, 2500, 16, 40, 2
+    q, k, v, qo, ko, cnt, idx, lists, qo_np, ko_np = _attn_case("bf16", 128, bh, N, n_q, n_k, 0.9, seed=93,
+                                                               empty_rows=True)
+    q8, sq = B.quantize_fp8(q.to(DEV))
+    k8, sk = B.quantize_fp8(k.to(DEV))
+    v8, sv = B.quantize_fp8(v.to(DEV))
+    perm = np.stack([oracle.counting_sort(synth.random_labels(N, 23, seed=40 + p), 23)[0] for p in range(bh)])
+    pd = torch.from_numpy(perm.astype(np.int32)).to(DEV)
+    o_ref, l_ref = B.varblock_attn_fp8(q8, k8, v8, sq, sk, sv, qo, ko, cnt, idx, lse=True)
+    if layout == "contiguous":
+        dst = torch.full((bh, N, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
+        view = dst
+        want = torch.empty_like(dst)
+        B.unpermute(o_ref, pd, out=want)
+    else:
+        dst = torch.full((bh // heads, N, heads, 128), float("nan"), dtype=torch.bfloat16, device=DEV)
+        view = dst.transpose(1, 2)
+        want_full = torch.empty_like(dst)
+        B.unpermute(o_ref, pd, out=want_full.transpose(1, 2))
+        want = want_full
+    _, lse = B.varblock_attn_fp8_unpermute(q8, k8, v8, sq, sk, sv, qo, ko, cnt, idx, pd, lse=True, out=view)
+    torch.cuda.synchronize()
+    assert torch.equal(dst.view(torch.int16), want.view(torch.int16))
+    lr = l_ref.cpu().numpy()
+    for p in range(bh):
+        np.testing.assert_array_equal(lse[p].cpu().numpy()[perm[p]], lr[p])
+
+
 def test_layer_fp8_attention_vs_oracle():
     """One head of the small bf16 config: the whole layer with FP8 attention
     against the oracle layer (fp64 on the bf16 inputs), at the FP8 tolerance."""
