@@ -132,6 +132,25 @@ int svg2_kmeans_permute(const void* x, const void* y, int32_t dtype, int32_t bh,
                         void* y_perm, int32_t* perm, int32_t* offsets,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* svg2_kmeans_permute_fp8 - svg2_kmeans_permute on bf16 inputs whose
+ * permuted copies are stored as E4M3 bytes, for the FP8 attention [Method,
+ * stages (1) and (2)]: x8_perm, x_scale (and y8_perm, y_scale) are, bit for
+ * bit, svg2_quantize_fp8 of the bf16 rows svg2_kmeans_permute would write
+ * (the per-problem max|.| does not depend on the row order, so it is taken
+ * from x and y before the clustering starts).
+ *
+ *   x8_perm, y8_perm  out [bh, n_tokens, head_dim] uint8 (E4M3).
+ *   x_scale, y_scale  out [bh] fp32 dequantization scales.
+ *   y, y8_perm and y_scale are all NULL or all given.  Other arguments as for
+ *   svg2_kmeans_permute (dtype is bf16; min_dist and seed_index are not
+ *   offered).  Workspace: svg2_kmeans_workspace_size bytes. */
+int svg2_kmeans_permute_fp8(const void* x, const void* y, int32_t bh, int32_t n_tokens,
+                            int32_t head_dim, int32_t n_clusters, int32_t n_iters,
+                            const float* init_centroids, uint64_t seed, float* centroids,
+                            int32_t* labels, int32_t* counts, void* x8_perm, float* x_scale,
+                            void* y8_perm, float* y_scale, int32_t* perm, int32_t* offsets,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * svg2_permute - build the permutation of each problem from its cluster
  * labels and gather rows into contiguous cluster blocks; with n_tensors = 2

@@ -24,7 +24,7 @@ _c_int, _c_i64, _c_u64, _c_sz, _c_p = ctypes.c_int32, ctypes.c_int64, ctypes.c_u
 
 EXPORTED = [
     "svg2_version", "svg2_status_string", "svg2_last_hip_error",
-    "svg2_kmeans_workspace_size", "svg2_kmeans", "svg2_kmeans_permute",
+    "svg2_kmeans_workspace_size", "svg2_kmeans", "svg2_kmeans_permute", "svg2_kmeans_permute_fp8",
     "svg2_permute_workspace_size", "svg2_permute",
     "svg2_select_topp_workspace_size", "svg2_select_topp",
     "svg2_varblock_attn_workspace_size", "svg2_varblock_attn", "svg2_varblock_attn_unpermute",
@@ -64,6 +64,9 @@ def lib() -> ctypes.CDLL:
     L.svg2_kmeans_permute.restype = ctypes.c_int
     L.svg2_kmeans_permute.argtypes = [_c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_p, _c_u64,
                                       _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]
+    L.svg2_kmeans_permute_fp8.restype = ctypes.c_int
+    L.svg2_kmeans_permute_fp8.argtypes = [_c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_int, _c_p, _c_u64, _c_p,
+                                          _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_sz, _c_p]
     L.svg2_permute_workspace_size.restype = _c_sz
     L.svg2_permute_workspace_size.argtypes = [_c_int] * 3
     L.svg2_permute.restype = ctypes.c_int
@@ -187,10 +190,13 @@ def kmeans_permute(x: torch.Tensor, n_clusters: int, n_iters: int, y: Optional[t
                    labels: Optional[torch.Tensor] = None, counts: Optional[torch.Tensor] = None,
                    x_out: Optional[torch.Tensor] = None, y_out: Optional[torch.Tensor] = None,
                    perm: Optional[torch.Tensor] = None, offsets: Optional[torch.Tensor] = None,
-                   workspace: Optional[torch.Tensor] = None):
+                   workspace: Optional[torch.Tensor] = None, fp8: bool = False,
+                   x_scale: Optional[torch.Tensor] = None, y_scale: Optional[torch.Tensor] = None):
     """k-means of x [bh, N, d] (n_iters >= 1) with the rows of x, and of y when
-    given, gathered into the final clusters' order in the last round.  Returns
-    dict(centroids, labels, counts, x_perm, y_perm, perm, offsets)."""
+    given, gathered into the final clusters' order in the last round.  With
+    ``fp8`` (bf16 inputs) the gathered rows are E4M3 (uint8) with [bh] fp32
+    scales, as quantize_fp8 of the bf16 rows.  Returns dict(centroids, labels,
+    counts, x_perm, y_perm, perm, offsets, x_scale, y_scale)."""
     _need_cuda(x, y, init)
     if x.dim() != 3 or not x.is_contiguous():
         raise Svg2Error("x must be a contiguous [bh, N, d] tensor")
@@ -205,24 +211,42 @@ def kmeans_permute(x: torch.Tensor, n_clusters: int, n_iters: int, y: Optional[t
     centroids = e(bh, n_clusters, d, dt=torch.float32) if centroids is None else centroids
     labels = e(bh, N) if labels is None else labels
     counts = e(bh, n_clusters) if counts is None else counts
-    x_out = torch.empty_like(x) if x_out is None else x_out
+    if fp8 and x.dtype != torch.bfloat16:
+        raise Svg2Error("E4M3 rows are made from bf16 inputs")
+    odt = torch.uint8 if fp8 else x.dtype
+    x_out = torch.empty(x.shape, dtype=odt, device=dev) if x_out is None else x_out
     if y is not None and y_out is None:
-        y_out = torch.empty_like(y)
+        y_out = torch.empty(x.shape, dtype=odt, device=dev)
     for o in (x_out, y_out):
-        if o is not None and (o.shape != x.shape or o.dtype != x.dtype or not o.is_contiguous()):
-            raise Svg2Error("permuted outputs must be contiguous tensors of x's shape and dtype")
+        if o is not None and (o.shape != x.shape or o.dtype != odt or not o.is_contiguous()):
+            raise Svg2Error("permuted outputs must be contiguous tensors of x's shape (uint8 for fp8)")
     perm = e(bh, N) if perm is None else perm
     offsets = e(bh, n_clusters + 1) if offsets is None else offsets
     L = lib()
     ws_n = L.svg2_kmeans_workspace_size(bh, N, d, n_clusters)
     ws = _workspace(ws_n, dev, workspace)
+    if fp8:
+        x_scale = e(bh, dt=torch.float32) if x_scale is None else x_scale
+        if y is not None and y_scale is None:
+            y_scale = e(bh, dt=torch.float32)
+        for t in (x_scale, y_scale):
+            if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (bh,) or not t.is_contiguous()):
+                raise Svg2Error("scales must be contiguous fp32 [bh]")
+        st = L.svg2_kmeans_permute_fp8(_ptr(x), _ptr(y), bh, N, d, n_clusters, n_iters, _ptr(init),
+                                       ctypes.c_uint64(seed & ((1 << 64) - 1)), _ptr(centroids), _ptr(labels),
+                                       _ptr(counts), _ptr(x_out), _ptr(x_scale), _ptr(y_out),
+                                       _ptr(y_scale if y is not None else None), _ptr(perm), _ptr(offsets),
+                                       _ptr(ws), ws_n, _stream(dev))
+        _check(st, "svg2_kmeans_permute_fp8")
+        return dict(centroids=centroids, labels=labels, counts=counts, x_perm=x_out, y_perm=y_out, perm=perm,
+                    offsets=offsets, x_scale=x_scale, y_scale=y_scale if y is not None else None)
     st = L.svg2_kmeans_permute(_ptr(x), _ptr(y), _dtype_code(x), bh, N, d, n_clusters, n_iters, _ptr(init),
                                ctypes.c_uint64(seed & ((1 << 64) - 1)), _ptr(centroids), _ptr(labels),
                                _ptr(counts), None, None, _ptr(x_out), _ptr(y_out), _ptr(perm), _ptr(offsets),
                                _ptr(ws), ws_n, _stream(dev))
     _check(st, "svg2_kmeans_permute")
     return dict(centroids=centroids, labels=labels, counts=counts, x_perm=x_out, y_perm=y_out, perm=perm,
-                offsets=offsets)
+                offsets=offsets, x_scale=None, y_scale=None)
 
 
 # ---------------------------------------------------------------- permute

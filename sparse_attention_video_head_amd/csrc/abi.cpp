@@ -56,6 +56,7 @@ struct KmeansWs {
   int32_t* perm;
   int32_t* offsets;
   double* partial;    // bh * (n + mean_chunks(N)) * d: per-chunk centroid sums
+  uint32_t* amax;     // 2 bh: max|x|, max|y| per problem (E4M3 row moves)
 };
 
 KmeansWs carve_kmeans(Carve& c, int bh, int N, int d, int n) {
@@ -73,6 +74,7 @@ KmeansWs carve_kmeans(Carve& c, int bh, int N, int d, int n) {
   w.perm = c.take<int32_t>(bN);
   w.offsets = c.take<int32_t>((size_t)bh * (n + 1));
   w.partial = c.take<double>((size_t)bh * (n + mean_chunks(N)) * d);
+  w.amax = c.take<uint32_t>((size_t)2 * bh);
   return w;
 }
 
@@ -103,13 +105,14 @@ AttnWs carve_attn(Carve& c, int bh, int N, int n_q) {
   return w;
 }
 
-// svg2_kmeans, and with x_sorted set, svg2_kmeans_permute: the last round's
-// sort writes perm / offsets and its centroid update also moves the rows.
+// svg2_kmeans, and with mv.x_out set, svg2_kmeans_permute(_fp8): the last
+// round's sort writes perm / offsets and its centroid update also moves the
+// rows (as E4M3 when fp8, with max|.| taken from the inputs first).
 int kmeans_run(const void* x, int32_t dtype, int32_t bh, int32_t n_tokens, int32_t head_dim,
                int32_t n_clusters, int32_t n_iters, const float* init_centroids, uint64_t seed,
                float* centroids, int32_t* labels, int32_t* counts, float* min_dist, int32_t* seed_index,
-               void* x_sorted, const void* y, void* y_sorted, int32_t* perm_out, int32_t* offsets_out,
-               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+               MeanMove mv, bool fp8, int32_t* perm_out, int32_t* offsets_out, void* workspace,
+               size_t workspace_bytes, hipStream_t stream) {
   if (!dtype_ok(dtype)) return SVG2_ERR_INVALID_ARG;
   if (!shape_ok(bh, n_tokens, n_clusters)) return SVG2_ERR_INVALID_ARG;
   if (!dim_ok(head_dim)) return SVG2_ERR_UNSUPPORTED;
@@ -129,6 +132,15 @@ int kmeans_run(const void* x, int32_t dtype, int32_t bh, int32_t n_tokens, int32
   const bool bf16 = dtype == SVG2_BF16;
   const int N = n_tokens, n = n_clusters, d = head_dim;
   int st;
+  if (fp8) {
+    mv.amax = w.amax;
+    st = hip_status(launch_amax_bf16(x, bh, N, d, w.amax, stream));
+    if (st) return st;
+    if (mv.y) {
+      st = hip_status(launch_amax_bf16(mv.y, bh, N, d, w.amax + bh, stream));
+      if (st) return st;
+    }
+  }
   if (!init_centroids) {
     st = hip_status(launch_kmeanspp(x, bf16, bh, N, d, n, seed, w.d2, w.near, centroids, seed_index,
                                     w.picks, w.cc, w.bsum, stream));
@@ -146,14 +158,13 @@ int kmeans_run(const void* x, int32_t dtype, int32_t bh, int32_t n_tokens, int32
     st = hip_status(launch_assign(x, bf16, bh, N, d, n, centroids, w.c_hi, w.c_lo, w.c_norm, labels,
                                   it == n_iters - 1 ? min_dist : nullptr, stream));
     if (st) return st;
-    const bool last = it == n_iters - 1 && x_sorted;
+    const bool last = it == n_iters - 1 && mv.x_out;
     int32_t* pm = last ? perm_out : w.perm;
     int32_t* of = last ? offsets_out : w.offsets;
     st = hip_status(launch_counting_sort(labels, bh, N, n, w.hist, pm, of, counts, stream));
     if (st) return st;
     st = hip_status(launch_centroid_mean(x, bf16, bh, N, d, n, pm, of, w.partial, centroids, stream,
-                                         last ? x_sorted : nullptr, last ? y : nullptr,
-                                         last ? y_sorted : nullptr));
+                                         last ? mv : MeanMove{}));
     if (st) return st;
   }
   return SVG2_OK;
@@ -216,7 +227,7 @@ int svg2_kmeans(const void* x, int32_t dtype, int32_t bh, int32_t n_tokens, int3
                 float* centroids, int32_t* labels, int32_t* counts, float* min_dist,
                 int32_t* seed_index, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return kmeans_run(x, dtype, bh, n_tokens, head_dim, n_clusters, n_iters, init_centroids, seed, centroids,
-                    labels, counts, min_dist, seed_index, nullptr, nullptr, nullptr, nullptr, nullptr, workspace,
+                    labels, counts, min_dist, seed_index, MeanMove{}, false, nullptr, nullptr, workspace,
                     workspace_bytes, stream);
 }
 
@@ -232,9 +243,36 @@ int svg2_kmeans_permute(const void* x, const void* y, int32_t dtype, int32_t bh,
   if (y && (!aligned(y, 16) || !aligned(y_perm, 16))) return SVG2_ERR_INVALID_ARG;
   if (x_perm == x || (y && (y_perm == y || y_perm == x || x_perm == y || y_perm == x_perm)))
     return SVG2_ERR_INVALID_ARG;
+  MeanMove mv;
+  mv.x_out = x_perm;
+  mv.y = y;
+  mv.y_out = y_perm;
   return kmeans_run(x, dtype, bh, n_tokens, head_dim, n_clusters, n_iters, init_centroids, seed, centroids,
-                    labels, counts, min_dist, seed_index, x_perm, y, y_perm, perm, offsets, workspace,
-                    workspace_bytes, stream);
+                    labels, counts, min_dist, seed_index, mv, false, perm, offsets, workspace, workspace_bytes,
+                    stream);
+}
+
+int svg2_kmeans_permute_fp8(const void* x, const void* y, int32_t bh, int32_t n_tokens, int32_t head_dim,
+                            int32_t n_clusters, int32_t n_iters, const float* init_centroids, uint64_t seed,
+                            float* centroids, int32_t* labels, int32_t* counts, void* x8_perm, float* x_scale,
+                            void* y8_perm, float* y_scale, int32_t* perm, int32_t* offsets, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  if (n_iters < 1) return SVG2_ERR_INVALID_ARG;
+  if (!x8_perm || !aligned(x8_perm, 16) || !x_scale || !aligned(x_scale, 4) || !perm || !aligned(perm, 4) ||
+      !offsets || !aligned(offsets, 4))
+    return SVG2_ERR_INVALID_ARG;
+  if ((y == nullptr) != (y8_perm == nullptr) || (y == nullptr) != (y_scale == nullptr)) return SVG2_ERR_INVALID_ARG;
+  if (y && (!aligned(y, 16) || !aligned(y8_perm, 16) || !aligned(y_scale, 4))) return SVG2_ERR_INVALID_ARG;
+  if (x8_perm == x || (y && (y8_perm == y || y8_perm == x || x8_perm == y || y8_perm == x8_perm)))
+    return SVG2_ERR_INVALID_ARG;
+  MeanMove mv;
+  mv.x_out = x8_perm;
+  mv.y = y;
+  mv.y_out = y8_perm;
+  mv.x_scale = x_scale;
+  mv.y_scale = y_scale;
+  return kmeans_run(x, SVG2_BF16, bh, n_tokens, head_dim, n_clusters, n_iters, init_centroids, seed, centroids,
+                    labels, counts, nullptr, nullptr, mv, true, perm, offsets, workspace, workspace_bytes, stream);
 }
 
 // ------------------------------------------------------------------ permute

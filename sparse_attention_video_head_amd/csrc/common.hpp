@@ -99,4 +99,37 @@ __device__ T block_sum(T v, T* scratch) {
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
+// OCP E4M3 with one scale per problem: scale = max|x| / 448 dequantizes,
+// r = 448 / max|x| quantizes (both correctly rounded fp32, 1 for an all-zero
+// problem); x8 = E4M3(x * r), the product in fp32 clamped to +-448 and the
+// conversion round-to-nearest-even.  amax_bits: max|x| as float bits.
+constexpr float kE4M3Max = 448.f;
+
+__device__ __forceinline__ float quant_scale(uint32_t amax_bits) {
+  const float a = __uint_as_float(amax_bits);
+  return a > 0.f ? a / kE4M3Max : 1.f;
+}
+
+__device__ __forceinline__ float quant_ratio(uint32_t amax_bits) {
+  const float a = __uint_as_float(amax_bits);
+  return a > 0.f ? kE4M3Max / a : 1.f;
+}
+
+__device__ __forceinline__ float quant_mul(float v, float r) {
+  return fminf(fmaxf(v * r, -kE4M3Max), kE4M3Max);
+}
+
+// 8 bf16 values (16 bytes) -> 8 E4M3 bytes
+__device__ __forceinline__ uint2 quant8_bf16(const u32x4_t& v, float r) {
+  int lo = 0, hi = 0;
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(quant_mul(bf16_lo(v[0]), r), quant_mul(bf16_hi(v[0]), r), lo, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(quant_mul(bf16_lo(v[1]), r), quant_mul(bf16_hi(v[1]), r), lo, true);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(quant_mul(bf16_lo(v[2]), r), quant_mul(bf16_hi(v[2]), r), hi, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(quant_mul(bf16_lo(v[3]), r), quant_mul(bf16_hi(v[3]), r), hi, true);
+  uint2 w;
+  w.x = (uint32_t)lo;
+  w.y = (uint32_t)hi;
+  return w;
+}
+
 }  // namespace svg2

@@ -45,12 +45,24 @@ hipError_t launch_assign(const void* x, bool bf16, int bh, int N, int d, int n, 
 // partial_ws: bh * (n + mean_chunks(N)) * d doubles.
 constexpr int kMeanChunk = 512;              // sorted positions per partial-sum work-group
 inline int mean_chunks(int n_tokens) { return (n_tokens + kMeanChunk - 1) / kMeanChunk; }
-// x_sorted (with y / y_sorted optional): also store row perm[r] of x (of y)
-// to row r, in the same pass.
+// Rows moved by the centroid update: row perm[r] of x (and of y, if given)
+// stored to row r of x_out (y_out).  With amax set (bf16 inputs only) the
+// rows are stored as E4M3 bytes scaled by 448 / max|.|, amax[p] for x and
+// amax[bh + p] for y, and x_scale / y_scale[p] receive the dequantization
+// scales.  x_out == nullptr: no move.
+struct MeanMove {
+  void* x_out = nullptr;
+  const void* y = nullptr;
+  void* y_out = nullptr;
+  const uint32_t* amax = nullptr;
+  float* x_scale = nullptr;
+  float* y_scale = nullptr;
+};
 hipError_t launch_centroid_mean(const void* x, bool bf16, int bh, int N, int d, int n,
                                 const int32_t* perm, const int32_t* offsets, double* partial_ws, float* c,
-                                hipStream_t s, void* x_sorted = nullptr, const void* y = nullptr,
-                                void* y_sorted = nullptr);
+                                hipStream_t s, const MeanMove& mv = MeanMove{});
+// max|x| per problem of a bf16 [bh, N, d] tensor, as float bits in amax_ws[bh]
+hipError_t launch_amax_bf16(const void* x, int bh, int N, int d, uint32_t* amax_ws, hipStream_t s);
 
 // --------------------------------------------------------------- select.hip
 hipError_t launch_select_topp(const float* cq, const int32_t* q_counts, int n_q, const float* ck,

@@ -785,15 +785,16 @@ hipError_t launch_assign(const void* x, bool bf16, int bh, int N, int d, int n, 
 // every cluster is a contiguous, increasing range of the sorted order).  A
 // second kernel adds each cluster's partials in chunk order.  Every sum runs
 // in a fixed order, so the result is the same run to run.
-// MOVE: the rows read at sorted position r are also stored to row r of Xo
-// (and, when Y is given, row perm[r] of Y to row r of Yo): the permutation
-// into cluster blocks rides on the reads the update makes anyway.
-template <typename T, int D, bool MOVE>
+// MOVE (1: same dtype, 2: E4M3 from bf16): the rows read at sorted position
+// r are also stored to row r of mv.x_out (and, when mv.y is given, row
+// perm[r] of y to row r of mv.y_out): the permutation into cluster blocks
+// rides on the reads the update makes anyway.
+template <typename T, int D, int MOVE>
 __global__ __launch_bounds__(256) void k_centroid_partial(const T* __restrict__ X, int N, int n,
                                                           const int32_t* __restrict__ perm,
                                                           const int32_t* __restrict__ offsets,
-                                                          double* __restrict__ partial, T* __restrict__ Xo,
-                                                          const T* __restrict__ Y, T* __restrict__ Yo) {
+                                                          double* __restrict__ partial, MeanMove mv) {
+  static_assert(MOVE != 2 || sizeof(T) == 2, "E4M3 rows from bf16 only");
   constexpr int EPV = 16 / sizeof(T);          // elements per 16-byte vector
   constexpr int VPR = D / EPV;                 // lanes per row
   constexpr int G = 256 / VPR;                 // row groups
@@ -819,9 +820,22 @@ __global__ __launch_bounds__(256) void k_centroid_partial(const T* __restrict__ 
   __syncthreads();
   const int cv = threadIdx.x % VPR, g = threadIdx.x / VPR;
   const T* Xp = X + (size_t)p * N * D + cv * EPV;
-  T* Xq = MOVE ? Xo + (size_t)p * N * D + cv * EPV : nullptr;
-  const T* Yp = MOVE && Y ? Y + (size_t)p * N * D + cv * EPV : nullptr;
-  T* Yq = MOVE && Y ? Yo + (size_t)p * N * D + cv * EPV : nullptr;
+  // destinations: element offset of this lane's 16 source bytes (E4M3: 8 bytes)
+  using OutT = typename std::conditional<MOVE == 2, uint8_t, T>::type;
+  const size_t o_lane = (size_t)p * N * D + cv * EPV;
+  OutT* Xq = MOVE ? static_cast<OutT*>(mv.x_out) + o_lane : nullptr;
+  const T* Yp = MOVE && mv.y ? static_cast<const T*>(mv.y) + o_lane : nullptr;
+  OutT* Yq = MOVE && mv.y ? static_cast<OutT*>(mv.y_out) + o_lane : nullptr;
+  float rx = 1.f, ry = 1.f;
+  if constexpr (MOVE == 2) {
+    const int bh = (int)gridDim.y;
+    rx = quant_ratio(mv.amax[p]);
+    if (Yp) ry = quant_ratio(mv.amax[bh + p]);
+    if (k == 0 && threadIdx.x == 0) {
+      mv.x_scale[p] = quant_scale(mv.amax[p]);
+      if (Yp) mv.y_scale[p] = quant_scale(mv.amax[bh + p]);
+    }
+  }
   double* part = partial + (size_t)p * (n + chunks) * D;
   int c = s_c0, pos = j0;
   while (pos < j1 && c < n) {
@@ -845,8 +859,13 @@ __global__ __launch_bounds__(256) void k_centroid_partial(const T* __restrict__ 
         for (int u = 0; u < U; ++u) {
           const int r = i + u * G;
           if (r < end) {
-            *reinterpret_cast<u32x4_t*>(Xq + (size_t)r * D) = v[u];
-            if (Yp) *reinterpret_cast<u32x4_t*>(Yq + (size_t)r * D) = w[u];
+            if constexpr (MOVE == 2) {
+              *reinterpret_cast<uint2*>(Xq + (size_t)r * D) = quant8_bf16(v[u], rx);
+              if (Yp) *reinterpret_cast<uint2*>(Yq + (size_t)r * D) = quant8_bf16(w[u], ry);
+            } else {
+              *reinterpret_cast<u32x4_t*>(Xq + (size_t)r * D) = v[u];
+              if (Yp) *reinterpret_cast<u32x4_t*>(Yq + (size_t)r * D) = w[u];
+            }
           }
         }
       }
@@ -897,27 +916,34 @@ __global__ __launch_bounds__(D) void k_centroid_finish(int n, int chunks, const 
   C[((size_t)p * n + c) * D + threadIdx.x] = (float)(sum / (double)(b - a));
 }
 
-hipError_t launch_centroid_mean(const void* x, bool bf16, int bh, int N, int d, int n,
-                                const int32_t* perm, const int32_t* offsets, double* partial_ws, float* c,
-                                hipStream_t s, void* x_sorted, const void* y, void* y_sorted) {
+template <typename T, int D>
+void centroid_mean_t(const void* x, int bh, int N, int n, const int32_t* perm, const int32_t* offsets,
+                     double* partial_ws, float* c, hipStream_t s, const MeanMove& mv, int mode) {
   const int chunks = mean_chunks(N);
   const dim3 grid(chunks, bh);
-#define SVG2_MEAN(T, D)                                                                                   \
-  if (x_sorted)                                                                                           \
-    hipLaunchKernelGGL((k_centroid_partial<T, D, true>), grid, dim3(256), 0, s, static_cast<const T*>(x), \
-                       N, n, perm, offsets, partial_ws, static_cast<T*>(x_sorted),                        \
-                       static_cast<const T*>(y), static_cast<T*>(y_sorted));                              \
-  else                                                                                                    \
-    hipLaunchKernelGGL((k_centroid_partial<T, D, false>), grid, dim3(256), 0, s,                          \
-                       static_cast<const T*>(x), N, n, perm, offsets, partial_ws, nullptr, nullptr,       \
-                       nullptr);                                                                          \
-  hipLaunchKernelGGL((k_centroid_finish<D>), dim3(n, bh), dim3(D), 0, s, n, chunks, offsets, partial_ws, c)
-  if (bf16) {
-    if (d == 128) { SVG2_MEAN(uint16_t, 128); } else { SVG2_MEAN(uint16_t, 64); }
-  } else {
-    if (d == 128) { SVG2_MEAN(float, 128); } else { SVG2_MEAN(float, 64); }
+  const T* xt = static_cast<const T*>(x);
+  if (mode == 0) {
+    hipLaunchKernelGGL((k_centroid_partial<T, D, 0>), grid, dim3(256), 0, s, xt, N, n, perm, offsets, partial_ws, mv);
+  } else if (mode == 1) {
+    hipLaunchKernelGGL((k_centroid_partial<T, D, 1>), grid, dim3(256), 0, s, xt, N, n, perm, offsets, partial_ws, mv);
+  } else if constexpr (sizeof(T) == 2) {
+    hipLaunchKernelGGL((k_centroid_partial<T, D, 2>), grid, dim3(256), 0, s, xt, N, n, perm, offsets, partial_ws, mv);
   }
-#undef SVG2_MEAN
+  hipLaunchKernelGGL((k_centroid_finish<D>), dim3(n, bh), dim3(D), 0, s, n, chunks, offsets, partial_ws, c);
+}
+
+hipError_t launch_centroid_mean(const void* x, bool bf16, int bh, int N, int d, int n,
+                                const int32_t* perm, const int32_t* offsets, double* partial_ws, float* c,
+                                hipStream_t s, const MeanMove& mv) {
+  const int mode = !mv.x_out ? 0 : (mv.amax ? 2 : 1);
+  if (mode == 2 && !bf16) return hipErrorInvalidValue;
+  if (bf16) {
+    if (d == 128) centroid_mean_t<uint16_t, 128>(x, bh, N, n, perm, offsets, partial_ws, c, s, mv, mode);
+    else centroid_mean_t<uint16_t, 64>(x, bh, N, n, perm, offsets, partial_ws, c, s, mv, mode);
+  } else {
+    if (d == 128) centroid_mean_t<float, 128>(x, bh, N, n, perm, offsets, partial_ws, c, s, mv, mode);
+    else centroid_mean_t<float, 64>(x, bh, N, n, perm, offsets, partial_ws, c, s, mv, mode);
+  }
   return hipGetLastError();
 }
 

@@ -15,7 +15,6 @@ constexpr int kQuantThreads = 256;
 constexpr int kQuantVec = 8;                     // bf16 elements per 16-byte load
 constexpr int kQuantUnroll = 4;
 constexpr int kQuantPerWG = kQuantThreads * kQuantVec * kQuantUnroll;
-constexpr float kE4M3Max = 448.f;
 
 __global__ void k_quant_zero(uint32_t* amax, int bh) {
   const int p = blockIdx.x * blockDim.x + threadIdx.x;
@@ -53,20 +52,6 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_amax(const uint16_t* __
   }
 }
 
-__device__ __forceinline__ float quant_scale(uint32_t amax_bits) {
-  const float a = __uint_as_float(amax_bits);
-  return a > 0.f ? a / kE4M3Max : 1.f;
-}
-
-__device__ __forceinline__ float quant_ratio(uint32_t amax_bits) {
-  const float a = __uint_as_float(amax_bits);
-  return a > 0.f ? kE4M3Max / a : 1.f;
-}
-
-__device__ __forceinline__ float quant_mul(float v, float r) {
-  return fminf(fmaxf(v * r, -kE4M3Max), kE4M3Max);
-}
-
 __global__ __launch_bounds__(kQuantThreads) void k_quant_fp8(const uint16_t* __restrict__ x, size_t per_problem,
                                                              const uint32_t* __restrict__ amax,
                                                              uint8_t* __restrict__ x8, float* __restrict__ scale) {
@@ -81,15 +66,7 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_fp8(const uint16_t* __r
     const size_t e = base + ((size_t)u * kQuantThreads + threadIdx.x) * kQuantVec;
     if (e + kQuantVec <= per_problem) {
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(xp + e);
-      uint2 w;
-      int lo = 0, hi = 0;
-      lo = __builtin_amdgcn_cvt_pk_fp8_f32(quant_mul(bf16_lo(v[0]), s), quant_mul(bf16_hi(v[0]), s), lo, false);
-      lo = __builtin_amdgcn_cvt_pk_fp8_f32(quant_mul(bf16_lo(v[1]), s), quant_mul(bf16_hi(v[1]), s), lo, true);
-      hi = __builtin_amdgcn_cvt_pk_fp8_f32(quant_mul(bf16_lo(v[2]), s), quant_mul(bf16_hi(v[2]), s), hi, false);
-      hi = __builtin_amdgcn_cvt_pk_fp8_f32(quant_mul(bf16_lo(v[3]), s), quant_mul(bf16_hi(v[3]), s), hi, true);
-      w.x = (uint32_t)lo;
-      w.y = (uint32_t)hi;
-      *reinterpret_cast<uint2*>(op + e) = w;
+      *reinterpret_cast<uint2*>(op + e) = quant8_bf16(v, s);
     } else {
       for (size_t i = e; i < per_problem && i < e + kQuantVec; ++i) {
         const float f = quant_mul(__uint_as_float((uint32_t)xp[i] << 16), s);
@@ -99,12 +76,19 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_fp8(const uint16_t* __r
   }
 }
 
-hipError_t launch_quantize_fp8(const void* x, int bh, int N, int d, uint8_t* x8, float* scale, uint32_t* amax_ws,
-                               hipStream_t s) {
+hipError_t launch_amax_bf16(const void* x, int bh, int N, int d, uint32_t* amax_ws, hipStream_t s) {
   const size_t per = (size_t)N * d;
   const dim3 grid((unsigned)((per + kQuantPerWG - 1) / kQuantPerWG), bh);
   hipLaunchKernelGGL(k_quant_zero, dim3((bh + 255) / 256), dim3(256), 0, s, amax_ws, bh);
   hipLaunchKernelGGL(k_quant_amax, grid, dim3(kQuantThreads), 0, s, static_cast<const uint16_t*>(x), per, amax_ws);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_fp8(const void* x, int bh, int N, int d, uint8_t* x8, float* scale, uint32_t* amax_ws,
+                               hipStream_t s) {
+  const size_t per = (size_t)N * d;
+  const dim3 grid((unsigned)((per + kQuantPerWG - 1) / kQuantPerWG), bh);
+  launch_amax_bf16(x, bh, N, d, amax_ws, s);
   hipLaunchKernelGGL(k_quant_fp8, grid, dim3(kQuantThreads), 0, s, static_cast<const uint16_t*>(x), per, amax_ws,
                      x8, scale);
   return hipGetLastError();

@@ -86,7 +86,7 @@ class SVG2Layer:
         side_q()
         main.wait_stream(self.side)
 
-    def permute(self, q, k, v):
+    def permute(self, q, k, v, quantize: bool = True):
         def side_q():
             B.permute(self.labels_q, self.n_q, q, outs=[self.qp], perm=self.perm_q, offsets=self.off_q,
                       workspace=self.ws_pq)
@@ -98,14 +98,16 @@ class SVG2Layer:
         if self.side is None:
             side_q()
             side_k()
-            return
-        # the Q side on the second stream: its small sort kernels overlap the K/V row moves
-        main = torch.cuda.current_stream(self.dev)
-        self.side.wait_stream(main)
-        with torch.cuda.stream(self.side):
-            side_q()
-        side_k()
-        main.wait_stream(self.side)
+        else:
+            # the Q side on the second stream: its small sort kernels overlap the K/V row moves
+            main = torch.cuda.current_stream(self.dev)
+            self.side.wait_stream(main)
+            with torch.cuda.stream(self.side):
+                side_q()
+            side_k()
+            main.wait_stream(self.side)
+        if self.fp8 and quantize:
+            self.quantize()
 
     def cluster(self, q, k, v, iters: int, warm: bool, seed_q: int, seed_k: int):
         """k-means of Q and K with the permutation fused into the last Lloyd
@@ -115,15 +117,21 @@ class SVG2Layer:
             self.permute(q, k, v)
             return
 
+        # FP8 attention: the moved rows are stored as E4M3 directly
+        f8 = self.fp8
+        qo, ko, vo = (self.q8, self.k8, self.v8) if f8 else (self.qp, self.kp, self.vp)
+        sq, sk, sv = (self.s8[0], self.s8[1], self.s8[2]) if f8 else (None, None, None)
+
         def side_q():
             B.kmeans_permute(q, self.n_q, iters, init=self.cq if warm else None, seed=seed_q, centroids=self.cq,
-                             labels=self.labels_q, counts=self.counts_q, x_out=self.qp, perm=self.perm_q,
-                             offsets=self.off_q, workspace=self.ws_kq)
+                             labels=self.labels_q, counts=self.counts_q, x_out=qo, perm=self.perm_q,
+                             offsets=self.off_q, workspace=self.ws_kq, fp8=f8, x_scale=sq)
 
         def side_k():
             B.kmeans_permute(k, self.n_k, iters, y=v, init=self.ck if warm else None, seed=seed_k,
-                             centroids=self.ck, labels=self.labels_k, counts=self.counts_k, x_out=self.kp,
-                             y_out=self.vp, perm=self.perm_k, offsets=self.off_k, workspace=self.ws_kk)
+                             centroids=self.ck, labels=self.labels_k, counts=self.counts_k, x_out=ko,
+                             y_out=vo, perm=self.perm_k, offsets=self.off_k, workspace=self.ws_kk, fp8=f8,
+                             x_scale=sk, y_scale=sv)
 
         if self.side is None:
             side_q()
@@ -142,14 +150,14 @@ class SVG2Layer:
                       workspace=self.ws_sel)
 
     def quantize(self):
-        """E4M3 copies of Q', K', V' with per-problem scales (FP8 attention)."""
+        """E4M3 copies of Q', K', V' with per-problem scales (FP8 attention;
+        ``cluster`` writes them directly, ``permute`` calls this)."""
         for x, x8, sc in ((self.qp, self.q8, self.s8[0]), (self.kp, self.k8, self.s8[1]),
                           (self.vp, self.v8, self.s8[2])):
             B.quantize_fp8(x, x8, sc, workspace=self.ws_q8)
 
     def attend(self):
         if self.fp8:
-            self.quantize()
             B.varblock_attn_fp8(self.q8, self.k8, self.v8, self.s8[0], self.s8[1], self.s8[2], self.off_q,
                                 self.off_k, self.sel_count, self.sel_idx, scale=self.scale, out=self.op,
                                 workspace=self.ws_attn)
@@ -165,7 +173,6 @@ class SVG2Layer:
         pass less over the output)."""
         dst = self.out if out is None else out
         if self.fp8:
-            self.quantize()
             B.varblock_attn_fp8_unpermute(self.q8, self.k8, self.v8, self.s8[0], self.s8[1], self.s8[2],
                                           self.off_q, self.off_k, self.sel_count, self.sel_idx, self.perm_q,
                                           scale=self.scale, out=dst, workspace=self.ws_attn)

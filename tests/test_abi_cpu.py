@@ -174,6 +174,27 @@ def test_kmeans_permute_validation(kw, code):
     assert _kmeans_perm(**kw) == code
 
 
+def _kmeans_perm8(**kw):
+    a = dict(x=FAKE, y=FAKE + 4096, bh=2, N=1000, d=128, n=8, it=3, init=None, cent=FAKE + 8192, lab=FAKE + 12288,
+             cnt=FAKE + 16384, xp=FAKE + 20480, xs=FAKE + 40960, yp=FAKE + 24576, ys=FAKE + 45056,
+             perm=FAKE + 28672, off=FAKE + 32768, ws=FAKE + 36864, wsn=1 << 30)
+    a.update(kw)
+    return B.lib().svg2_kmeans_permute_fp8(
+        a["x"], a["y"], a["bh"], a["N"], a["d"], a["n"], a["it"], a["init"], ctypes.c_uint64(7), a["cent"], a["lab"],
+        a["cnt"], a["xp"], a["xs"], a["yp"], a["ys"], a["perm"], a["off"], a["ws"], a["wsn"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(it=0), INVALID), (dict(xp=None), INVALID), (dict(xs=None), INVALID), (dict(xs=FAKE + 40962), INVALID),
+    (dict(y=None), INVALID), (dict(ys=None), INVALID), (dict(yp=None), INVALID),
+    (dict(y=None, yp=None), INVALID), (dict(y=None, ys=None), INVALID), (dict(xp=FAKE), INVALID),
+    (dict(yp=FAKE + 20480), INVALID), (dict(d=96), UNSUPPORTED), (dict(n=2000), INVALID), (dict(wsn=16), WORKSPACE),
+])
+def test_kmeans_permute_fp8_validation(kw, code):
+    """The E4M3 variant adds the scale outputs; y, y8_perm and y_scale go together."""
+    assert _kmeans_perm8(**kw) == code
+
+
 def test_unpermute_validation():
     L = B.lib()
     assert L.svg2_unpermute(None, 1, 1, 10, 128, FAKE, FAKE, 1, 1280, 0, 128, None) == INVALID

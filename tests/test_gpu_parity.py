@@ -339,6 +339,34 @@ def test_kmeans_permute_equals_kmeans_then_permute(dt, d, N, n, iters, warm, wit
             assert torch.equal(got["y_perm"][h].cpu(), v[h][idx])
 
 
+@pytest.mark.parametrize("d,N,n,iters,with_y", [(128, 5000, 40, 2, True), (128, 3001, 37, 1, False),
+                                               (64, 2000, 17, 2, True)])
+def test_kmeans_permute_fp8_equals_quantized_rows(d, N, n, iters, with_y):
+    """E4M3 rows stored by the last Lloyd round equal, byte for byte, the
+    quantization of the bf16 rows the same call gives without fp8, and the
+    scales are the quantization's; clusters, perm and offsets are unchanged."""
+    bh = 3
+    q, k, v = mixture(bh, N, d, comps=max(2, n // 2), seed=7 * N + n, dtype=torch.bfloat16)
+    # one all-zero problem of V: scale 1, zero bytes
+    v[1] = 0
+    xd, yd = k.to(DEV), v.to(DEV)
+    ref = B.kmeans_permute(xd, n, iters, y=yd if with_y else None, seed=9)
+    got = B.kmeans_permute(xd, n, iters, y=yd if with_y else None, seed=9, fp8=True)
+    torch.cuda.synchronize()
+    for key in ("centroids", "labels", "counts", "perm", "offsets"):
+        assert torch.equal(got[key], ref[key]), key
+    pairs = [("x_perm", "x_scale")] + ([("y_perm", "y_scale")] if with_y else [])
+    for rows, sc in pairs:
+        x8, s8 = B.quantize_fp8(ref[rows])
+        torch.cuda.synchronize()
+        assert got[rows].dtype == torch.uint8 and torch.equal(got[rows], x8), rows
+        assert torch.equal(got[sc], s8), sc
+    if with_y:
+        assert float(got["y_scale"][1]) == 1.0 and int(got["y_perm"][1].abs().sum()) == 0
+    else:
+        assert got["y_perm"] is None and got["y_scale"] is None
+
+
 @pytest.mark.parametrize("dt,d,N,n,heads", [("f32", 64, 4096, 64, 1), ("bf16", 128, 16384, 250, 2),
                                            ("bf16", 128, 3000, 100, 2), ("bf16", 64, 700, 700, 1)])
 def test_kmeanspp_picks_match_oracle(dt, d, N, n, heads):
