@@ -698,6 +698,28 @@ def main():
     # the stand-alone inverse permutation (the layer fuses it into the
     # attention's stores, where it costs no pass of its own)
     unpermute_ms = median_ms(layer.unpermute)
+    # the Lloyd round's kernels one side at a time (one stream, final labels):
+    # the update alone (counting sort + segmented mean) and a whole round
+    # (centroid halves + assignment + update); the assignment is the difference
+    lloyd_rows = {}
+    for side, x, n, lab, cent in (("q", q, cfg.n_q, layer.labels_q, layer.cq),
+                                  ("k", k, cfg.n_k, layer.labels_k, layer.ck)):
+        bhn_, N_, d_ = x.shape
+        means, cnt = torch.empty_like(cent), torch.empty(bhn_, n, dtype=torch.int32, device=x.device)
+        c_out, lab_out = torch.empty_like(cent), torch.empty_like(lab)
+        ws_m = torch.empty(B.lib().svg2_cluster_means_workspace_size(bhn_, N_, d_, n), dtype=torch.uint8,
+                           device=x.device)
+        ws_k = torch.empty(B.lib().svg2_kmeans_workspace_size(bhn_, N_, d_, n), dtype=torch.uint8, device=x.device)
+        upd = median_ms(lambda: B.cluster_means(x, lab, n, means=means, counts=cnt, workspace=ws_m))
+        rnd = median_ms(lambda: B.kmeans(x, n, 1, init=cent, centroids=c_out, labels=lab_out, counts=cnt,
+                                         workspace=ws_k))
+        e_ = x.element_size()
+        upd_bytes = bhn_ * (N_ * (d_ * e_ + 12.0) + n * d_ * 4.0)
+        asg_flops = 2.0 * bhn_ * N_ * n * d_
+        lloyd_rows[side] = {"update_ms": round(upd, 4), "update_gbps": round(upd_bytes / (upd * 1e-3) / 1e9, 1),
+                            "round_ms": round(rnd, 4), "assign_ms": round(rnd - upd, 4),
+                            "assign_tflops": round(asg_flops / ((rnd - upd) * 1e-3) / 1e12, 2)}
+    log(f"Lloyd kernels per side: {lloyd_rows}")
 
     dense_ms = rel_dense = None
     if not args.no_dense:
@@ -767,6 +789,10 @@ def main():
         "speedup_vs_dense_cold": round(dense_ms / cold_ms, 3) if dense_ms else None,
         "speedup_vs_dense_warm": round(dense_ms / warm_ms, 3) if dense_ms else None,
         "lloyd_round_distance_tflops": round(lloyd_flops / (ms_per_iter * 1e-3) / 1e12, 2) if ms_per_iter > 0 else None,
+        # per side on one stream: update = counting sort + segmented mean (HBM-bound,
+        # N (d e + 12) + n d 4 bytes per problem); assign = the rest of a round
+        # (centroid halves + distance contraction, 2 N n d flop per problem, twice that issued for bf16)
+        "lloyd_kernels_per_side": lloyd_rows,
         "select_share_of_dense": round(float(cold_stage[1]) / dense_ms, 5) if dense_ms else None,
         "rel_l2_sparse_vs_dense": round(rel_dense, 5) if rel_dense is not None else None,
         "padding_ratio_fixed128_blocks": round(pad_fixed128, 4),
