@@ -306,16 +306,6 @@ struct KeyCursor {
 // softmax; only the intermediate scaling differs.
 constexpr float kLazyTau = 8.f;
 
-// Work-groups are dispatched round-robin over the 8 XCDs (block b runs on XCD
-// b % 8).  Items are handed out in chunks of kXcdChunk consecutive items per
-// XCD, so the slabs of one Q-cluster (which read the same key list) share an
-// XCD and its L2, while all XCDs still advance through the same head at the
-// same time (its K/V stays in the last-level cache):
-//   block b -> item ((b / 8 / C) * 8 + b % 8) * C + (b / 8) % C,  C = kXcdChunk
-// which is a bijection on [0, grid) when grid is a multiple of 8 C.
-constexpr int kXcds = 8;
-constexpr int kXcdChunk = 4;
-
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -890,7 +880,7 @@ __global__ __launch_bounds__(256, 3) void k_attn_fp8(
     int N, const int32_t* __restrict__ q_off, int n_q,
     const int32_t* __restrict__ k_off, int n_k, const int32_t* __restrict__ sel_count,
     const int32_t* __restrict__ sel_idx, float scale_log2, uint16_t* __restrict__ O, float* __restrict__ lse,
-    OutMap om, const int32_t* __restrict__ item_count, const int32_t* __restrict__ items, int max_items, int bh) {
+    OutMap om, const int32_t* __restrict__ flat, int32_t* __restrict__ queue, size_t cap) {
   constexpr int BN = kAttnF8BN;
   constexpr int D = kAttnF8D;
   constexpr int ROW = D;                         // bytes per tile row
@@ -898,236 +888,257 @@ __global__ __launch_bounds__(256, 3) void k_attn_fp8(
   constexpr int kWaitAll = 0xF70;
   __shared__ __attribute__((aligned(16))) uint8_t sT0[2 * BN * ROW], sT1[2 * BN * ROW], sT2[2 * BN * ROW];
   __shared__ int s_rs[kRangeChunk], s_rl[kRangeChunk];
+  __shared__ int s_job[2];
 
-  const int total = max_items * bh;
-  const int jx = (int)(blockIdx.x / kXcds), xx = (int)(blockIdx.x % kXcds);
-  const int logical = ((jx / kXcdChunk) * kXcds + xx) * kXcdChunk + jx % kXcdChunk;
-  if (logical >= total) return;
-  const int p = logical / max_items, slot = logical % max_items;
-  if (slot >= item_count[p]) return;
-  const int item = items[(size_t)p * max_items + slot];
-  const int ci = item & 0xfff, rb = item >> 12;
-  const int32_t* qo = q_off + (size_t)p * (n_q + 1);
-  const int qa = clampi(qo[ci], 0, N), qb = clampi(qo[ci + 1], qa, N);
-  const int tid = threadIdx.x, lane = tid & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int col = lane & 31, half = lane >> 5;
-  const int row0 = qa + rb * kAttnBM + wave * 32;
-  const bool active = row0 < qb;
-  const int row = row0 + col;
-  const bool row_ok = row < qb;
-  const size_t base = (size_t)p * N * D;
-  const uint8_t* Kp = K + base;
-  const uint8_t* Vp = V + base;
-  const float sq = q_scale[p], sk = k_scale[p], sv = v_scale[p];
-  const float sl2 = scale_log2 * sq * sk;
+  // Work items come from the queue of the XCD this work-group runs on (hardware
+  // register XCC_ID), then, once it is empty, from the other XCDs' queues.
+  const int xcc = __builtin_amdgcn_s_getreg((3 << 11) | 20) & (kAttnXcds - 1);
+  for (int qx = 0; qx < kAttnXcds; ++qx) {
+    const int x = (xcc + qx) & (kAttnXcds - 1);
+    const int total_x = queue[kAttnXcds + x];
+    for (;;) {
+      __syncthreads();                               // the previous item is done with LDS
+      if (threadIdx.x == 0) {
+        const int j = atomicAdd(&queue[x], 1);
+        int pj = -1, ij = 0;
+        if (j < total_x) {
+          pj = flat[2 * ((size_t)x * cap + j)];
+          ij = flat[2 * ((size_t)x * cap + j) + 1];
+        }
+        s_job[0] = pj;
+        s_job[1] = ij;
+      }
+      __syncthreads();
+      const int p = s_job[0];
+      if (p < 0) break;
+      const int item = s_job[1];
+      const int ci = item & 0xfff, rb = item >> 12;
+      const int32_t* qo = q_off + (size_t)p * (n_q + 1);
+      const int qa = clampi(qo[ci], 0, N), qb = clampi(qo[ci + 1], qa, N);
+      const int tid = threadIdx.x, lane = tid & (kWave - 1);
+      const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+      const int col = lane & 31, half = lane >> 5;
+      const int row0 = qa + rb * kAttnBM + wave * 32;
+      const bool active = row0 < qb;
+      const int row = row0 + col;
+      const bool row_ok = row < qb;
+      const size_t base = (size_t)p * N * D;
+      const uint8_t* Kp = K + base;
+      const uint8_t* Vp = V + base;
+      const float sq = q_scale[p], sk = k_scale[p], sv = v_scale[p];
+      const float sl2 = scale_log2 * sq * sk;
 
-  // Q operand of S^T = K Q^T: lane (n, h) holds dims 64 kd + 32 h + 0..31 of query n
-  i32x8_t qf[2];
-#pragma unroll
-  for (int kd = 0; kd < 2; ++kd) {
-    u32x4_t a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-    if (row_ok) {
-      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(Q + base + (size_t)row * D + 64 * kd + 32 * half);
-      a = src[0];
-      b = src[1];
-    }
-    qf[kd] = (i32x8_t){(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
-  }
-
-  // this lane's tile rows for the direct-to-LDS loads: 16 rows per wave, 8 per load
-  int slot_of[2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) slot_of[q] = 16 * wave + 8 * q + lane / 8;
-  uint32_t l_off[2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) l_off[q] = (uint32_t)(((lane & 7) ^ f8_swz(slot_of[q])) * 16);
-
-  LdsCursor cur;
-  cur.init(sel_idx + ((size_t)p * n_q + ci) * n_k, k_off + (size_t)p * (n_k + 1),
-           clampi(sel_count[(size_t)p * n_q + ci], 0, n_k), n_k, N, s_rs, s_rl);
-
-  float m_ref = -__builtin_inff();
-  float l_part = 0.f;
-  f32x16_t o[4];
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
-
-  // K operand: lane (m, h) reads row 32 t + m, chunks 4 kd + 2 h + {0, 1}
-  const int fc = f8_swz(col);
-  uint32_t koff[2][2];
-#pragma unroll
-  for (int kd = 0; kd < 2; ++kd)
-#pragma unroll
-    for (int u = 0; u < 2; ++u) koff[kd][u] = (uint32_t)(col * ROW + ((4 * kd + 2 * half + u) ^ fc) * 16);
-  // V^T operand, read q of 4 (bytes 8 q .. 8 q + 7 of the lane's operand): the
-  // lane addresses row key(q, r, h) = 16 q + 8 (r / 4) + 4 h + r % 4, r = (lane % 16) / 2,
-  // dims 32 dt + 16 g + 8 s .. + 8, g = (lane / 16) % 2, s = lane % 2
-  const int vr = (lane & 15) >> 1, vs = lane & 1, vg = (lane >> 4) & 1;
-  const int vrow = 8 * (vr >> 2) + 4 * half + (vr & 3);
-  const int fv = f8_swz(vrow);
-  uint32_t voff[4];
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt) voff[dt] = (uint32_t)(vrow * ROW + ((2 * dt + vg) ^ fv) * 16 + 8 * vs);
-
-  auto step = [&](const uint8_t* kt, const uint8_t* vt, int filled) __attribute__((always_inline)) {
-    const __attribute__((address_space(3))) uint8_t* kb = (const __attribute__((address_space(3))) uint8_t*)(
-        const __attribute__((address_space(3))) void*)(const void*)kt;
-    const __attribute__((address_space(3))) uint8_t* vb = (const __attribute__((address_space(3))) uint8_t*)(
-        const __attribute__((address_space(3))) void*)(const void*)vt;
-    f32x16_t sc[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sc[t][i] = 0.f;
+      // Q operand of S^T = K Q^T: lane (n, h) holds dims 64 kd + 32 h + 0..31 of query n
+      i32x8_t qf[2];
 #pragma unroll
       for (int kd = 0; kd < 2; ++kd) {
-        const u32x4_t a0 = *(const lds_u32x4_t*)(kb + t * 32 * ROW + koff[kd][0]);
-        const u32x4_t a1 = *(const lds_u32x4_t*)(kb + t * 32 * ROW + koff[kd][1]);
-        const i32x8_t a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
-                           (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-        sc[t] = mfma_f8(a, qf[kd], sc[t]);
+        u32x4_t a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+        if (row_ok) {
+          const u32x4_t* src = reinterpret_cast<const u32x4_t*>(Q + base + (size_t)row * D + 64 * kd + 32 * half);
+          a = src[0];
+          b = src[1];
+        }
+        qf[kd] = (i32x8_t){(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
       }
-    }
-    if (filled < BN) {
-      const int lim = filled - 4 * half;
+
+      // this lane's tile rows for the direct-to-LDS loads: 16 rows per wave, 8 per load
+      int slot_of[2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int q = 0; q < 2; ++q) slot_of[q] = 16 * wave + 8 * q + lane / 8;
+      uint32_t l_off[2];
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (32 * t + (i >> 2) * 8 + (i & 3) >= lim) sc[t][i] = -__builtin_inff();
-    }
-    float mx = sc[0][0];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[t][i]);
-    {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sl2;
-    }
-    if (mx > m_ref + kLazyTau) {
-      const float alpha = __builtin_amdgcn_exp2f(m_ref - mx);
-      l_part *= alpha;
+      for (int q = 0; q < 2; ++q) l_off[q] = (uint32_t)(((lane & 7) ^ f8_swz(slot_of[q])) * 16);
+
+      LdsCursor cur;
+      cur.init(sel_idx + ((size_t)p * n_q + ci) * n_k, k_off + (size_t)p * (n_k + 1),
+               clampi(sel_count[(size_t)p * n_q + ci], 0, n_k), n_k, N, s_rs, s_rl);
+
+      float m_ref = -__builtin_inff();
+      float l_part = 0.f;
+      f32x16_t o[4];
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
-      m_ref = mx;
-    }
-    const float neg = -m_ref;
-    i32x8_t pf;
+        for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
+
+      // K operand: lane (m, h) reads row 32 t + m, chunks 4 kd + 2 h + {0, 1}
+      const int fc = f8_swz(col);
+      uint32_t koff[2][2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int kd = 0; kd < 2; ++kd)
 #pragma unroll
-      for (int i = 0; i < 16; i += 4) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[t][i], sl2, neg));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[t][i + 1], sl2, neg));
-        const float p2 = __builtin_amdgcn_exp2f(fmaf(sc[t][i + 2], sl2, neg));
-        const float p3 = __builtin_amdgcn_exp2f(fmaf(sc[t][i + 3], sl2, neg));
-        l_part += (p0 + p1) + (p2 + p3);
-        int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-        w = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
-        pf[4 * t + (i >> 2)] = w;
+        for (int u = 0; u < 2; ++u) koff[kd][u] = (uint32_t)(col * ROW + ((4 * kd + 2 * half + u) ^ fc) * 16);
+      // V^T operand, read q of 4 (bytes 8 q .. 8 q + 7 of the lane's operand): the
+      // lane addresses row key(q, r, h) = 16 q + 8 (r / 4) + 4 h + r % 4, r = (lane % 16) / 2,
+      // dims 32 dt + 16 g + 8 s .. + 8, g = (lane / 16) % 2, s = lane % 2
+      const int vr = (lane & 15) >> 1, vs = lane & 1, vg = (lane >> 4) & 1;
+      const int vrow = 8 * (vr >> 2) + 4 * half + (vr & 3);
+      const int fv = f8_swz(vrow);
+      uint32_t voff[4];
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) voff[dt] = (uint32_t)(vrow * ROW + ((2 * dt + vg) ^ fv) * 16 + 8 * vs);
+
+      auto step = [&](const uint8_t* kt, const uint8_t* vt, int filled) __attribute__((always_inline)) {
+        const __attribute__((address_space(3))) uint8_t* kb = (const __attribute__((address_space(3))) uint8_t*)(
+            const __attribute__((address_space(3))) void*)(const void*)kt;
+        const __attribute__((address_space(3))) uint8_t* vb = (const __attribute__((address_space(3))) uint8_t*)(
+            const __attribute__((address_space(3))) void*)(const void*)vt;
+        f32x16_t sc[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sc[t][i] = 0.f;
+#pragma unroll
+          for (int kd = 0; kd < 2; ++kd) {
+            const u32x4_t a0 = *(const lds_u32x4_t*)(kb + t * 32 * ROW + koff[kd][0]);
+            const u32x4_t a1 = *(const lds_u32x4_t*)(kb + t * 32 * ROW + koff[kd][1]);
+            const i32x8_t a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3],
+                               (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+            sc[t] = mfma_f8(a, qf[kd], sc[t]);
+          }
+        }
+        if (filled < BN) {
+          const int lim = filled - 4 * half;
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              if (32 * t + (i >> 2) * 8 + (i & 3) >= lim) sc[t][i] = -__builtin_inff();
+        }
+        float mx = sc[0][0];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[t][i]);
+        {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+          mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sl2;
+        }
+        if (mx > m_ref + kLazyTau) {
+          const float alpha = __builtin_amdgcn_exp2f(m_ref - mx);
+          l_part *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+          m_ref = mx;
+        }
+        const float neg = -m_ref;
+        i32x8_t pf;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; i += 4) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[t][i], sl2, neg));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[t][i + 1], sl2, neg));
+            const float p2 = __builtin_amdgcn_exp2f(fmaf(sc[t][i + 2], sl2, neg));
+            const float p3 = __builtin_amdgcn_exp2f(fmaf(sc[t][i + 3], sl2, neg));
+            l_part += (p0 + p1) + (p2 + p3);
+            int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+            w = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
+            pf[4 * t + (i >> 2)] = w;
+          }
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          i32x8_t a;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const i32x2_t r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(vb + q * 16 * ROW + voff[dt]));
+            a[2 * q] = r[0];
+            a[2 * q + 1] = r[1];
+          }
+          o[dt] = mfma_f8(a, pf, o[dt]);
+        }
+      };
+
+      uint8_t* k0 = sT0;
+      uint8_t* k1 = sT1;
+      uint8_t* k2 = sT2;
+      uint8_t* v0 = k0 + BN * ROW;
+      uint8_t* v1 = k1 + BN * ROW;
+      uint8_t* v2 = k2 + BN * ROW;
+      auto dma = [&](const uint8_t* src, uint8_t* dst, const int (&key)[2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const uint32_t off = (uint32_t)max(key[q], 0) * (uint32_t)ROW + l_off[q];
+          __builtin_amdgcn_global_load_lds((const void*)(src + off), (lds_void_t*)(void*)(dst + (16 * wave + 8 * q) * ROW),
+                                           16, 0, 0);
+        }
+      };
+
+      int key[2];
+      int f0 = cur.fill<2>(BN, slot_of, key);
+      if (f0 > 0) {
+        dma(Kp, k0, key);
+        dma(Vp, v0, key);
       }
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      i32x8_t a;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const i32x2_t r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(vb + q * 16 * ROW + voff[dt]));
-        a[2 * q] = r[0];
-        a[2 * q + 1] = r[1];
+      int f1 = f0 > 0 ? cur.fill<2>(BN, slot_of, key) : 0;
+      if (f1 > 0) {
+        dma(Kp, k1, key);
+        dma(Vp, v1, key);
+        __builtin_amdgcn_s_waitcnt(kWaitTile);
+      } else {
+        __builtin_amdgcn_s_waitcnt(kWaitAll);
       }
-      o[dt] = mfma_f8(a, pf, o[dt]);
-    }
-  };
+      lds_barrier();
 
-  uint8_t* k0 = sT0;
-  uint8_t* k1 = sT1;
-  uint8_t* k2 = sT2;
-  uint8_t* v0 = k0 + BN * ROW;
-  uint8_t* v1 = k1 + BN * ROW;
-  uint8_t* v2 = k2 + BN * ROW;
-  auto dma = [&](const uint8_t* src, uint8_t* dst, const int (&key)[2]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const uint32_t off = (uint32_t)max(key[q], 0) * (uint32_t)ROW + l_off[q];
-      __builtin_amdgcn_global_load_lds((const void*)(src + off), (lds_void_t*)(void*)(dst + (16 * wave + 8 * q) * ROW),
-                                       16, 0, 0);
-    }
-  };
-
-  int key[2];
-  int f0 = cur.fill<2>(BN, slot_of, key);
-  if (f0 > 0) {
-    dma(Kp, k0, key);
-    dma(Vp, v0, key);
-  }
-  int f1 = f0 > 0 ? cur.fill<2>(BN, slot_of, key) : 0;
-  if (f1 > 0) {
-    dma(Kp, k1, key);
-    dma(Vp, v1, key);
-    __builtin_amdgcn_s_waitcnt(kWaitTile);
-  } else {
-    __builtin_amdgcn_s_waitcnt(kWaitAll);
-  }
-  lds_barrier();
-
-  auto iter = [&](auto late, const uint8_t* kc, const uint8_t* vc, uint8_t* kd, uint8_t* vd)
-      __attribute__((always_inline)) -> bool {
-    int f2 = 0;
-    if (f1 > 0) {
-      f2 = cur.fill<2>(BN, slot_of, key);
-    } else {
-      key[0] = key[1] = -1;
-    }
-    if constexpr (!decltype(late)::value) {
-      dma(Kp, kd, key);
-      dma(Vp, vd, key);
-    }
-    if (active) step(kc, vc, f0);
-    if constexpr (decltype(late)::value) {
-      dma(Kp, kd, key);
-      dma(Vp, vd, key);
-    }
-    __builtin_amdgcn_s_waitcnt(kWaitTile);
-    lds_barrier();
-    f0 = f1;
-    f1 = f2;
-    return f0 > 0;
-  };
-  if (f0 > 0) {
-    constexpr std::true_type late{};
-    constexpr std::false_type early{};
-    while (iter(late, k0, v0, k2, v2) && iter(early, k1, v1, k0, v0) && iter(early, k2, v2, k1, v1)) {
-    }
-  }
-
-  float l_tot;
-  {
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part), __float_as_uint(l_part), false, false);
-    l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-  }
-  // output row: row itself, or token perm[row] through the destination's strides
-  const int tout = row_ok ? (om.perm ? om.perm[(size_t)p * N + row] : row) : -1;
-  if (row_ok && (unsigned)tout < (unsigned)N) {
-    const float inv = l_tot > 0.f ? sv / l_tot : 0.f;
-    uint16_t* orow = O + (p / om.heads) * om.bs + (p % om.heads) * om.hs + (int64_t)tout * om.ts;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        uint2 w;
-        w.x = pack_bf16x2(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv);
-        w.y = pack_bf16x2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv);
-        *reinterpret_cast<uint2*>(orow + dt * 32 + g * 8 + half * 4) = w;
+      auto iter = [&](auto late, const uint8_t* kc, const uint8_t* vc, uint8_t* kd, uint8_t* vd)
+          __attribute__((always_inline)) -> bool {
+        int f2 = 0;
+        if (f1 > 0) {
+          f2 = cur.fill<2>(BN, slot_of, key);
+        } else {
+          key[0] = key[1] = -1;
+        }
+        if constexpr (!decltype(late)::value) {
+          dma(Kp, kd, key);
+          dma(Vp, vd, key);
+        }
+        if (active) step(kc, vc, f0);
+        if constexpr (decltype(late)::value) {
+          dma(Kp, kd, key);
+          dma(Vp, vd, key);
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitTile);
+        lds_barrier();
+        f0 = f1;
+        f1 = f2;
+        return f0 > 0;
+      };
+      if (f0 > 0) {
+        constexpr std::true_type late{};
+        constexpr std::false_type early{};
+        while (iter(late, k0, v0, k2, v2) && iter(early, k1, v1, k0, v0) && iter(early, k2, v2, k1, v1)) {
+        }
       }
-    if (lse && half == 0)
-      lse[(size_t)p * N + tout] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * 0.69314718055994531f
-                                             : -__builtin_inff();
+      // the last iterations' loads (of key row 0 past the list's end) must land
+      // before the next item's loads reuse the ring
+      __builtin_amdgcn_s_waitcnt(kWaitAll);
+
+      float l_tot;
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part), __float_as_uint(l_part), false, false);
+        l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      }
+      // output row: row itself, or token perm[row] through the destination's strides
+      const int tout = row_ok ? (om.perm ? om.perm[(size_t)p * N + row] : row) : -1;
+      if (row_ok && (unsigned)tout < (unsigned)N) {
+        const float inv = l_tot > 0.f ? sv / l_tot : 0.f;
+        uint16_t* orow = O + (p / om.heads) * om.bs + (p % om.heads) * om.hs + (int64_t)tout * om.ts;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            uint2 w;
+            w.x = pack_bf16x2(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv);
+            w.y = pack_bf16x2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv);
+            *reinterpret_cast<uint2*>(orow + dt * 32 + g * 8 + half * 4) = w;
+          }
+        if (lse && half == 0)
+          lse[(size_t)p * N + tout] = l_tot > 0.f ? (m_ref + __log2f(l_tot)) * 0.69314718055994531f
+                                                 : -__builtin_inff();
+      }
+    }
   }
 }
 
@@ -1265,20 +1276,17 @@ hipError_t launch_varblock_attn_fp8(const void* q, const void* k, const void* v,
                                     const int32_t* sel_count, const int32_t* sel_idx, float scale, void* out,
                                     float* lse, const OutMap& om, const AttnWs& ws, hipStream_t s) {
   const int max_items = attn_max_items(N, n_q, kAttnBM);
-  int32_t* tiles_ws = ws.tiles;
-  int32_t* item_count_ws = ws.item_count;
-  int32_t* items_ws = ws.items;
   hipLaunchKernelGGL(k_attn_lengths, dim3((n_q + 3) / 4, bh), dim3(256), 0, s, k_off, n_k, N, sel_count, sel_idx,
-                     n_q, kAttnF8BN, tiles_ws);
-  hipLaunchKernelGGL(k_attn_plan, dim3(bh), dim3(1024), 0, s, q_off, n_q, N, kAttnBM, max_items, tiles_ws,
-                     item_count_ws, items_ws);
-  const int total = max_items * bh;
-  constexpr int span = kXcds * kXcdChunk;
-  hipLaunchKernelGGL(k_attn_fp8, dim3((total + span - 1) / span * span), dim3(256), 0, s,
+                     n_q, kAttnF8BN, ws.tiles);
+  hipLaunchKernelGGL(k_attn_plan_xcd, dim3(bh), dim3(1024), 0, s, q_off, n_q, N, kAttnBM, max_items, ws.tiles,
+                     ws.xcount, ws.xitems);
+  hipLaunchKernelGGL(k_attn_flatten, dim3(kAttnXcds), dim3(256), 0, s, ws.xcount, ws.xitems, bh, max_items,
+                     ws.flat, ws.queue);
+  const size_t cap = (size_t)bh * max_items;
+  hipLaunchKernelGGL(k_attn_fp8, dim3(attn_persistent_grid()), dim3(256), 0, s,
                      static_cast<const uint8_t*>(q), static_cast<const uint8_t*>(k), static_cast<const uint8_t*>(v),
                      q_scale, k_scale, v_scale, N, q_off, n_q, k_off, n_k, sel_count, sel_idx,
-                     scale * 1.4426950408889634f, static_cast<uint16_t*>(out), lse, om, item_count_ws, items_ws,
-                     max_items, bh);
+                     scale * 1.4426950408889634f, static_cast<uint16_t*>(out), lse, om, ws.flat, ws.queue, cap);
   return hipGetLastError();
 }
 
