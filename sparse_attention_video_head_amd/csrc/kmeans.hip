@@ -798,7 +798,7 @@ __global__ __launch_bounds__(256) void k_centroid_partial(const T* __restrict__ 
   constexpr int EPV = 16 / sizeof(T);          // elements per 16-byte vector
   constexpr int VPR = D / EPV;                 // lanes per row
   constexpr int G = 256 / VPR;                 // row groups
-  constexpr int U = 4;                         // rows in flight per lane
+  constexpr int U = MOVE ? 8 : 4;              // rows in flight per lane (more when moving rows)
   __shared__ double red[G][D];
   __shared__ int32_t s_perm[kMeanChunk];
   __shared__ int s_c0;
