@@ -40,7 +40,7 @@
  *     on entry does not matter and on exit is unspecified.
  *   - Results are bitwise reproducible run to run (no floating-point atomics).
  *   - Supported: head_dim 64 or 128; dtype fp32 or bf16; 1 <= n_clusters <=
- *     min(n_tokens, 4096); 1 <= n_tokens <= 2^24.
+ *     min(n_tokens, 4096); 1 <= n_tokens < 2^24.
  */
 #ifndef SVG2_H
 #define SVG2_H

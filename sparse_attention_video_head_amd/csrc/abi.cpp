@@ -14,7 +14,9 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
-constexpr int kMaxTokens = 1 << 24;
+// below 2^24 so that one head's rows at d = 128 (N x 256 bytes) stay under the
+// 4 GiB a buffer resource's 32-bit record count covers
+constexpr int kMaxTokens = (1 << 24) - 1;
 constexpr size_t kAlign = 256;
 
 int hip_status(hipError_t e) {

@@ -654,7 +654,7 @@ __global__ __launch_bounds__(256, 3) void k_attn_bf16(
       auto load_tile = [&](int s, int first, const int (&key)[INS]) __attribute__((always_inline)) {
         const uint32_t kdst = lds0 + (uint32_t)(s * SLOT + 8 * wave * ROWB);
         if (first >= 0) {
-          const uint32_t so = (uint32_t)__builtin_amdgcn_readfirstlane(first * ROWB);   // uniform by construction
+          const uint32_t so = (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)first * ROWB));   // uniform
 #pragma unroll
           for (int q = 0; q < INS; ++q) {
             lds_dma16(Kr, kdst + (uint32_t)(RPI * q * ROWB), krun[q], so);

@@ -72,6 +72,16 @@ def test_kmeans_size_queries():
     assert L.svg2_kmeans_workspace_size(24, 118800, 128, 1000) > 24 * 118800 * 8
 
 
+def test_token_limit_below_2_pow_24():
+    """n_tokens < 2^24: one head's rows at d = 128 then stay under the 4 GiB a
+    buffer resource addresses."""
+    L = B.lib()
+    assert L.svg2_kmeans_workspace_size(1, (1 << 24) - 1, 128, 8) > 0
+    assert L.svg2_kmeans_workspace_size(1, 1 << 24, 128, 8) == 0
+    assert L.svg2_varblock_attn_workspace_size(1, (1 << 24) - 1, 8, 8, 128) > 0
+    assert L.svg2_varblock_attn_workspace_size(1, 1 << 24, 8, 8, 128) == 0
+
+
 def _perm(**kw):
     a = dict(lab=FAKE, bh=4, N=500, n=8, nt=1, src=[FAKE], heads=1, sb=500 * 128, sh=0, st=128, dst=[FAKE],
              dtype=1, d=128, perm=FAKE, off=FAKE, ws=FAKE, wsn=1 << 30)
