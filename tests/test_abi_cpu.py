@@ -220,6 +220,14 @@ def test_binding_refuses_cpu_tensors():
         B.kmeans(torch.zeros(1, 8, 64), 2, 1)
     with pytest.raises(B.Svg2Error):
         B.unpermute(torch.zeros(1, 8, 64), torch.zeros(1, 8, dtype=torch.int32))
+    with pytest.raises(B.Svg2Error):
+        B.kmeans_permute(torch.zeros(1, 8, 64), 2, 1, y=torch.zeros(1, 8, 64))
+    with pytest.raises(B.Svg2Error):
+        z8 = torch.zeros(1, 8, 128, dtype=torch.uint8)
+        s1 = torch.ones(1)
+        i1 = torch.zeros(1, 2, dtype=torch.int32)
+        B.varblock_attn_fp8_unpermute(z8, z8, z8, s1, s1, s1, i1, i1, torch.ones(1, 1, dtype=torch.int32),
+                                      torch.zeros(1, 1, 1, dtype=torch.int32), torch.zeros(1, 8, dtype=torch.int32))
 
 
 def _means(**kw):
