@@ -551,9 +551,12 @@ FP8_TOL_DEQ = (5e-2, 4e-2)        # max-abs, rel-L2 against the oracle on the de
 FP8_TOL_RAW = 1e-1                # rel-L2 against the oracle on the bf16 inputs
 
 
-def test_varblock_attn_fp8_vs_oracle():
-    bh, N, n_q, n_k = 2, 3000, 20, 50
-    q, k, v, qo, ko, cnt, idx, lists, qo_np, ko_np = _attn_case("bf16", 128, bh, N, n_q, n_k, 0.9, seed=91,
+@pytest.mark.parametrize("N,n_q,n_k", [(3000, 20, 50), (6000, 1500, 200), (4099, 7, 130)])
+def test_varblock_attn_fp8_vs_oracle(N, n_q, n_k):
+    """Including many Q-clusters (the per-XCD plan over more than 1024 clusters)
+    and a ragged token count."""
+    bh = 2
+    q, k, v, qo, ko, cnt, idx, lists, qo_np, ko_np = _attn_case("bf16", 128, bh, N, n_q, n_k, 0.9, seed=91 + n_q,
                                                                empty_rows=True)
     q8, sq = B.quantize_fp8(q.to(DEV))
     k8, sk = B.quantize_fp8(k.to(DEV))
