@@ -144,12 +144,66 @@ def _need_cuda(*ts):
             raise Svg2Error("svg2 operates on GPU tensors only")
 
 
+def _same_device(dev: torch.device, *ts):
+    """Every given tensor lives on ``dev``, the device of the call's first
+    input (which _need_cuda has already required to be a GPU)."""
+    for t in ts:
+        if t is not None and t.device != dev:
+            raise Svg2Error(f"every tensor of one call must be on {dev} (got {t.device})")
+
+
+def _need_out(t: Optional[torch.Tensor], shape, dtype: torch.dtype, dev: torch.device, what: str):
+    """A caller-supplied output or in/out buffer: on ``dev``, of ``dtype``, of
+    exactly ``shape`` and contiguous, since the kernels write through its raw
+    pointer at that size."""
+    if t is None:
+        return
+    _same_device(dev, t)
+    if t.dtype != dtype:
+        raise Svg2Error(f"{what} must be {dtype} (got {t.dtype})")
+    if tuple(t.shape) != tuple(shape):
+        raise Svg2Error(f"{what} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise Svg2Error(f"{what} must be contiguous")
+
+
 def _workspace(nbytes: int, dev, workspace: Optional[torch.Tensor]):
+    """The caller's workspace (on ``dev``, contiguous, at least ``nbytes``) or
+    a new one when none is given."""
     if nbytes == 0:
         return None
-    if workspace is not None and workspace.numel() * workspace.element_size() >= nbytes:
-        return workspace
-    return torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    if workspace is None:
+        return torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _same_device(dev, workspace)
+    if not workspace.is_contiguous():
+        raise Svg2Error("the workspace must be contiguous")
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise Svg2Error(f"the workspace holds {workspace.numel() * workspace.element_size()} bytes, "
+                        f"{nbytes} are needed")
+    return workspace
+
+
+def _lists(bh: int, dev: torch.device, q_offsets, k_offsets, sel_count, sel_idx):
+    """Checks the attention's cluster offsets and selection lists against bh
+    problems; returns (n_q, n_k)."""
+    for t, name in ((q_offsets, "q_offsets"), (k_offsets, "k_offsets")):
+        if t.dim() != 2 or t.shape[0] != bh or t.shape[1] < 2:
+            raise Svg2Error(f"{name} must be [bh, n + 1] with bh = {bh} and n >= 1")
+    n_q = q_offsets.shape[1] - 1
+    n_k = k_offsets.shape[1] - 1
+    _need_out(q_offsets, (bh, n_q + 1), torch.int32, dev, "q_offsets")
+    _need_out(k_offsets, (bh, n_k + 1), torch.int32, dev, "k_offsets")
+    _need_out(sel_count, (bh, n_q), torch.int32, dev, "sel_count")
+    _need_out(sel_idx, (bh, n_q, n_k), torch.int32, dev, "sel_idx")
+    return n_q, n_k
+
+
+def _lse_buffer(lse, bh: int, N: int, dev: torch.device):
+    """``lse`` is a flag (allocate or not) or the caller's fp32 [bh, N] tensor."""
+    if isinstance(lse, torch.Tensor):
+        _need_out(lse, (bh, N), torch.float32, dev, "lse")
+        return lse
+    return torch.empty(bh, N, dtype=torch.float32, device=dev) if lse else None
 
 
 # ---------------------------------------------------------------- kmeans
@@ -164,11 +218,12 @@ def kmeans(x: torch.Tensor, n_clusters: int, n_iters: int, init: Optional[torch.
         raise Svg2Error("x must be a contiguous [bh, N, d] tensor")
     bh, N, d = x.shape
     dev = x.device
+    _need_out(init, (bh, n_clusters, d), torch.float32, dev, "init")
+    _need_out(centroids, (bh, n_clusters, d), torch.float32, dev, "centroids")
+    _need_out(labels, (bh, N), torch.int32, dev, "labels")
+    _need_out(counts, (bh, n_clusters), torch.int32, dev, "counts")
     if centroids is None:
         centroids = torch.empty(bh, n_clusters, d, dtype=torch.float32, device=dev)
-    if init is not None and (init.dtype != torch.float32 or not init.is_contiguous()
-                             or tuple(init.shape) != (bh, n_clusters, d)):
-        raise Svg2Error("init must be a contiguous fp32 [bh, n_clusters, d] tensor")
     if labels is None and n_iters > 0:
         labels = torch.empty(bh, N, dtype=torch.int32, device=dev)
     if counts is None and n_iters > 0:
@@ -202,11 +257,13 @@ def kmeans_permute(x: torch.Tensor, n_clusters: int, n_iters: int, y: Optional[t
         raise Svg2Error("x must be a contiguous [bh, N, d] tensor")
     bh, N, d = x.shape
     dev = x.device
-    if y is not None and (y.shape != x.shape or y.dtype != x.dtype or not y.is_contiguous()):
-        raise Svg2Error("y must be a contiguous tensor of x's shape and dtype")
-    if init is not None and (init.dtype != torch.float32 or not init.is_contiguous()
-                             or tuple(init.shape) != (bh, n_clusters, d)):
-        raise Svg2Error("init must be a contiguous fp32 [bh, n_clusters, d] tensor")
+    _need_out(y, x.shape, x.dtype, dev, "y")
+    _need_out(init, (bh, n_clusters, d), torch.float32, dev, "init")
+    _need_out(centroids, (bh, n_clusters, d), torch.float32, dev, "centroids")
+    _need_out(labels, (bh, N), torch.int32, dev, "labels")
+    _need_out(counts, (bh, n_clusters), torch.int32, dev, "counts")
+    _need_out(perm, (bh, N), torch.int32, dev, "perm")
+    _need_out(offsets, (bh, n_clusters + 1), torch.int32, dev, "offsets")
     e = lambda *sh, dt=torch.int32: torch.empty(*sh, dtype=dt, device=dev)
     centroids = e(bh, n_clusters, d, dt=torch.float32) if centroids is None else centroids
     labels = e(bh, N) if labels is None else labels
@@ -217,9 +274,8 @@ def kmeans_permute(x: torch.Tensor, n_clusters: int, n_iters: int, y: Optional[t
     x_out = torch.empty(x.shape, dtype=odt, device=dev) if x_out is None else x_out
     if y is not None and y_out is None:
         y_out = torch.empty(x.shape, dtype=odt, device=dev)
-    for o in (x_out, y_out):
-        if o is not None and (o.shape != x.shape or o.dtype != odt or not o.is_contiguous()):
-            raise Svg2Error("permuted outputs must be contiguous tensors of x's shape (uint8 for fp8)")
+    _need_out(x_out, x.shape, odt, dev, "x_out")
+    _need_out(y_out, x.shape, odt, dev, "y_out")
     perm = e(bh, N) if perm is None else perm
     offsets = e(bh, n_clusters + 1) if offsets is None else offsets
     L = lib()
@@ -229,9 +285,8 @@ def kmeans_permute(x: torch.Tensor, n_clusters: int, n_iters: int, y: Optional[t
         x_scale = e(bh, dt=torch.float32) if x_scale is None else x_scale
         if y is not None and y_scale is None:
             y_scale = e(bh, dt=torch.float32)
-        for t in (x_scale, y_scale):
-            if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (bh,) or not t.is_contiguous()):
-                raise Svg2Error("scales must be contiguous fp32 [bh]")
+        _need_out(x_scale, (bh,), torch.float32, dev, "x_scale")
+        _need_out(y_scale, (bh,), torch.float32, dev, "y_scale")
         st = L.svg2_kmeans_permute_fp8(_ptr(x), _ptr(y), bh, N, d, n_clusters, n_iters, _ptr(init),
                                        ctypes.c_uint64(seed & ((1 << 64) - 1)), _ptr(centroids), _ptr(labels),
                                        _ptr(counts), _ptr(x_out), _ptr(x_scale), _ptr(y_out),
@@ -279,11 +334,15 @@ def permute(labels: torch.Tensor, n_clusters: int, *tensors: torch.Tensor,
     if labels.dtype != torch.int32 or not labels.is_contiguous() or tuple(labels.shape) != (bh, N):
         raise Svg2Error("labels must be contiguous int32 [bh, N]")
     dev = labels.device
+    _same_device(dev, *tensors)
     if outs is None:
         outs = [torch.empty(bh, N, d, dtype=tensors[0].dtype, device=dev) for _ in tensors]
+    if len(outs) != len(tensors):
+        raise Svg2Error("one output per permuted tensor")
     for o in outs:
-        if tuple(o.shape) != (bh, N, d) or not o.is_contiguous() or o.dtype != tensors[0].dtype:
-            raise Svg2Error("permute outputs must be contiguous [bh, N, d] of the input dtype")
+        _need_out(o, (bh, N, d), tensors[0].dtype, dev, "permute output")
+    _need_out(perm, (bh, N), torch.int32, dev, "perm")
+    _need_out(offsets, (bh, n_clusters + 1), torch.int32, dev, "offsets")
     if perm is None:
         perm = torch.empty(bh, N, dtype=torch.int32, device=dev)
     if offsets is None:
@@ -308,6 +367,8 @@ def select_topp(q_centroids: torch.Tensor, q_counts: torch.Tensor, k_centroids: 
     """Top-p K-cluster selection per Q-cluster.  Returns dict(sel_count [bh,n_q],
     sel_idx [bh,n_q,n_k], probs, pair_count [bh] int64)."""
     _need_cuda(q_centroids, q_counts, k_centroids, k_counts)
+    if q_centroids.dim() != 3 or k_centroids.dim() != 3:
+        raise Svg2Error("centroids must be [bh, n, d] tensors")
     bh, n_q, d = q_centroids.shape
     n_k = k_centroids.shape[1]
     for t, dt in ((q_centroids, torch.float32), (k_centroids, torch.float32), (q_counts, torch.int32),
@@ -317,6 +378,12 @@ def select_topp(q_centroids: torch.Tensor, q_counts: torch.Tensor, k_centroids: 
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dev = q_centroids.device
+    _need_out(q_counts, (bh, n_q), torch.int32, dev, "q_counts")
+    _need_out(k_centroids, (bh, n_k, d), torch.float32, dev, "k_centroids")
+    _need_out(k_counts, (bh, n_k), torch.int32, dev, "k_counts")
+    _need_out(sel_count, (bh, n_q), torch.int32, dev, "sel_count")
+    _need_out(sel_idx, (bh, n_q, n_k), torch.int32, dev, "sel_idx")
+    _need_out(pair_count, (bh,), torch.int64, dev, "pair_count")
     if sel_count is None:
         sel_count = torch.empty(bh, n_q, dtype=torch.int32, device=dev)
     if sel_idx is None:
@@ -342,29 +409,19 @@ def varblock_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_offsets: 
     tensors.  Returns (out [bh,N,d], lse [bh,N] fp32 or None); ``lse`` is a
     flag or a contiguous fp32 [bh, N] tensor to write it into."""
     _need_cuda(q, k, v, q_offsets, k_offsets, sel_count, sel_idx)
-    for t in (q, k, v):
-        if t.dim() != 3 or not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype:
-            raise Svg2Error("q, k, v must be contiguous [bh, N, d] tensors of one dtype")
+    if q.dim() != 3:
+        raise Svg2Error("q, k, v must be contiguous [bh, N, d] tensors of one dtype")
     bh, N, d = q.shape
-    n_q = q_offsets.shape[1] - 1
-    n_k = k_offsets.shape[1] - 1
-    for t in (q_offsets, k_offsets, sel_count, sel_idx):
-        if t.dtype != torch.int32 or not t.is_contiguous():
-            raise Svg2Error("offsets and lists must be contiguous int32")
-    if tuple(sel_count.shape) != (bh, n_q) or tuple(sel_idx.shape) != (bh, n_q, n_k):
-        raise Svg2Error("sel_count [bh, n_q] and sel_idx [bh, n_q, n_k] expected")
+    dev = q.device
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need_out(t, q.shape, q.dtype, dev, name)
+    n_q, n_k = _lists(bh, dev, q_offsets, k_offsets, sel_count, sel_idx)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    dev = q.device
+    _need_out(out, q.shape, q.dtype, dev, "out")
     if out is None:
         out = torch.empty_like(q)
-    if isinstance(lse, torch.Tensor):
-        if lse.dtype != torch.float32 or tuple(lse.shape) != (bh, N) or not lse.is_contiguous():
-            raise Svg2Error("lse must be a contiguous fp32 [bh, N] tensor")
-        _need_cuda(lse)
-        ls = lse
-    else:
-        ls = torch.empty(bh, N, dtype=torch.float32, device=dev) if lse else None
+    ls = _lse_buffer(lse, bh, N, dev)
     L = lib()
     ws_n = L.svg2_varblock_attn_workspace_size(bh, N, n_q, n_k, d)
     ws = _workspace(ws_n, dev, workspace)
@@ -384,34 +441,23 @@ def varblock_attn_unpermute(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q
     a strided [bh,N,d] or [B,H,N,d] view (default: new contiguous tensor);
     ``lse`` (flag or fp32 [bh, N] tensor) is in the original order too."""
     _need_cuda(q, k, v, q_offsets, k_offsets, sel_count, sel_idx, perm, out)
-    for t in (q, k, v):
-        if t.dim() != 3 or not t.is_contiguous() or t.shape != q.shape or t.dtype != q.dtype:
-            raise Svg2Error("q, k, v must be contiguous [bh, N, d] tensors of one dtype")
+    if q.dim() != 3:
+        raise Svg2Error("q, k, v must be contiguous [bh, N, d] tensors of one dtype")
     bh, N, d = q.shape
-    n_q = q_offsets.shape[1] - 1
-    n_k = k_offsets.shape[1] - 1
-    for t in (q_offsets, k_offsets, sel_count, sel_idx, perm):
-        if t.dtype != torch.int32 or not t.is_contiguous():
-            raise Svg2Error("offsets, lists and perm must be contiguous int32")
-    if tuple(sel_count.shape) != (bh, n_q) or tuple(sel_idx.shape) != (bh, n_q, n_k):
-        raise Svg2Error("sel_count [bh, n_q] and sel_idx [bh, n_q, n_k] expected")
-    if tuple(perm.shape) != (bh, N):
-        raise Svg2Error("perm must be [bh, N]")
+    dev = q.device
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need_out(t, q.shape, q.dtype, dev, name)
+    n_q, n_k = _lists(bh, dev, q_offsets, k_offsets, sel_count, sel_idx)
+    _need_out(perm, (bh, N), torch.int32, dev, "perm")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    dev = q.device
     if out is None:
         out = torch.empty_like(q)
+    _same_device(dev, out)
     obh, oN, od, heads, sb, sh, st = _strided_view(out)
     if (obh, oN, od) != (bh, N, d) or out.dtype != q.dtype:
         raise Svg2Error("out does not match q")
-    if isinstance(lse, torch.Tensor):
-        if lse.dtype != torch.float32 or tuple(lse.shape) != (bh, N) or not lse.is_contiguous():
-            raise Svg2Error("lse must be a contiguous fp32 [bh, N] tensor")
-        _need_cuda(lse)
-        ls = lse
-    else:
-        ls = torch.empty(bh, N, dtype=torch.float32, device=dev) if lse else None
+    ls = _lse_buffer(lse, bh, N, dev)
     L = lib()
     ws_n = L.svg2_varblock_attn_workspace_size(bh, N, n_q, n_k, d)
     ws = _workspace(ws_n, dev, workspace)
@@ -433,8 +479,10 @@ def unpermute(src: torch.Tensor, perm: torch.Tensor, out: Optional[torch.Tensor]
     bh, N, d = src.shape
     if perm.dtype != torch.int32 or not perm.is_contiguous() or tuple(perm.shape) != (bh, N):
         raise Svg2Error("perm must be contiguous int32 [bh, N]")
+    _same_device(src.device, perm)
     if out is None:
         out = torch.empty_like(src)
+    _same_device(src.device, out)
     obh, oN, od, heads, sb, sh, st = _strided_view(out)
     if (obh, oN, od) != (bh, N, d) or out.dtype != src.dtype:
         raise Svg2Error("out does not match src")
@@ -457,13 +505,13 @@ def cluster_means(x: torch.Tensor, labels: torch.Tensor, n_clusters: int, means:
     if labels.dtype != torch.int32 or tuple(labels.shape) != (bh, N) or not labels.is_contiguous():
         raise Svg2Error("labels must be contiguous int32 [bh, N]")
     dev = x.device
+    _same_device(dev, labels)
+    _need_out(means, (bh, n_clusters, d), torch.float32, dev, "means")
+    _need_out(counts, (bh, n_clusters), torch.int32, dev, "counts")
     if means is None:
         means = torch.zeros(bh, n_clusters, d, dtype=torch.float32, device=dev)
     if counts is None:
         counts = torch.empty(bh, n_clusters, dtype=torch.int32, device=dev)
-    if (tuple(means.shape) != (bh, n_clusters, d) or means.dtype != torch.float32 or not means.is_contiguous()
-            or tuple(counts.shape) != (bh, n_clusters) or counts.dtype != torch.int32 or not counts.is_contiguous()):
-        raise Svg2Error("means [bh, n, d] fp32 and counts [bh, n] int32, contiguous, expected")
     L = lib()
     ws_n = L.svg2_cluster_means_workspace_size(bh, N, d, n_clusters)
     ws = _workspace(ws_n, dev, workspace)
@@ -481,6 +529,8 @@ def recall_mass(lse_sel: torch.Tensor, lse_all: torch.Tensor, out: Optional[torc
         if t.dtype != torch.float32 or t.dim() != 2 or not t.is_contiguous() or t.shape != lse_sel.shape:
             raise Svg2Error("lse_sel and lse_all must be contiguous fp32 [bh, N] tensors of one shape")
     bh, N = lse_sel.shape
+    _same_device(lse_sel.device, lse_all)
+    _need_out(out, (bh,), torch.float64, lse_sel.device, "out")
     if out is None:
         out = torch.empty(bh, dtype=torch.float64, device=lse_sel.device)
     L = lib()
@@ -499,13 +549,12 @@ def quantize_fp8(x: torch.Tensor, x8: Optional[torch.Tensor] = None, scale: Opti
         raise Svg2Error("x must be a contiguous bf16 [bh, N, d] tensor")
     bh, N, d = x.shape
     dev = x.device
+    _need_out(x8, (bh, N, d), torch.uint8, dev, "x8")
+    _need_out(scale, (bh,), torch.float32, dev, "scale")
     if x8 is None:
         x8 = torch.empty(bh, N, d, dtype=torch.uint8, device=dev)
     if scale is None:
         scale = torch.empty(bh, dtype=torch.float32, device=dev)
-    if (tuple(x8.shape) != (bh, N, d) or x8.dtype != torch.uint8 or not x8.is_contiguous()
-            or tuple(scale.shape) != (bh,) or scale.dtype != torch.float32):
-        raise Svg2Error("x8 uint8 [bh, N, d] and scale fp32 [bh], contiguous, expected")
     L = lib()
     ws_n = L.svg2_quantize_fp8_workspace_size(bh)
     ws = _workspace(ws_n, dev, workspace)
@@ -521,24 +570,21 @@ def varblock_attn_fp8(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Tensor, q_sc
     """svg2_varblock_attn on E4M3 inputs (uint8 [bh, N, 128] with [bh] fp32
     scales).  Returns (out bf16 [bh, N, 128], lse or None)."""
     _need_cuda(q8, k8, v8, q_scale, k_scale, v_scale, q_offsets, k_offsets, sel_count, sel_idx)
-    for t in (q8, k8, v8):
-        if t.dim() != 3 or not t.is_contiguous() or t.shape != q8.shape or t.dtype != torch.uint8:
-            raise Svg2Error("q8, k8, v8 must be contiguous uint8 [bh, N, d] tensors of one shape")
+    if q8.dim() != 3:
+        raise Svg2Error("q8, k8, v8 must be contiguous uint8 [bh, N, d] tensors of one shape")
     bh, N, d = q8.shape
-    for t in (q_scale, k_scale, v_scale):
-        if t.dtype != torch.float32 or tuple(t.shape) != (bh,) or not t.is_contiguous():
-            raise Svg2Error("scales must be contiguous fp32 [bh]")
-    n_q = q_offsets.shape[1] - 1
-    n_k = k_offsets.shape[1] - 1
+    dev = q8.device
+    for t, name in ((q8, "q8"), (k8, "k8"), (v8, "v8")):
+        _need_out(t, q8.shape, torch.uint8, dev, name)
+    for t, name in ((q_scale, "q_scale"), (k_scale, "k_scale"), (v_scale, "v_scale")):
+        _need_out(t, (bh,), torch.float32, dev, name)
+    n_q, n_k = _lists(bh, dev, q_offsets, k_offsets, sel_count, sel_idx)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    dev = q8.device
+    _need_out(out, (bh, N, d), torch.bfloat16, dev, "out")
     if out is None:
         out = torch.empty(bh, N, d, dtype=torch.bfloat16, device=dev)
-    if isinstance(lse, torch.Tensor):
-        ls = lse
-    else:
-        ls = torch.empty(bh, N, dtype=torch.float32, device=dev) if lse else None
+    ls = _lse_buffer(lse, bh, N, dev)
     L = lib()
     ws_n = L.svg2_varblock_attn_workspace_size(bh, N, n_q, n_k, d)
     ws = _workspace(ws_n, dev, workspace)
@@ -558,31 +604,25 @@ def varblock_attn_fp8_unpermute(q8: torch.Tensor, k8: torch.Tensor, v8: torch.Te
     out row perm[i] = attention output row i.  ``out`` is a bf16 [bh,N,d] or
     [B,H,N,d] view; ``lse`` (flag or fp32 [bh, N] tensor) in the original order."""
     _need_cuda(q8, k8, v8, q_scale, k_scale, v_scale, q_offsets, k_offsets, sel_count, sel_idx, perm, out)
-    for t in (q8, k8, v8):
-        if t.dim() != 3 or not t.is_contiguous() or t.shape != q8.shape or t.dtype != torch.uint8:
-            raise Svg2Error("q8, k8, v8 must be contiguous uint8 [bh, N, d] tensors of one shape")
+    if q8.dim() != 3:
+        raise Svg2Error("q8, k8, v8 must be contiguous uint8 [bh, N, d] tensors of one shape")
     bh, N, d = q8.shape
-    for t in (q_scale, k_scale, v_scale):
-        if t.dtype != torch.float32 or tuple(t.shape) != (bh,) or not t.is_contiguous():
-            raise Svg2Error("scales must be contiguous fp32 [bh]")
-    if perm.dtype != torch.int32 or not perm.is_contiguous() or tuple(perm.shape) != (bh, N):
-        raise Svg2Error("perm must be contiguous int32 [bh, N]")
-    n_q = q_offsets.shape[1] - 1
-    n_k = k_offsets.shape[1] - 1
+    dev = q8.device
+    for t, name in ((q8, "q8"), (k8, "k8"), (v8, "v8")):
+        _need_out(t, q8.shape, torch.uint8, dev, name)
+    for t, name in ((q_scale, "q_scale"), (k_scale, "k_scale"), (v_scale, "v_scale")):
+        _need_out(t, (bh,), torch.float32, dev, name)
+    n_q, n_k = _lists(bh, dev, q_offsets, k_offsets, sel_count, sel_idx)
+    _need_out(perm, (bh, N), torch.int32, dev, "perm")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    dev = q8.device
     if out is None:
         out = torch.empty(bh, N, d, dtype=torch.bfloat16, device=dev)
+    _same_device(dev, out)
     obh, oN, od, heads, sb, sh, st = _strided_view(out)
     if (obh, oN, od) != (bh, N, d) or out.dtype != torch.bfloat16:
         raise Svg2Error("out must be a bf16 view of shape [bh, N, d]")
-    if isinstance(lse, torch.Tensor):
-        if lse.dtype != torch.float32 or tuple(lse.shape) != (bh, N) or not lse.is_contiguous():
-            raise Svg2Error("lse must be a contiguous fp32 [bh, N] tensor")
-        ls = lse
-    else:
-        ls = torch.empty(bh, N, dtype=torch.float32, device=dev) if lse else None
+    ls = _lse_buffer(lse, bh, N, dev)
     L = lib()
     ws_n = L.svg2_varblock_attn_workspace_size(bh, N, n_q, n_k, d)
     ws = _workspace(ws_n, dev, workspace)

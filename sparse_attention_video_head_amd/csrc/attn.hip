@@ -606,8 +606,15 @@ __global__ __launch_bounds__(256, 3) void k_attn_bf16(
       // included) at the first use of Q in each step.
       __builtin_amdgcn_s_waitcnt(0xF70);
 
+      // Softmax state.  m_ref is the reference max (log2 units); thr is the raw
+      // score above which a tile moves it: (m_ref + kLazyTau) / scale_log2, kept
+      // in raw units so the common path needs no multiply.  The row sum adds the
+      // bf16-rounded P that feed the P.V product (two dot2 accumulators over the
+      // packed pairs), so the normaliser is the sum of the weights actually used.
       float m_ref = -__builtin_inff();
-      float l_part = 0.f;                            // this lane's share of the row sum
+      float thr = -__builtin_inff();
+      const float inv_scale_log2 = 1.f / scale_log2;
+      float l_a = 0.f, l_b = 0.f;                    // this lane's share of the row sum
       f32x16_t o[DT];
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
@@ -723,30 +730,40 @@ __global__ __launch_bounds__(256, 3) void k_attn_bf16(
           for (int i = 0; i < 16; ++i)
             if ((i >> 2) * 8 + (i & 3) >= lim) sc[i] = -__builtin_inff();
         }
+        // raw max of the tile's scores for this query (v_maximum3: scores are
+        // never NaN, and the NaN-propagating maximum needs no canonicalising)
         float mx = sc[0];
 #pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+        for (int i = 1; i < 16; ++i) mx = __builtin_elementwise_maximum(mx, sc[i]);
         {
           const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-          mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
+          mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
         }
-        if (mx > m_ref + kLazyTau) {
-          const float alpha = __builtin_amdgcn_exp2f(m_ref - mx);
-          l_part *= alpha;
+        if (mx > thr) {
+          const float m_new = mx * scale_log2;
+          const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+          l_a *= alpha;
+          l_b *= alpha;
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
-          m_ref = mx;
+          m_ref = m_new;
+          thr = (m_new + kLazyTau) * inv_scale_log2;
         }
         const float neg = -m_ref;
+        const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
         u32x4_t pw[2];
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
           const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[i], scale_log2, neg));
           const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[i + 1], scale_log2, neg));
-          l_part += p0 + p1;
-          pw[i >> 3][(i & 7) >> 1] = pack_bf16x2(p0, p1);
+          const uint32_t w = pack_bf16x2(p0, p1);
+          pw[i >> 3][(i & 7) >> 1] = w;
+          if (i & 2)
+            l_b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), ones, l_b, false);
+          else
+            l_a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), ones, l_a, false);
         }
         // V^T fragments: two transposing reads per MFMA, issued kAhead MFMAs early
         constexpr int NV = 2 * DT;
@@ -816,6 +833,7 @@ __global__ __launch_bounds__(256, 3) void k_attn_bf16(
       // lanes i and i+32 hold the two halves of query col's keys
       float l_tot;
       {
+        const float l_part = l_a + l_b;
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part), __float_as_uint(l_part), false, false);
         l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
       }

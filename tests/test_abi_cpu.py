@@ -309,3 +309,104 @@ def test_fp8_validation():
     assert attn_unperm(sv=None) == INVALID
     assert attn_unperm(lse=FAKE + 2) == INVALID
     assert attn_unperm(wsn=8) == WORKSPACE
+
+
+def test_binding_checks_caller_buffers(monkeypatch):
+    """Outputs, in/out buffers and workspaces handed in by the caller are
+    checked for device, dtype, exact shape and contiguity before any library
+    call: the kernels write through their raw pointers.  Without a GPU the
+    inputs are host tensors with the GPU check switched off; a buffer on the
+    "meta" device stands for one on another device."""
+    import torch
+    monkeypatch.setattr(B, "_need_cuda", lambda *ts: None)
+    real = B.lib()
+
+    class SizeQueriesOnly:
+        """The library with only its workspace-size queries: a check that lets
+        a bad buffer through reaches a compute call and fails the test."""
+        def __getattr__(self, name):
+            if name.endswith("_workspace_size"):
+                return getattr(real, name)
+            raise AssertionError(f"{name} reached with a bad buffer")
+
+    monkeypatch.setattr(B, "lib", lambda: SizeQueriesOnly())
+    bf, i32, f32 = torch.bfloat16, torch.int32, torch.float32
+    bh, N, d, n = 2, 100, 64, 5
+    meta = lambda *s, dt=i32: torch.empty(*s, dtype=dt, device="meta")
+    z = lambda *s, dt=i32: torch.zeros(*s, dtype=dt)
+    x = z(bh, N, d, dt=bf)
+
+    def bad(fn, *a, **kw):
+        with pytest.raises(B.Svg2Error):
+            fn(*a, **kw)
+
+    # k-means
+    bad(B.kmeans, x, n, 1, centroids=z(bh, n + 1, d, dt=f32))
+    bad(B.kmeans, x, n, 1, labels=meta(bh, N))
+    bad(B.kmeans, x, n, 1, counts=z(bh, n, dt=torch.int64))
+    bad(B.kmeans, x, n, 1, init=z(bh, n, d + 1, dt=f32))
+    bad(B.kmeans, x, n, 1, workspace=meta(1 << 20, dt=torch.uint8))
+    bad(B.kmeans, x, n, 1, workspace=z(4, dt=torch.uint8))
+    # k-means with the permutation
+    bad(B.kmeans_permute, x, n, 1, perm=z(bh, N + 1))
+    bad(B.kmeans_permute, x, n, 1, offsets=meta(bh, n + 1))
+    bad(B.kmeans_permute, x, n, 1, x_out=z(bh, N, d, dt=f32))
+    bad(B.kmeans_permute, x, n, 1, y=x, y_out=z(bh, d, N, dt=bf).transpose(1, 2))
+    bad(B.kmeans_permute, x, n, 1, y=meta(bh, N, d, dt=bf))
+    bad(B.kmeans_permute, x, n, 1, fp8=True, x_scale=z(bh + 1, dt=f32))
+    # permute
+    lab = z(bh, N)
+    bad(B.permute, lab, n, x, outs=[z(bh, N, d + 1, dt=bf)])
+    bad(B.permute, lab, n, x, perm=meta(bh, N))
+    bad(B.permute, lab, n, x, offsets=z(bh, n))
+    bad(B.permute, lab, n, meta(bh, N, d, dt=bf))
+    # select
+    cq, ck = z(bh, 3, d, dt=f32), z(bh, n, d, dt=f32)
+    qc, kc = z(bh, 3), z(bh, n)
+    bad(B.select_topp, cq, z(bh, 4), ck, kc, 0.9)
+    bad(B.select_topp, cq, qc, ck, z(bh, n + 1), 0.9)
+    bad(B.select_topp, cq, qc, z(bh, n, d + 1, dt=f32), kc, 0.9)
+    bad(B.select_topp, cq, qc, ck, kc, 0.9, sel_idx=meta(bh, 3, n))
+    bad(B.select_topp, cq, qc, ck, kc, 0.9, pair_count=z(bh, dt=i32))
+    # attention
+    qo, ko = z(bh, 4), z(bh, n + 1)
+    sc, si = z(bh, 3), z(bh, 3, n)
+    bad(B.varblock_attn, x, x, x, z(bh + 1, 4), ko, sc, si)
+    bad(B.varblock_attn, x, x, x, qo, ko, z(bh, 4), si)
+    bad(B.varblock_attn, x, x, x, qo, ko, sc, si, out=meta(bh, N, d, dt=bf))
+    bad(B.varblock_attn, x, x, x, qo, ko, sc, si, out=z(bh, N, d, dt=f32))
+    bad(B.varblock_attn, x, x, x, qo, ko, sc, si, lse=z(bh, N + 1, dt=f32))
+    bad(B.varblock_attn, x, x, x, qo, ko, sc, si, workspace=z(8, dt=torch.uint8))
+    bad(B.varblock_attn_unpermute, x, x, x, qo, ko, sc, si, z(bh, N - 1))
+    bad(B.varblock_attn_unpermute, x, x, x, qo, ko, sc, si, z(bh, N), out=meta(bh, N, d, dt=bf))
+    bad(B.varblock_attn_unpermute, x, x, x, qo, ko, z(bh, 3, n + 1), si, z(bh, N))
+    # un-permute
+    bad(B.unpermute, x, z(bh, N), out=meta(bh, N, d, dt=bf))
+    bad(B.unpermute, x, meta(bh, N))
+    # identification study
+    bad(B.cluster_means, x, lab, n, means=z(bh, n, d + 1, dt=f32))
+    bad(B.cluster_means, x, lab, n, counts=meta(bh, n))
+    bad(B.recall_mass, z(bh, N, dt=f32), z(bh, N, dt=f32), out=z(bh, dt=f32))
+    # FP8
+    bad(B.quantize_fp8, x, x8=meta(bh, N, d, dt=torch.uint8))
+    bad(B.quantize_fp8, x, scale=z(bh, 1, dt=f32))
+    q8, s1 = z(bh, N, 128, dt=torch.uint8), z(bh, dt=f32)
+    bad(B.varblock_attn_fp8, q8, q8, q8, s1, s1, s1, qo, ko, sc, si, out=z(bh, N, 128, dt=f32))
+    bad(B.varblock_attn_fp8, q8, q8, q8, s1, s1, s1, qo, ko, sc, si, lse=z(bh, N + 3, dt=f32))
+    bad(B.varblock_attn_fp8, q8, q8, q8, z(bh + 1, dt=f32), s1, s1, qo, ko, sc, si)
+    bad(B.varblock_attn_fp8_unpermute, q8, q8, q8, s1, s1, s1, qo, ko, z(bh, 2), si, z(bh, N))
+    bad(B.varblock_attn_fp8_unpermute, q8, q8, q8, s1, s1, s1, qo, ko, sc, si, z(bh, N),
+        out=meta(bh, N, 128, dt=bf))
+
+    # well-formed buffers pass every check and reach the library's compute call
+    def good(fn, *a, **kw):
+        with pytest.raises(AssertionError, match="reached"):
+            fn(*a, **kw)
+
+    good(B.kmeans, x, n, 1, centroids=z(bh, n, d, dt=f32), labels=z(bh, N), counts=z(bh, n))
+    good(B.kmeans_permute, x, n, 1, y=x, perm=z(bh, N), offsets=z(bh, n + 1))
+    good(B.permute, lab, n, x, outs=[z(bh, N, d, dt=bf)])
+    good(B.select_topp, cq, qc, ck, kc, 0.9, pair_count=z(bh, dt=torch.int64))
+    good(B.varblock_attn, x, x, x, qo, ko, sc, si, lse=z(bh, N, dt=f32))
+    good(B.varblock_attn_unpermute, x, x, x, qo, ko, sc, si, z(bh, N), out=z(bh, N, d, dt=bf))
+    good(B.varblock_attn_fp8, q8, q8, q8, s1, s1, s1, qo, ko, sc, si, lse=True)

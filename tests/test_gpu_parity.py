@@ -1,7 +1,8 @@
 """GPU parity: every HIP entry point against the fp64 oracle on the same
 seeded inputs.  Inputs come from the generator and, for later stages, from
-the oracle's own earlier stages; nothing computed on the GPU is fed back to
-the oracle.
+the oracle's own earlier stages, except where a stage is teacher-forced: the
+centroid update is checked against the oracle's update of the GPU's own
+labels, so that one near-tie token cannot skip the check.
 
 Bars (the tolerances are fixed by the method's statement of the path):
   * integer / index outputs (labels, offsets, permutation, selections,
@@ -17,6 +18,7 @@ import pytest
 import torch
 
 import oracle
+from parity_checks import check_labels_in_tie_band
 from sparse_attention_video_head_amd import binding as B
 from sparse_attention_video_head_amd import synth
 
@@ -188,8 +190,10 @@ def test_varblock_attn_vs_oracle(dt, d, N, n_q, n_k, top_p):
         assert rel_l2(got, ref) <= tol[1]
         gl = lse[h].cpu().numpy().astype(np.float64)
         fin = np.isfinite(ref_lse)
-        # bf16: the normaliser sums the bf16-rounded probabilities (relative
-        # error <= 2^-9 each), so the log of the sum may move by up to 2^-9
+        # bf16: the kernel's normaliser is the sum of the bf16-rounded
+        # probabilities that weight V (each within 2^-9 relative of the exact
+        # one), so log(sum) may move by up to 2^-9 = 1.95e-3 from the oracle's,
+        # plus fp32 rounding of the scores and the sum
         np.testing.assert_allclose(gl[fin], ref_lse[fin], rtol=0, atol=2.5e-3 if dt == "bf16" else 1e-4)
         assert np.all(gl[~fin] == -np.inf) and np.all(got[~fin] == 0)
 
@@ -274,17 +278,16 @@ def test_kmeans_one_round_vs_oracle(dt, d, N, n):
     torch.cuda.synchronize()
     for h in range(bh):
         X = np64(q[h])
-        a = oracle.assign(X, init32[h].astype(np.float64))
+        C0 = init32[h].astype(np.float64)
+        a = oracle.assign(X, C0)
         lab = r["labels"][h].cpu().numpy()
-        clear = a.margin >= 1e-5
-        assert np.mean(~clear) <= 1e-3 + 1.0 / N
-        np.testing.assert_array_equal(lab[clear], a.labels[clear])
+        check_labels_in_tie_band(X, C0, lab, a, max_share=1e-3 + 1.0 / N)
         np.testing.assert_array_equal(r["counts"][h].cpu().numpy(), np.bincount(lab, minlength=n))
         np.testing.assert_allclose(r["min_dist"][h].cpu().numpy(), a.min_dist, rtol=1e-4, atol=1e-3)
-        if np.all(lab == a.labels):
-            C, _ = oracle.update(X, a.labels, init32[h].astype(np.float64))
-            got = r["centroids"][h].cpu().numpy().astype(np.float64)
-            assert np.all(np.abs(got - C) <= 1e-5 * np.maximum(1.0, np.abs(C)))
+        # the update teacher-forced with the GPU's labels: every centroid
+        C, _ = oracle.update(X, lab.astype(np.int64), C0)
+        got = r["centroids"][h].cpu().numpy().astype(np.float64)
+        assert np.all(np.abs(got - C) <= 1e-5 * np.maximum(1.0, np.abs(C)))
 
 
 def test_kmeans_chained_rounds_equal_one_call():
@@ -406,6 +409,35 @@ def test_layer_tiny_config_end_to_end():
     assert rel_l2(got, ref.out) <= 1e-4
     assert np.max(np.abs(got - ref.out)) <= 1e-3
     assert int(layer.pairs[0]) == ref.pairs
+
+
+def test_layer_small_bf16_untethered_vs_oracle():
+    """The small bf16 config (4 heads x 16,384 tokens, d = 128, 100 / 250
+    clusters, 5 rounds, top-p 0.9), whole layer on the GPU from the same seeds
+    as the oracle's layer, with nothing passed between them.  Reports the label
+    agreement of both sides and the output's error against the oracle per head;
+    the bars allow the few tokens a near tie sends elsewhere."""
+    from sparse_attention_video_head_amd.pipeline import SVG2Layer
+    cfg = synth.CONFIGS["small"]
+    data = synth.make_layer(cfg)
+    layer = SVG2Layer(cfg.bh, cfg.n_tokens, cfg.head_dim, torch.bfloat16, cfg.n_q, cfg.n_k)
+    top_p = cfg.top_p[0]
+    out = layer.run(data["q"].to(DEV), data["k"].to(DEV), data["v"].to(DEV), top_p, iters=cfg.iters,
+                    seed_q=100, seed_k=200)
+    torch.cuda.synchronize()
+    for h in range(cfg.bh):
+        q, k, v = (np64(data[x][h]) for x in "qkv")
+        ref = oracle.layer(q, k, v, cfg.n_q, cfg.n_k, cfg.iters, float(np.float32(top_p)), seed_q=100,
+                           seed_k=200, problem=h)
+        agree_q = float(np.mean(layer.labels_q[h].cpu().numpy() == ref.km_q.labels))
+        agree_k = float(np.mean(layer.labels_k[h].cpu().numpy() == ref.km_k.labels))
+        got = np64(out[h])
+        err = rel_l2(got, ref.out)
+        mx = float(np.max(np.abs(got - ref.out)))
+        print(f"head {h}: label agreement Q {agree_q:.5f} K {agree_k:.5f}; output rel-L2 {err:.3e} "
+              f"max-abs {mx:.3e}; pairs {int(layer.pairs[h])} vs {ref.pairs}", flush=True)
+        assert agree_q >= 0.99 and agree_k >= 0.99
+        assert err <= 2e-2
 
 
 # ====================================================================== denoising run

@@ -39,7 +39,61 @@ def test_seeding_uniform_range_and_uniformity():
     assert oracle.seeding_uniform(7, 0, 1) != oracle.seeding_uniform(7, 0, 2)
 
 
+@pytest.mark.parametrize("problem,pick", [(0, 0), (0, 7), (3, 0), (5, 999), ((1 << 20) + 1, 12345)])
+def test_seeding_uniform_published_vector(problem, pick):
+    """u(seed, problem, pick) is the top 53 bits of splitmix64 of
+    seed XOR (problem * 2^32 + pick), times 2^-53.  With the seed chosen so that
+    this state is i * gamma, the generator's output is output i of the
+    published vector: a '+' for the XOR, a dropped or shifted problem term, or
+    a wrong bit count in the conversion fails it."""
+    want = _golden_ints("splitmix64_state0.txt")
+    gamma = 0x9E3779B97F4A7C15
+    for i, w in enumerate(want):
+        state = (i * gamma) & ((1 << 64) - 1)
+        seed = state ^ ((problem << 32) + pick)
+        u = oracle.seeding_uniform(seed, problem, pick)
+        assert u == (w >> 11) / 2.0 ** 53
+        assert u == float(np.ldexp(float(w >> 11), -53))
+
+
 # ---------------------------------------------------------------- k-means++
+def _kmeanspp_with_uniforms(monkeypatch, X, n, us):
+    """kmeanspp with the draws u_k replaced by the given values."""
+    from oracle import svg2_oracle as so
+    monkeypatch.setattr(so, "seeding_uniform", lambda seed, problem, k: us[k])
+    return so.kmeanspp(X, n, seed=0)
+
+
+def test_kmeanspp_margin_hand_built(monkeypatch):
+    """Points 0, 1, 3 on a line, pick 0 = token 0 (u_0 = 0): D2 = (0, 1, 9),
+    cumulative sums (0, 1, 10).  u_1 = 0.3 puts the target at 3, inside token
+    2's interval (1, 10]: margin = min(3 - 1, 10 - 3) / 10 = 0.2.  u_1 = 0.05
+    puts it at 0.5 in token 1's interval (0, 1]: margin = 0.05."""
+    X = np.array([[0.0], [1.0], [3.0]])
+    r = _kmeanspp_with_uniforms(monkeypatch, X, 2, [0.0, 0.3])
+    assert list(r.index) == [0, 2]
+    assert r.margin[0] == np.inf
+    assert abs(r.margin[1] - 0.2) < 1e-15
+    r = _kmeanspp_with_uniforms(monkeypatch, X, 2, [0.0, 0.05])
+    assert list(r.index) == [0, 1]
+    assert abs(r.margin[1] - 0.05) < 1e-15
+
+
+def test_kmeanspp_margin_is_the_pick_preserving_radius(monkeypatch):
+    """The margin of pick k is how far u_k may move with the pick unchanged:
+    moving u_k by 0.999 margin keeps it, moving it by 1.001 margin one way or
+    the other changes it."""
+    X = np.random.default_rng(3).standard_normal((40, 4))
+    for u1 in (0.137, 0.5, 0.861):
+        base = _kmeanspp_with_uniforms(monkeypatch, X, 2, [0.25, u1])
+        m = base.margin[1]
+        assert 0 < m < 0.5
+        for f in (0.999, -0.999):
+            assert _kmeanspp_with_uniforms(monkeypatch, X, 2, [0.25, u1 + f * m]).index[1] == base.index[1]
+        moved = [_kmeanspp_with_uniforms(monkeypatch, X, 2, [0.25, u1 + f * m]).index[1] for f in (1.001, -1.001)]
+        assert any(t != base.index[1] for t in moved)
+
+
 def test_kmeanspp_first_pick_and_rows():
     rng = np.random.default_rng(0)
     X = rng.standard_normal((97, 5))

@@ -147,6 +147,27 @@ def _mixture(seed, N=300, d=16, comps=6):
     return q, k, v
 
 
+def test_topp_ambiguous_flag_hand_built():
+    """Rows whose cut sits within ``band`` of p, or whose order at the cut is
+    within band * P_(1), are flagged; others are not.  Probabilities chosen by
+    hand (exact binary fractions where equality matters)."""
+    kc = np.ones(3, np.int64)
+    P = np.array([[0.5, 0.25, 0.25],       # cumsum 0.5, 0.75, 1: p = 0.75 is reached exactly at the cut
+                  [0.625, 0.25, 0.125],    # p = 0.7: cut at 1 (0.875); neighbours 0.625 and 0.875 are far
+                  [0.375, 0.375, 0.25],    # p = 0.3: cut at 0, P_(1) = P_(2): a tie at the cut
+                  [0.6, 0.3, 0.1]])        # p = 0.7: cut at 1; |0.6 - 0.7| = 0.1
+    want = {(0, 0.75, 1e-12): True, (1, 0.7, 1e-12): False, (1, 0.7, 0.2): True,
+            (2, 0.3, 1e-12): True, (3, 0.7, 0.05): False, (3, 0.7, 0.11): True}
+    for (i, p, band), amb in want.items():
+        sel = oracle.select_topp(P[i:i + 1], kc, p, band=band)
+        assert bool(sel.ambiguous[0]) == amb, (i, p, band)
+    # the lists themselves do not depend on the band
+    assert list(oracle.select_topp(P[0:1], kc, 0.75).lists[0]) == [0, 1]
+    assert list(oracle.select_topp(P[2:3], kc, 0.3).lists[0]) == [0]
+    # p >= 1 keeps everything and is never ambiguous
+    assert not oracle.select_topp(P, kc, 1.0, band=0.5).ambiguous.any()
+
+
 def test_layer_at_p1_equals_dense_attention():
     """With every cluster selected the permutations cancel and the layer is
     plain softmax attention (wiki: Key claims, §4.1; Method, stage (2))."""
