@@ -16,7 +16,9 @@ from typing import Optional, Sequence
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsvg2.so")
+# SVG2_LIBRARY points the binding at another build of the same library (the
+# host-sanitizer build of the CPU tests); by default the in-tree one.
+_LIB_PATH = os.environ.get("SVG2_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsvg2.so")
 _lib = None
 
 F32, BF16 = 0, 1
