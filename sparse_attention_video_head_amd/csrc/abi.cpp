@@ -59,6 +59,7 @@ struct KmeansWs {
   int32_t* offsets;
   double* partial;    // bh * (n + mean_chunks(N)) * d: per-chunk centroid sums
   uint32_t* amax;     // 2 bh: max|x|, max|y| per problem (E4M3 row moves)
+  AsgFixWs fix;       // near ties of the bf16 assignment (count bh; token, dmin bh * N)
 };
 
 KmeansWs carve_kmeans(Carve& c, int bh, int N, int d, int n) {
@@ -77,6 +78,9 @@ KmeansWs carve_kmeans(Carve& c, int bh, int N, int d, int n) {
   w.offsets = c.take<int32_t>((size_t)bh * (n + 1));
   w.partial = c.take<double>((size_t)bh * (n + mean_chunks(N)) * d);
   w.amax = c.take<uint32_t>((size_t)2 * bh);
+  w.fix.count = c.take<int32_t>((size_t)bh);
+  w.fix.token = c.take<int32_t>(bN);
+  w.fix.dmin = c.take<float>(bN);
   return w;
 }
 
@@ -154,11 +158,11 @@ int kmeans_run(const void* x, int32_t dtype, int32_t bh, int32_t n_tokens, int32
   }
   for (int it = 0; it < n_iters; ++it) {
     if (bf16) {
-      st = hip_status(launch_prep_centroids(centroids, bh, n, d, w.c_hi, w.c_lo, w.c_norm, stream));
+      st = hip_status(launch_prep_centroids(centroids, bh, n, d, w.c_hi, w.c_lo, w.c_norm, w.fix.count, stream));
       if (st) return st;
     }
     st = hip_status(launch_assign(x, bf16, bh, N, d, n, centroids, w.c_hi, w.c_lo, w.c_norm, labels,
-                                  it == n_iters - 1 ? min_dist : nullptr, stream));
+                                  it == n_iters - 1 ? min_dist : nullptr, w.fix, stream));
     if (st) return st;
     const bool last = it == n_iters - 1 && mv.x_out;
     int32_t* pm = last ? perm_out : w.perm;

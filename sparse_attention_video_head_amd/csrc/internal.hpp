@@ -36,11 +36,19 @@ hipError_t launch_kmeanspp(const void* x, bool bf16, int bh, int N, int d, int n
 // kCentroidPad-row padded per problem (padding rows: zeros, ||c||^2 = +inf)
 constexpr int kCentroidPad = 32;
 __host__ __device__ inline int centroid_rows(int n) { return (n + kCentroidPad - 1) / kCentroidPad * kCentroidPad; }
+// (also empties the per-problem near-tie lists of the next bf16 assignment)
 hipError_t launch_prep_centroids(const float* c, int bh, int n, int d, uint16_t* c_hi,
-                                 uint16_t* c_lo, float* c_norm, hipStream_t s);
+                                 uint16_t* c_lo, float* c_norm, int32_t* fix_count, hipStream_t s);
+// Near ties of the bf16 assignment, decided again in fp64: count [bh], token
+// and dmin [bh, N] (the listed tokens and their smallest matrix-core distance).
+struct AsgFixWs {
+  int32_t* count;
+  int32_t* token;
+  float* dmin;
+};
 hipError_t launch_assign(const void* x, bool bf16, int bh, int N, int d, int n, const float* c,
                          const uint16_t* c_hi, const uint16_t* c_lo, const float* c_norm,
-                         int32_t* labels, float* min_dist, hipStream_t s);
+                         int32_t* labels, float* min_dist, const AsgFixWs& fw, hipStream_t s);
 // centroid c = mean of the rows perm[offsets[c] .. offsets[c+1]); empty keeps c.
 // partial_ws: bh * (n + mean_chunks(N)) * d doubles.
 constexpr int kMeanChunk = 512;              // sorted positions per partial-sum work-group

@@ -493,11 +493,14 @@ hipError_t launch_kmeanspp(const void* x, bool bf16, int bh, int N, int d, int n
 __global__ __launch_bounds__(256) void k_prep_centroids(const float* __restrict__ c, int bh, int n, int npad,
                                                         int d, uint16_t* __restrict__ hi,
                                                         uint16_t* __restrict__ lo,
-                                                        float* __restrict__ cn) {
+                                                        float* __restrict__ cn,
+                                                        int32_t* __restrict__ fix_count) {
   const int row = blockIdx.x * 4 + threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   if (row >= bh * npad) return;
   const int p = row / npad, j = row % npad;
+  // the round's near-tie list starts empty (the assignment appends to it)
+  if (j == 0 && lane == 0) fix_count[p] = 0;
   if (j >= n) {
     for (int e = lane; e < d; e += kWave) {
       hi[(size_t)row * d + e] = 0;
@@ -507,25 +510,28 @@ __global__ __launch_bounds__(256) void k_prep_centroids(const float* __restrict_
     return;
   }
   const float* src = c + ((size_t)p * n + j) * d;
-  float acc = 0.f;
+  // ||c||^2: the squares of fp32 values are exact in fp64 and the sum of at
+  // most 128 of them errs by ~1e-14 relative, so the stored fp32 norm is
+  // within one fp32 rounding (2^-24 relative) of the exact one
+  double acc = 0.0;
   for (int e = lane; e < d; e += kWave) {
     const float v = src[e];
     const uint16_t h = f32_to_bf16(v);
     const uint16_t l = f32_to_bf16(v - bf16_to_f32(h));
     hi[(size_t)row * d + e] = h;
     lo[(size_t)row * d + e] = l;
-    acc = fmaf(v, v, acc);
+    acc = fma((double)v, (double)v, acc);
   }
   acc = wave_sum(acc);
-  if (lane == 0) cn[row] = acc;
+  if (lane == 0) cn[row] = (float)acc;
 }
 
 hipError_t launch_prep_centroids(const float* c, int bh, int n, int d, uint16_t* c_hi,
-                                 uint16_t* c_lo, float* c_norm, hipStream_t s) {
+                                 uint16_t* c_lo, float* c_norm, int32_t* fix_count, hipStream_t s) {
   const int npad = centroid_rows(n);
   const int rows = bh * npad;
   hipLaunchKernelGGL(k_prep_centroids, dim3((rows + 3) / 4), dim3(256), 0, s, c, bh, n, npad, d, c_hi, c_lo,
-                     c_norm);
+                     c_norm, fix_count);
   return hipGetLastError();
 }
 
@@ -537,8 +543,25 @@ hipError_t launch_prep_centroids(const float* c, int bh, int n, int d, uint16_t*
 // hi and lo rows plus ||c||^2), filled by direct global -> LDS loads three
 // chunks ahead; the rows' 16-byte chunks are XOR-swizzled by row % 16 so that
 // the operand reads are conflict-free without padding.
+//
+// Exact labels.  The matrix-core distance of token x to centroid c,
+// a(c) = fl(||c||^2) - 2 acc(x, c_hi + c_lo), differs from the exact
+// ||c||^2 - 2 x.c by at most
+//   E(x) = 2 (2^-18 + g256) (1 + 2^-8) ||x|| cmax + 2u (cmax^2 + ||x|| cmax)
+// with u = 2^-24, g256 = 256u / (1 - 256u) (the fp32 accumulation of 256
+// exact products in any order), 2^-18 the relative error of c_hi + c_lo, and
+// cmax the largest centroid norm of the problem (||c||^2 is rounded once from
+// fp64).  So when the second-smallest a exceeds the smallest by more than
+// 2E, the smallest is the true nearest centroid.  Otherwise the token is a
+// near tie: it is appended, with its smallest a, to the problem's fix list,
+// and a second launch of this kernel (FIX) re-walks the centroids for the
+// listed tokens, keeps every centroid whose a is within 2E of that smallest
+// value (the true nearest is among them), and decides between those with
+// exact fp64 distances (ties to the lowest index).
 constexpr int kAsgTB = 4;                 // 32-token blocks per wave
 constexpr int kAsgCB = kCentroidPad;      // centroids per LDS chunk
+constexpr int kAsgTok = 4 * kAsgTB * 32;  // tokens per work-group
+constexpr int kFixCand = 16;              // candidate centroids kept per listed token
 
 // s_waitcnt immediates (vmcnt only; expcnt and lgkmcnt not waited for)
 constexpr int asg_wait_vm(int n) { return 0xF70 | n; }
@@ -548,13 +571,27 @@ __device__ __forceinline__ void lds_barrier_asg() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-template <int D>
+// Error bound E(x) of a matrix-core distance (see above), rounded up.
+__device__ __forceinline__ float asg_error_bound(float xn, float cmax2) {
+  const float xnorm = sqrtf(xn) * (1.f + 1e-5f);
+  const float cmax = sqrtf(cmax2) * (1.f + 1e-6f);
+  return 3.85e-5f * xnorm * cmax + 1.2e-7f * cmax2;
+}
+
+struct AsgFix {
+  int32_t* count;         // [bh] near ties listed this round
+  int32_t* token;         // [bh, N] listed tokens
+  float* dmin;            // [bh, N] their smallest matrix-core distance
+  const float* C;         // [bh, n, D] fp32 centroids (the exact values)
+};
+
+template <int D, bool FIX>
 __global__ __launch_bounds__(256, 2) void k_assign_bf16(const uint16_t* __restrict__ X, int N, int n,
                                                         const uint16_t* __restrict__ Chi,
                                                         const uint16_t* __restrict__ Clo,
                                                         const float* __restrict__ Cn,
                                                         int32_t* __restrict__ labels,
-                                                        float* __restrict__ min_dist) {
+                                                        float* __restrict__ min_dist, AsgFix fx) {
   typedef __attribute__((address_space(3))) void lds_void_t;
   typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
   typedef __attribute__((address_space(3))) float lds_f32_t;
@@ -566,18 +603,24 @@ __global__ __launch_bounds__(256, 2) void k_assign_bf16(const uint16_t* __restri
   // ring slot j: hi rows [0, CB*D), lo rows [CB*D, 2*CB*D), then CB norms
   constexpr int SLOT = 2 * kAsgCB * D + 2 * kAsgCB;   // uint16 elements
   __shared__ __attribute__((aligned(16))) uint16_t sC0[SLOT], sC1[SLOT], sC2[SLOT], sC3[SLOT];
+  // FIX: candidate centroids per listed token (token slot = wave, block, column)
+  __shared__ int32_t s_cand[FIX ? kAsgTok * kFixCand : 1];
+  __shared__ int32_t s_ncand[FIX ? kAsgTok : 1];
 
   const int p = blockIdx.y;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int col = lane & 31, half = lane >> 5;
-  const int tok0 = blockIdx.x * (4 * kAsgTB * 32) + wave * (kAsgTB * 32);
   const uint16_t* Xp = X + (size_t)p * N * D;
   const int npad = centroid_rows(n);
   const int nchunk = npad / kAsgCB;
   const uint16_t* Hp = Chi + (size_t)p * npad * D;
   const uint16_t* Lp = Clo + (size_t)p * npad * D;
   const float* Np = Cn + (size_t)p * npad;
+  // FIX: this work-group's share of the list, kAsgTok entries at a time
+  const int nfix = FIX ? min(fx.count[p], N) : 0;
+  int li0 = FIX ? (int)blockIdx.x * kAsgTok : 0;
+  if (FIX && li0 >= nfix) return;
 
   // this lane's part of a chunk load: row 8 wave + RPI q + lane / CPR,
   // 16-byte slot lane % CPR holding source chunk (lane % CPR) ^ (row % 16)
@@ -605,107 +648,222 @@ __global__ __launch_bounds__(256, 2) void k_assign_bf16(const uint16_t* __restri
                                        (lds_void_t*)(dst + 2 * kAsgCB * D), 4, 0, 0);
   };
 
-  bf16x8_t xb[kAsgTB][KS];
-  float xn[kAsgTB];
-#pragma unroll
-  for (int tb = 0; tb < kAsgTB; ++tb) {
-    const int t = tok0 + tb * 32 + col;
-    float acc = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (t < N) v = *reinterpret_cast<const u32x4_t*>(Xp + (size_t)t * D + ks * 16 + half * 8);
-      xb[tb][ks] = __builtin_bit_cast(bf16x8_t, v);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float a0 = bf16_lo(v[e]), a1 = bf16_hi(v[e]);
-        acc = fmaf(a0, a0, fmaf(a1, a1, acc));
-      }
-    }
-    xn[tb] = acc + __shfl_xor(acc, 32);
-  }
-
-  float best[kAsgTB];
-  int bidx[kAsgTB];
-#pragma unroll
-  for (int tb = 0; tb < kAsgTB; ++tb) {
-    best[tb] = __builtin_inff();
-    bidx[tb] = 0;
-  }
-  // operand row col: its chunk (2 ks + half) sits at (2 ks + half) ^ (col % 16)
-  const int arow = col * D, aswz = col & (CPR - 1) & 15;
-
-  auto compute = [&](const uint16_t* slot, int c0) __attribute__((always_inline)) {
-    const lds_u16_t* sh = (const lds_u16_t*)(const lds_void_t*)(const void*)slot;
-    const lds_f32_t* sn = (const lds_f32_t*)(sh + 2 * kAsgCB * D);
-    f32x16_t acc[kAsgTB];
-#pragma unroll
-    for (int tb = 0; tb < kAsgTB; ++tb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[tb][i] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int aoff = arow + (((2 * ks + half) ^ aswz) * 8);
-      const bf16x8_t ah = *(const __attribute__((address_space(3))) bf16x8_t*)(sh + aoff);
-      const bf16x8_t al = *(const __attribute__((address_space(3))) bf16x8_t*)(sh + kAsgCB * D + aoff);
+  for (;;) {
+    // tokens of this lane's blocks: consecutive tokens, or (FIX) listed ones
+    // with the candidate bound
+    const int tok0 = (int)blockIdx.x * kAsgTok + wave * (kAsgTB * 32) + col;
+    int tokf[FIX ? kAsgTB : 1];
+    float thr[FIX ? kAsgTB : 1];
+    auto tok = [&](int tb) __attribute__((always_inline)) -> int {
+      if constexpr (FIX) return tokf[tb];
+      else return tok0 + tb * 32 < N ? tok0 + tb * 32 : -1;
+    };
+    if constexpr (FIX) {
 #pragma unroll
       for (int tb = 0; tb < kAsgTB; ++tb) {
-        acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xb[tb][ks], acc[tb], 0, 0, 0);
-        acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xb[tb][ks], acc[tb], 0, 0, 0);
+        const int li = li0 + wave * (kAsgTB * 32) + tb * 32 + col;
+        tokf[tb] = li < nfix ? clampi(fx.token[(size_t)p * N + li], 0, N - 1) : -1;
+        thr[tb] = li < nfix ? fx.dmin[(size_t)p * N + li] : -__builtin_inff();
       }
     }
-    // lane (col, half) holds centroid rows (i/4)*8 + half*4 + i%4 of the chunk
+    if constexpr (FIX) {
+      for (int i = threadIdx.x; i < kAsgTok; i += 256) s_ncand[i] = 0;
+    }
+
+    bf16x8_t xb[kAsgTB][KS];
+    float xn[kAsgTB];
 #pragma unroll
-    for (int tb = 0; tb < kAsgTB; ++tb)
+    for (int tb = 0; tb < kAsgTB; ++tb) {
+      float acc = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = (i / 4) * 8 + half * 4 + (i % 4);
-        const float dist = sn[r] - 2.f * acc[tb][i];
-        if (dist < best[tb]) {
-          best[tb] = dist;
-          bidx[tb] = c0 + r;
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (tok(tb) >= 0) v = *reinterpret_cast<const u32x4_t*>(Xp + (size_t)tok(tb) * D + ks * 16 + half * 8);
+        xb[tb][ks] = __builtin_bit_cast(bf16x8_t, v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float a0 = bf16_lo(v[e]), a1 = bf16_hi(v[e]);
+          acc = fmaf(a0, a0, fmaf(a1, a1, acc));
         }
       }
-  };
+      xn[tb] = acc + __shfl_xor(acc, 32);
+    }
 
-  // prologue: chunks 0..2 in flight, chunks 0 and 1 landed
-  load_chunk(0, sC0);
-  load_chunk(1, sC1);
-  load_chunk(2, sC2);
-  constexpr int kLoadsPerChunk = 2 * INS + 1;   // wave 0 issues one more (the norms)
-  if (wave == 0) __builtin_amdgcn_s_waitcnt(asg_wait_vm(kLoadsPerChunk));
-  else __builtin_amdgcn_s_waitcnt(asg_wait_vm(2 * INS));
-  lds_barrier_asg();
-  // chunk c: compute slot c % 4, load chunk c + 3 into slot (c + 3) % 4; the
-  // first chunk of each trip loads after computing (at the loop head the
-  // compiler's tracking of the loads is lost and it would wait for all of them)
-  int c = 0;
-  auto iter = [&](auto late, const uint16_t* cur, uint16_t* nxt) __attribute__((always_inline)) -> bool {
-    if constexpr (!decltype(late)::value) load_chunk(c + 3, nxt);
-    compute(cur, c * kAsgCB);
-    if constexpr (decltype(late)::value) load_chunk(c + 3, nxt);
+    float best[kAsgTB], best2[kAsgTB];
+    int bidx[kAsgTB];
+#pragma unroll
+    for (int tb = 0; tb < kAsgTB; ++tb) {
+      best[tb] = __builtin_inff();
+      best2[tb] = __builtin_inff();
+      bidx[tb] = 0;
+    }
+    // operand row col: its chunk (2 ks + half) sits at (2 ks + half) ^ (col % 16)
+    const int arow = col * D, aswz = col & (CPR - 1) & 15;
+
+    auto compute = [&](const uint16_t* slot, int c0) __attribute__((always_inline)) {
+      const lds_u16_t* sh = (const lds_u16_t*)(const lds_void_t*)(const void*)slot;
+      const lds_f32_t* sn = (const lds_f32_t*)(sh + 2 * kAsgCB * D);
+      f32x16_t acc[kAsgTB];
+#pragma unroll
+      for (int tb = 0; tb < kAsgTB; ++tb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[tb][i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int aoff = arow + (((2 * ks + half) ^ aswz) * 8);
+        const bf16x8_t ah = *(const __attribute__((address_space(3))) bf16x8_t*)(sh + aoff);
+        const bf16x8_t al = *(const __attribute__((address_space(3))) bf16x8_t*)(sh + kAsgCB * D + aoff);
+#pragma unroll
+        for (int tb = 0; tb < kAsgTB; ++tb) {
+          acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xb[tb][ks], acc[tb], 0, 0, 0);
+          acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xb[tb][ks], acc[tb], 0, 0, 0);
+        }
+      }
+      // lane (col, half) holds centroid rows (i/4)*8 + half*4 + i%4 of the chunk
+#pragma unroll
+      for (int tb = 0; tb < kAsgTB; ++tb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = (i / 4) * 8 + half * 4 + (i % 4);
+          const float dist = sn[r] - 2.f * acc[tb][i];
+          if constexpr (FIX) {
+            if (dist <= thr[tb]) {
+              const int ts = wave * (kAsgTB * 32) + tb * 32 + col;
+              const int k = atomicAdd(&s_ncand[ts], 1);
+              if (k < kFixCand) s_cand[ts * kFixCand + k] = c0 + r;
+            }
+          } else {
+            // second smallest: with best <= best2, the median of the three
+            best2[tb] = __builtin_amdgcn_fmed3f(dist, best[tb], best2[tb]);
+            if (dist < best[tb]) {
+              best[tb] = dist;
+              bidx[tb] = c0 + r;
+            }
+          }
+        }
+    };
+
+    // cmax^2: the largest ||c||^2 of the problem's real rows
+    auto cmax_sq = [&]() __attribute__((always_inline)) -> float {
+      float cm = 0.f;
+      for (int r = lane; r < n; r += kWave) cm = fmaxf(cm, Np[r]);
+      return wave_max(cm);
+    };
+    if constexpr (FIX) {
+      const float cm = cmax_sq();
+#pragma unroll
+      for (int tb = 0; tb < kAsgTB; ++tb)
+        if (tok(tb) >= 0) thr[tb] += 2.02f * asg_error_bound(xn[tb], cm);
+      __syncthreads();                           // s_ncand cleared
+    }
+
+    // prologue: chunks 0..2 in flight, chunks 0 and 1 landed
+    load_chunk(0, sC0);
+    load_chunk(1, sC1);
+    load_chunk(2, sC2);
+    constexpr int kLoadsPerChunk = 2 * INS + 1;   // wave 0 issues one more (the norms)
     if (wave == 0) __builtin_amdgcn_s_waitcnt(asg_wait_vm(kLoadsPerChunk));
     else __builtin_amdgcn_s_waitcnt(asg_wait_vm(2 * INS));
     lds_barrier_asg();
-    return ++c < nchunk;
-  };
-  constexpr std::true_type late{};
-  constexpr std::false_type early{};
-  while (iter(late, sC0, sC3) && iter(early, sC1, sC0) && iter(early, sC2, sC1) && iter(early, sC3, sC2)) {
-  }
-
-#pragma unroll
-  for (int tb = 0; tb < kAsgTB; ++tb) {
-    const float ob = __shfl_xor(best[tb], 32);
-    const int oi = __shfl_xor(bidx[tb], 32);
-    if (ob < best[tb] || (ob == best[tb] && oi < bidx[tb])) {
-      best[tb] = ob;
-      bidx[tb] = oi;
+    // chunk c: compute slot c % 4, load chunk c + 3 into slot (c + 3) % 4; the
+    // first chunk of each trip loads after computing (at the loop head the
+    // compiler's tracking of the loads is lost and it would wait for all of them)
+    int c = 0;
+    auto iter = [&](auto late, const uint16_t* cur, uint16_t* nxt) __attribute__((always_inline)) -> bool {
+      if constexpr (!decltype(late)::value) load_chunk(c + 3, nxt);
+      compute(cur, c * kAsgCB);
+      if constexpr (decltype(late)::value) load_chunk(c + 3, nxt);
+      if (wave == 0) __builtin_amdgcn_s_waitcnt(asg_wait_vm(kLoadsPerChunk));
+      else __builtin_amdgcn_s_waitcnt(asg_wait_vm(2 * INS));
+      lds_barrier_asg();
+      return ++c < nchunk;
+    };
+    constexpr std::true_type late{};
+    constexpr std::false_type early{};
+    while (iter(late, sC0, sC3) && iter(early, sC1, sC0) && iter(early, sC2, sC1) && iter(early, sC3, sC2)) {
     }
-    const int t = tok0 + tb * 32 + col;
-    if (half == 0 && t < N) {
-      labels[(size_t)p * N + t] = bidx[tb];
-      if (min_dist) min_dist[(size_t)p * N + t] = fmaxf(xn[tb] + best[tb], 0.f);
+    __builtin_amdgcn_s_waitcnt(0xF70);           // no chunk load outlives the loop
+
+    if constexpr (!FIX) {
+      const float cmax2 = cmax_sq();
+#pragma unroll
+      for (int tb = 0; tb < kAsgTB; ++tb) {
+        const float ob = __shfl_xor(best[tb], 32);
+        const float ob2 = __shfl_xor(best2[tb], 32);
+        const int oi = __shfl_xor(bidx[tb], 32);
+        // second smallest of the two halves' (best, best2) pairs
+        best2[tb] = fminf(fmaxf(best[tb], ob), fminf(best2[tb], ob2));
+        if (ob < best[tb] || (ob == best[tb] && oi < bidx[tb])) {
+          best[tb] = ob;
+          bidx[tb] = oi;
+        }
+        const int t = tok(tb);
+        const bool tie = t >= 0 && half == 0 && !(best2[tb] - best[tb] > 2.02f * asg_error_bound(xn[tb], cmax2));
+        if (half == 0 && t >= 0) {
+          labels[(size_t)p * N + t] = bidx[tb];
+          if (min_dist) min_dist[(size_t)p * N + t] = fmaxf(xn[tb] + best[tb], 0.f);
+        }
+        // near ties to the fix list: one counter bump per wave
+        const uint64_t m = __ballot(tie);
+        if (m) {
+          int base = 0;
+          if (lane == __ffsll((unsigned long long)m) - 1) base = atomicAdd(&fx.count[p], __popcll(m));
+          base = __shfl(base, __ffsll((unsigned long long)m) - 1);
+          if (tie) {
+            const int k = base + __popcll(m & ((1ull << lane) - 1ull));
+            fx.token[(size_t)p * N + k] = t;
+            fx.dmin[(size_t)p * N + k] = best[tb];
+          }
+        }
+      }
+      return;
+    } else {
+      __syncthreads();                           // every candidate recorded
+      // exact fp64 decision between the candidates (all centroids if they
+      // overflowed the list): differences and squares of bf16 / fp32 values are
+      // exact in fp64; ties go to the lowest index
+      const float* Cp = fx.C + (size_t)p * n * D;
+#pragma unroll 1
+      for (int tb = 0; tb < kAsgTB; ++tb) {
+        const int t = tok(tb);
+        if (half != 0 || t < 0) continue;
+        const int ts = wave * (kAsgTB * 32) + tb * 32 + col;
+        const int nc = s_ncand[ts];
+        const bool all = nc > kFixCand;
+        const int m = all ? n : nc;
+        const uint16_t* xr = Xp + (size_t)t * D;
+        double bd = __builtin_inf();
+        int bi = 0x7fffffff;
+        for (int k = 0; k < m; ++k) {
+          const int cj = all ? k : s_cand[ts * kFixCand + k];
+          if ((unsigned)cj >= (unsigned)n) continue;
+          const float* cr = Cp + (size_t)cj * D;
+          double acc = 0.0;
+#pragma unroll 4
+          for (int q = 0; q < D / 8; ++q) {
+            const u32x4_t v = reinterpret_cast<const u32x4_t*>(xr)[q];
+            const float4 c0 = reinterpret_cast<const float4*>(cr)[2 * q];
+            const float4 c1 = reinterpret_cast<const float4*>(cr)[2 * q + 1];
+            const double e0 = (double)bf16_lo(v[0]) - c0.x, e1 = (double)bf16_hi(v[0]) - c0.y;
+            const double e2 = (double)bf16_lo(v[1]) - c0.z, e3 = (double)bf16_hi(v[1]) - c0.w;
+            const double e4 = (double)bf16_lo(v[2]) - c1.x, e5 = (double)bf16_hi(v[2]) - c1.y;
+            const double e6 = (double)bf16_lo(v[3]) - c1.z, e7 = (double)bf16_hi(v[3]) - c1.w;
+            acc = fma(e0, e0, acc); acc = fma(e1, e1, acc); acc = fma(e2, e2, acc); acc = fma(e3, e3, acc);
+            acc = fma(e4, e4, acc); acc = fma(e5, e5, acc); acc = fma(e6, e6, acc); acc = fma(e7, e7, acc);
+          }
+          if (acc < bd || (acc == bd && cj < bi)) {
+            bd = acc;
+            bi = cj;
+          }
+        }
+        if (m > 0) {
+          labels[(size_t)p * N + t] = bi;
+          if (min_dist) min_dist[(size_t)p * N + t] = (float)bd;
+        }
+      }
+      li0 += (int)gridDim.x * kAsgTok;
+      if (li0 >= nfix) return;
+      __syncthreads();                           // s_ncand and the ring are reused
     }
   }
 }
@@ -753,15 +911,25 @@ __global__ __launch_bounds__(256) void k_assign_f32(const float* __restrict__ X,
 
 hipError_t launch_assign(const void* x, bool bf16, int bh, int N, int d, int n, const float* c,
                          const uint16_t* c_hi, const uint16_t* c_lo, const float* c_norm,
-                         int32_t* labels, float* min_dist, hipStream_t s) {
+                         int32_t* labels, float* min_dist, const AsgFixWs& fw, hipStream_t s) {
   if (bf16) {
-    const dim3 grid((N + 4 * kAsgTB * 32 - 1) / (4 * kAsgTB * 32), bh);
-    if (d == 128)
-      hipLaunchKernelGGL(k_assign_bf16<128>, grid, dim3(256), 0, s, static_cast<const uint16_t*>(x), N, n,
-                         c_hi, c_lo, c_norm, labels, min_dist);
-    else
-      hipLaunchKernelGGL(k_assign_bf16<64>, grid, dim3(256), 0, s, static_cast<const uint16_t*>(x), N, n,
-                         c_hi, c_lo, c_norm, labels, min_dist);
+    const AsgFix fx{fw.count, fw.token, fw.dmin, c};
+    const dim3 grid((N + kAsgTok - 1) / kAsgTok, bh);
+    // the near-tie pass: enough work-groups per problem for 1/16 of the tokens
+    // per sweep; each loops over the list until it is done
+    const dim3 gfix((N + 16 * kAsgTok - 1) / (16 * kAsgTok), bh);
+    const uint16_t* xt = static_cast<const uint16_t*>(x);
+    if (d == 128) {
+      hipLaunchKernelGGL((k_assign_bf16<128, false>), grid, dim3(256), 0, s, xt, N, n, c_hi, c_lo, c_norm, labels,
+                         min_dist, fx);
+      hipLaunchKernelGGL((k_assign_bf16<128, true>), gfix, dim3(256), 0, s, xt, N, n, c_hi, c_lo, c_norm, labels,
+                         min_dist, fx);
+    } else {
+      hipLaunchKernelGGL((k_assign_bf16<64, false>), grid, dim3(256), 0, s, xt, N, n, c_hi, c_lo, c_norm, labels,
+                         min_dist, fx);
+      hipLaunchKernelGGL((k_assign_bf16<64, true>), gfix, dim3(256), 0, s, xt, N, n, c_hi, c_lo, c_norm, labels,
+                         min_dist, fx);
+    }
   } else {
     const dim3 grid((N + 255) / 256, bh);
     if (d == 128)

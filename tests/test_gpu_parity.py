@@ -290,6 +290,40 @@ def test_kmeans_one_round_vs_oracle(dt, d, N, n):
         assert np.all(np.abs(got - C) <= 1e-5 * np.maximum(1.0, np.abs(C)))
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_assign_near_ties_decided_exactly(d):
+    """Centroids built to put many tokens at near ties: an exact duplicate
+    (ties go to the lower index), a copy moved by ~1e-6 relative (margins far
+    inside the matrix-core error bound, decided again in fp64), and a group of
+    20 copies moved by ~1e-7 (more near candidates than the per-token list
+    holds: every centroid is then evaluated in fp64).  Labels must equal the
+    oracle's for every token outside a 1e-12 relative band, min-distances
+    within fp32 rounding of the oracle's."""
+    bh, N, n = 2, 4000, 64
+    q, _, _ = mixture(bh, N, d, comps=24, seed=17 + d, dtype=torch.bfloat16)
+    rng = np.random.default_rng(d)
+    init = np.stack([np64(q[h])[rng.choice(N, n, replace=False)] for h in range(bh)])
+    init = init + 0.05 * rng.standard_normal(init.shape)
+    init[:, 1] = init[:, 0]
+    init[:, 2] = init[:, 3] * (1 + 1e-6 * rng.standard_normal((bh, d)))
+    init[:, 10:30] = init[:, 9:10] * (1 + 1e-7 * rng.standard_normal((bh, 20, d)))
+    init32 = init.astype(np.float32)
+    r = B.kmeans(q.to(DEV), n, 1, init=torch.from_numpy(init32).to(DEV), min_dist=True)
+    torch.cuda.synchronize()
+    for h in range(bh):
+        X = np64(q[h])
+        C0 = init32[h].astype(np.float64)
+        a = oracle.assign(X, C0)
+        lab = r["labels"][h].cpu().numpy()
+        near = a.margin < 1e-5
+        print(f"head {h}: {int(near.sum())} tokens with margin < 1e-5", flush=True)
+        assert near.sum() >= 50                          # the case exercises the near-tie pass
+        check_labels_in_tie_band(X, C0, lab, a, max_share=0.5)
+        assert not np.any(lab == 1)                      # the duplicate of centroid 0 never wins
+        np.testing.assert_array_equal(r["counts"][h].cpu().numpy(), np.bincount(lab, minlength=n))
+        np.testing.assert_allclose(r["min_dist"][h].cpu().numpy(), a.min_dist, rtol=1e-4, atol=1e-3)
+
+
 def test_kmeans_chained_rounds_equal_one_call():
     """T chained one-round calls equal one T-round call, bit for bit."""
     bh, N, d, n = 2, 5000, 128, 40
