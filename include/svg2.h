@@ -267,6 +267,32 @@ int svg2_varblock_attn_unpermute(const void* q, const void* k, const void* v, in
                                  size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * svg2_varblock_attn_noalloc - svg2_varblock_attn with no workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, serving loops that must not call hipMalloc, harnesses that
+ * forbid it.  Same arguments (minus workspace), same results, same kernels.
+ *
+ *   Scratch: a fixed array of svg2_varblock_attn_noalloc_max_scratch() bytes
+ *   (16 MiB) inside the library, one per GPU, held until the process ends;
+ *   its device address is resolved on the first call on each device.  The
+ *   call allocates and frees nothing.
+ *   Limit: a problem whose svg2_varblock_attn_workspace_size exceeds that
+ *   size returns SVG2_ERR_WORKSPACE before any HIP call (at head_dim 128 and
+ *   400 / 1000 clusters: 24 x 118,800 tokens needs 3.2 MiB, 40 x 75,600
+ *   needs 3.9 MiB).  Argument errors are those of svg2_varblock_attn.
+ *   Concurrency: every call on one GPU uses that GPU's one array, so calls
+ *   that overlap on one GPU (several streams or threads) race; calls queued
+ *   in order on one stream are safe.  Nothing needs clearing between calls.
+ * ---------------------------------------------------------------------- */
+size_t svg2_varblock_attn_noalloc_max_scratch(void);
+int svg2_varblock_attn_noalloc(const void* q, const void* k, const void* v, int32_t dtype,
+                               int32_t bh, int32_t n_tokens, int32_t head_dim,
+                               const int32_t* q_offsets, int32_t n_q,
+                               const int32_t* k_offsets, int32_t n_k,
+                               const int32_t* sel_count, const int32_t* sel_idx, float scale,
+                               void* out, float* lse, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * svg2_unpermute - scatter rows back to the original token order:
  * dst row perm[i] = src row i  [Method, stage (2)].
  *

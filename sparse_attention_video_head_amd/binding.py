@@ -34,6 +34,7 @@ EXPORTED = [
     "svg2_cluster_means_workspace_size", "svg2_cluster_means", "svg2_recall_mass",
     "svg2_quantize_fp8_workspace_size", "svg2_quantize_fp8", "svg2_varblock_attn_fp8",
     "svg2_varblock_attn_fp8_unpermute",
+    "svg2_varblock_attn_noalloc_max_scratch", "svg2_varblock_attn_noalloc",
 ]
 
 
@@ -109,6 +110,11 @@ def lib() -> ctypes.CDLL:
     L.svg2_varblock_attn_fp8_unpermute.argtypes = [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_p,
                                                    _c_int, _c_p, _c_int, _c_p, _c_p, ctypes.c_float, _c_p, _c_p,
                                                    _c_int, _c_i64, _c_i64, _c_i64, _c_p, _c_p, _c_sz, _c_p]
+    L.svg2_varblock_attn_noalloc_max_scratch.restype = _c_sz
+    L.svg2_varblock_attn_noalloc_max_scratch.argtypes = []
+    L.svg2_varblock_attn_noalloc.restype = ctypes.c_int
+    L.svg2_varblock_attn_noalloc.argtypes = [_c_p, _c_p, _c_p, _c_int, _c_int, _c_int, _c_int, _c_p, _c_int, _c_p,
+                                             _c_int, _c_p, _c_p, ctypes.c_float, _c_p, _c_p, _c_p]
     _lib = L
     return L
 
@@ -432,6 +438,30 @@ def varblock_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_offsets: 
                              _ptr(out), _ptr(ls), _ptr(ws), ws_n, _stream(dev))
     _check(s, "svg2_varblock_attn")
     return out, ls
+
+
+def varblock_attn_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_offsets: torch.Tensor,
+                          k_offsets: torch.Tensor, sel_count: torch.Tensor, sel_idx: torch.Tensor,
+                          out: torch.Tensor, lse: Optional[torch.Tensor] = None, scale: Optional[float] = None):
+    """varblock_attn through svg2_varblock_attn_noalloc: no workspace, the
+    library's fixed scratch array instead; ``out`` (and ``lse``) must be given,
+    so that nothing on this path allocates."""
+    _need_cuda(q, k, v, q_offsets, k_offsets, sel_count, sel_idx, out, lse)
+    if q.dim() != 3:
+        raise Svg2Error("q, k, v must be contiguous [bh, N, d] tensors of one dtype")
+    bh, N, d = q.shape
+    dev = q.device
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        _need_out(t, q.shape, q.dtype, dev, name)
+    n_q, n_k = _lists(bh, dev, q_offsets, k_offsets, sel_count, sel_idx)
+    _need_out(lse, (bh, N), torch.float32, dev, "lse")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    s = lib().svg2_varblock_attn_noalloc(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), bh, N, d, _ptr(q_offsets), n_q,
+                                         _ptr(k_offsets), n_k, _ptr(sel_count), _ptr(sel_idx), ctypes.c_float(scale),
+                                         _ptr(out), _ptr(lse), _stream(dev))
+    _check(s, "svg2_varblock_attn_noalloc")
+    return out, lse
 
 
 def varblock_attn_unpermute(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_offsets: torch.Tensor,

@@ -19,7 +19,7 @@ LIB_NAME = "libsvg2.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["abi.cpp", "sort.hip", "kmeans.hip", "select.hip", "attn.hip", "recall.hip", "quant.hip"]
+SOURCES = ["abi.cpp", "sort.hip", "kmeans.hip", "select.hip", "attn.hip", "recall.hip", "quant.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 

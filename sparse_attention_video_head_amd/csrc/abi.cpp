@@ -203,6 +203,10 @@ int attn_fp8_run(const void* q8, const void* k8, const void* v8, const float* q_
 
 }  // namespace
 
+namespace svg2 {
+void record_hip_error(int e) { g_last_hip_error = e; }
+}  // namespace svg2
+
 extern "C" {
 
 const char* svg2_version(void) { return "svg2-mi355x 0.1.0 (gfx950)"; }

@@ -6,6 +6,9 @@
 
 namespace svg2 {
 
+// the thread's SVG2_ERR_HIP cause, as svg2_last_hip_error() reports it
+void record_hip_error(int e);
+
 constexpr int kMaxClusters = 4096;
 constexpr int kSortChunk = 1024;             // tokens per counting-sort chunk
 inline int sort_chunks(int n_tokens) { return (n_tokens + kSortChunk - 1) / kSortChunk; }
