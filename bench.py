@@ -87,7 +87,7 @@ def parse():
     ap.add_argument("--warm-iters", type=int, default=2)
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work in the CPU leg")
+    ap.add_argument("--cpu-budget", type=float, default=30.0, help="seconds of oracle work in the CPU leg")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (counter calibration)")
     ap.add_argument("--denoise", action="store_true",
@@ -144,12 +144,13 @@ def cpu_baseline(host, cfg, top_p, budget_s):
     """The fp64 oracle as it stands, timed on the host on a bounded sample of
     the same layer, scaled to the metric's unit.
 
-    Sample (one head, head 0): k-means++ for the first m picks of each side
-    (time per pick x n picks), one Lloyd round per side (x rounds), the full
+    Sample (one head, head 0): k-means++ for the first 100 picks of each side
+    (time per pick x n picks), all Lloyd rounds of both sides, the full
     permutation / selection / un-permutation of the head, and block attention
-    for Q-clusters taken in order until the attention budget is spent (time
-    per query-key pair x the head's pairs).  The head's time x heads is the
-    extrapolated layer time; value = the layer's attention flops / that time.
+    for Q-clusters taken in order until the remaining budget is spent (every
+    Q-cluster when it allows; else time per query-key pair x the head's
+    pairs).  The head's time x heads is the extrapolated layer time; value =
+    the layer's attention flops / that time.
     """
     import numpy as np
     import oracle
@@ -162,8 +163,9 @@ def cpu_baseline(host, cfg, top_p, budget_s):
     N, d = X["q"].shape
     scale = 1.0 / math.sqrt(d)
     T = {}
-    t = time.perf_counter()
-    m = 8
+    t_start = time.perf_counter()
+    t = t_start
+    m = min(100, cfg.n_q, cfg.n_k)
     sq = oracle.kmeanspp(X["q"], m, seed=1)
     sk = oracle.kmeanspp(X["k"], m, seed=2)
     per_pick = (time.perf_counter() - t) / (2 * m)
@@ -172,9 +174,9 @@ def cpu_baseline(host, cfg, top_p, budget_s):
     rng = np.random.default_rng(0)
     cq0 = X["q"][rng.choice(N, cfg.n_q, replace=False)]
     ck0 = X["k"][rng.choice(N, cfg.n_k, replace=False)]
-    kq = oracle.kmeans(X["q"], cfg.n_q, 1, init=cq0)
-    kk = oracle.kmeans(X["k"], cfg.n_k, 1, init=ck0)
-    T["lloyd"] = (time.perf_counter() - t) * cfg.iters
+    kq = oracle.kmeans(X["q"], cfg.n_q, cfg.iters, init=cq0)
+    kk = oracle.kmeans(X["k"], cfg.n_k, cfg.iters, init=ck0)
+    T["lloyd"] = time.perf_counter() - t
     t = time.perf_counter()
     pq, oq, _ = oracle.counting_sort(kq.labels, cfg.n_q)
     pk, ok, _ = oracle.counting_sort(kk.labels, cfg.n_k)
@@ -185,8 +187,9 @@ def cpu_baseline(host, cfg, top_p, budget_s):
     head_pairs = oracle.pair_count(sel.lists, kq.counts, kk.counts)
     t = time.perf_counter()
     done_pairs, clusters = 0, []
+    attn_budget = max(budget_s - (t - t_start), 0.3 * budget_s)
     for i in range(cfg.n_q):
-        if time.perf_counter() - t > 0.6 * budget_s:
+        if time.perf_counter() - t > attn_budget:
             break
         oracle.block_attention(qp, kp, vp, oq, ok, sel.lists, scale, q_clusters=[i])
         done_pairs += int(kq.counts[i]) * int(np.sum(kk.counts[sel.lists[i]]))
@@ -201,9 +204,11 @@ def cpu_baseline(host, cfg, top_p, budget_s):
     layer_flops = 4.0 * d * head_pairs * cfg.bh
     return {"value": round(layer_flops / layer_s / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
-            "sample": (f"head 0 of {cfg.bh}: k-means++ {m} picks per side, 1 Lloyd round per side, full "
-                       f"permute/select/un-permute, attention on {len(clusters)} of {cfg.n_q} Q-clusters "
-                       f"({done_pairs} of {head_pairs} pairs); extrapolated x{cfg.bh} heads"),
+            "sample": (f"head 0 of {cfg.bh}: k-means++ {m} picks per side (scaled to {cfg.n_q} + {cfg.n_k}), "
+                       f"all {cfg.iters} Lloyd rounds per side, full permute/select/un-permute, attention on "
+                       f"{len(clusters)} of {cfg.n_q} Q-clusters ({done_pairs} of {head_pairs} pairs); "
+                       f"extrapolated x{cfg.bh} heads"),
+            "sample_s": round(time.perf_counter() - t_start, 2),
             "layer_s_extrapolated": round(layer_s, 2),
             "stage_s_per_head": {k_: round(v_, 3) for k_, v_ in T.items()}}
 

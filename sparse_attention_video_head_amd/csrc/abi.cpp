@@ -81,6 +81,7 @@ KmeansWs carve_kmeans(Carve& c, int bh, int N, int d, int n) {
   w.fix.count = c.take<int32_t>((size_t)bh);
   w.fix.token = c.take<int32_t>(bN);
   w.fix.dmin = c.take<float>(bN);
+  w.fix.hist = w.hist;
   return w;
 }
 
@@ -158,7 +159,8 @@ int kmeans_run(const void* x, int32_t dtype, int32_t bh, int32_t n_tokens, int32
   }
   for (int it = 0; it < n_iters; ++it) {
     if (bf16) {
-      st = hip_status(launch_prep_centroids(centroids, bh, n, d, w.c_hi, w.c_lo, w.c_norm, w.fix.count, stream));
+      const SortStart ss{w.fix.count, w.hist, (size_t)bh * sort_chunks(N) * n};
+      st = hip_status(launch_prep_centroids(centroids, bh, n, d, w.c_hi, w.c_lo, w.c_norm, ss, stream));
       if (st) return st;
     }
     st = hip_status(launch_assign(x, bf16, bh, N, d, n, centroids, w.c_hi, w.c_lo, w.c_norm, labels,
@@ -167,7 +169,7 @@ int kmeans_run(const void* x, int32_t dtype, int32_t bh, int32_t n_tokens, int32
     const bool last = it == n_iters - 1 && mv.x_out;
     int32_t* pm = last ? perm_out : w.perm;
     int32_t* of = last ? offsets_out : w.offsets;
-    st = hip_status(launch_counting_sort(labels, bh, N, n, w.hist, pm, of, counts, stream));
+    st = hip_status(launch_counting_sort(labels, bh, N, n, w.hist, bf16, pm, of, counts, stream));
     if (st) return st;
     st = hip_status(launch_centroid_mean(x, bf16, bh, N, d, n, pm, of, w.partial, centroids, stream,
                                          last ? mv : MeanMove{}));
@@ -316,8 +318,8 @@ int svg2_permute(const int32_t* labels, int32_t bh, int32_t n_tokens, int32_t n_
   Carve c(workspace);
   int32_t* hist = c.take<int32_t>((size_t)bh * sort_chunks(n_tokens) * n_clusters);
   int32_t* counts = c.take<int32_t>((size_t)bh * n_clusters);
-  int st = hip_status(launch_counting_sort(labels, bh, n_tokens, n_clusters, hist, perm, offsets,
-                                           counts, stream));
+  int st = hip_status(launch_counting_sort(labels, bh, n_tokens, n_clusters, hist, false, perm, offsets, counts,
+                                           stream));
   if (st) return st;
   return hip_status(launch_gather_rows(n_tensors, src, dst, esize(dtype), head_dim, bh, n_tokens, heads,
                                        src_b_stride, src_h_stride, src_token_stride, perm, stream));
@@ -515,7 +517,8 @@ int svg2_cluster_means(const void* x, int32_t dtype, int32_t bh, int32_t n_token
   int32_t* perm = c.take<int32_t>((size_t)bh * n_tokens);
   int32_t* offsets = c.take<int32_t>((size_t)bh * (n_clusters + 1));
   double* partial = c.take<double>((size_t)bh * (n_clusters + mean_chunks(n_tokens)) * head_dim);
-  int st = hip_status(launch_counting_sort(labels, bh, n_tokens, n_clusters, hist, perm, offsets, counts, stream));
+  int st = hip_status(launch_counting_sort(labels, bh, n_tokens, n_clusters, hist, false, perm, offsets, counts,
+                                           stream));
   if (st) return st;
   return hip_status(launch_centroid_mean(x, dtype == SVG2_BF16, bh, n_tokens, head_dim, n_clusters, perm, offsets,
                                          partial, means, stream));

@@ -3,14 +3,17 @@
 //
 // Work item = (problem, Q-cluster i, 128-row slab of that cluster).  The key
 // list of item i is the concatenation of the key ranges of its selected
-// K-clusters; it is walked in tiles of 64 keys that may straddle cluster
-// boundaries, so the only padding is the tail of the whole list (and of the
-// query slab), not a round-up of every cluster to a fixed block size.
+// K-clusters; it is walked in tiles of 32 keys (bf16; 64 for FP8) that may
+// straddle cluster boundaries, so the only padding is the tail of the whole
+// list (and of the query slab), not a round-up of every cluster to a fixed
+// block size.
 //
 // bf16 kernel, one wave = 32 query rows, 4 waves share each K/V tile in LDS:
 //   S^T = K Q^T        v_mfma_f32_32x32x16_bf16, K tile from LDS, Q in registers
 //   online softmax     fp32, base 2 (scale * log2 e folded in), per lane: one
-//                      query, 32 keys; one cross-half exchange for the max
+//                      query, 16 of the tile's keys; one cross-half exchange
+//                      for the max; the row sum adds the bf16-rounded P that
+//                      weight V, so the normaliser is the sum of the weights
 //   O^T += V^T P^T     P re-used straight from the S accumulator (no shuffle):
 //                      the key order inside each 16-key MFMA step is permuted,
 //                      and V^T is staged in LDS in the same permuted order.
@@ -971,8 +974,12 @@ __global__ __launch_bounds__(256, 3) void k_attn_fp8(
       cur.init(sel_idx + ((size_t)p * n_q + ci) * n_k, k_off + (size_t)p * (n_k + 1),
                clampi(sel_count[(size_t)p * n_q + ci], 0, n_k), n_k, N, s_rs, s_rl);
 
+      // softmax state as in the bf16 kernel: reference max m_ref (log2 units),
+      // the raw score thr that moves it, two row-sum accumulators
       float m_ref = -__builtin_inff();
-      float l_part = 0.f;
+      float thr = -__builtin_inff();
+      const float inv_sl2 = 1.f / sl2;
+      float l_a = 0.f, l_b = 0.f;
       f32x16_t o[4];
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
@@ -1023,23 +1030,27 @@ __global__ __launch_bounds__(256, 3) void k_attn_fp8(
             for (int i = 0; i < 16; ++i)
               if (32 * t + (i >> 2) * 8 + (i & 3) >= lim) sc[t][i] = -__builtin_inff();
         }
+        // raw tile max (v_maximum3: no canonicalising of the MFMA results)
         float mx = sc[0][0];
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[t][i]);
+          for (int i = (t == 0 ? 1 : 0); i < 16; ++i) mx = __builtin_elementwise_maximum(mx, sc[t][i]);
         {
           const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-          mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * sl2;
+          mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
         }
-        if (mx > m_ref + kLazyTau) {
-          const float alpha = __builtin_amdgcn_exp2f(m_ref - mx);
-          l_part *= alpha;
+        if (mx > thr) {
+          const float m_new = mx * sl2;
+          const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+          l_a *= alpha;
+          l_b *= alpha;
 #pragma unroll
           for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
-          m_ref = mx;
+          m_ref = m_new;
+          thr = (m_new + kLazyTau) * inv_sl2;
         }
         const float neg = -m_ref;
         i32x8_t pf;
@@ -1051,7 +1062,10 @@ __global__ __launch_bounds__(256, 3) void k_attn_fp8(
             const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[t][i + 1], sl2, neg));
             const float p2 = __builtin_amdgcn_exp2f(fmaf(sc[t][i + 2], sl2, neg));
             const float p3 = __builtin_amdgcn_exp2f(fmaf(sc[t][i + 3], sl2, neg));
-            l_part += (p0 + p1) + (p2 + p3);
+            if (i & 4)
+              l_b += (p0 + p1) + (p2 + p3);
+            else
+              l_a += (p0 + p1) + (p2 + p3);
             int w = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
             w = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, w, true);
             pf[4 * t + (i >> 2)] = w;
@@ -1135,6 +1149,7 @@ __global__ __launch_bounds__(256, 3) void k_attn_fp8(
 
       float l_tot;
       {
+        const float l_part = l_a + l_b;
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part), __float_as_uint(l_part), false, false);
         l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
       }

@@ -11,12 +11,15 @@ void record_hip_error(int e);
 
 constexpr int kMaxClusters = 4096;
 constexpr int kSortChunk = 1024;             // tokens per counting-sort chunk
-inline int sort_chunks(int n_tokens) { return (n_tokens + kSortChunk - 1) / kSortChunk; }
+__host__ __device__ inline int sort_chunks(int n_tokens) { return (n_tokens + kSortChunk - 1) / kSortChunk; }
 
 // ----------------------------------------------------------------- sort.hip
 // Stable counting sort of labels [bh, N] in [0, n): perm, offsets [bh, n+1],
 // counts [bh, n] (required).  hist_ws holds bh * sort_chunks(N) * n ints.
-hipError_t launch_counting_sort(const int32_t* labels, int bh, int N, int n, int32_t* hist_ws,
+// With have_hist the chunk histograms are already in hist_ws (the bf16
+// assignment adds them, after a k_prep_centroids that cleared them);
+// otherwise the sort builds them.
+hipError_t launch_counting_sort(const int32_t* labels, int bh, int N, int n, int32_t* hist_ws, bool have_hist,
                                 int32_t* perm, int32_t* offsets, int32_t* counts, hipStream_t s);
 // dst[t][p][i][:] = src[t] row perm[p][i] of problem p (strided source), t < n_tensors <= 2.
 hipError_t launch_gather_rows(int n_tensors, const void* const* src, void* const* dst, int esize,
@@ -39,15 +42,23 @@ hipError_t launch_kmeanspp(const void* x, bool bf16, int bh, int N, int d, int n
 // kCentroidPad-row padded per problem (padding rows: zeros, ||c||^2 = +inf)
 constexpr int kCentroidPad = 32;
 __host__ __device__ inline int centroid_rows(int n) { return (n + kCentroidPad - 1) / kCentroidPad * kCentroidPad; }
-// (also empties the per-problem near-tie lists of the next bf16 assignment)
+// What the prep clears for the round's assignment and sort: the near-tie
+// counts [bh] and the chunk histograms (hist_words ints).
+struct SortStart {
+  int32_t* fix_count;
+  int32_t* hist;
+  size_t hist_words;
+};
 hipError_t launch_prep_centroids(const float* c, int bh, int n, int d, uint16_t* c_hi,
-                                 uint16_t* c_lo, float* c_norm, int32_t* fix_count, hipStream_t s);
+                                 uint16_t* c_lo, float* c_norm, const SortStart& st, hipStream_t s);
 // Near ties of the bf16 assignment, decided again in fp64: count [bh], token
-// and dmin [bh, N] (the listed tokens and their smallest matrix-core distance).
+// and dmin [bh, N] (the listed tokens and their smallest matrix-core distance);
+// hist: the counting sort's chunk histograms, which the assignment fills.
 struct AsgFixWs {
   int32_t* count;
   int32_t* token;
   float* dmin;
+  int32_t* hist;
 };
 hipError_t launch_assign(const void* x, bool bf16, int bh, int N, int d, int n, const float* c,
                          const uint16_t* c_hi, const uint16_t* c_lo, const float* c_norm,

@@ -493,14 +493,23 @@ hipError_t launch_kmeanspp(const void* x, bool bf16, int bh, int N, int d, int n
 __global__ __launch_bounds__(256) void k_prep_centroids(const float* __restrict__ c, int bh, int n, int npad,
                                                         int d, uint16_t* __restrict__ hi,
                                                         uint16_t* __restrict__ lo,
-                                                        float* __restrict__ cn,
-                                                        int32_t* __restrict__ fix_count) {
+                                                        float* __restrict__ cn, SortStart st) {
+  // The round's counting sort starts from zero: the near-tie lists and the
+  // chunk histograms the assignment adds its labels to (a grid-stride pass,
+  // four ints per store).
+  {
+    const size_t nthreads = (size_t)gridDim.x * blockDim.x;
+    const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t words = st.hist_words / 4;
+    int4* h4 = reinterpret_cast<int4*>(st.hist);
+    for (size_t i = gid; i < words; i += nthreads) h4[i] = make_int4(0, 0, 0, 0);
+    for (size_t i = words * 4 + gid; i < st.hist_words; i += nthreads) st.hist[i] = 0;
+    for (size_t i = gid; i < (size_t)bh; i += nthreads) st.fix_count[i] = 0;
+  }
   const int row = blockIdx.x * 4 + threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   if (row >= bh * npad) return;
   const int p = row / npad, j = row % npad;
-  // the round's near-tie list starts empty (the assignment appends to it)
-  if (j == 0 && lane == 0) fix_count[p] = 0;
   if (j >= n) {
     for (int e = lane; e < d; e += kWave) {
       hi[(size_t)row * d + e] = 0;
@@ -527,11 +536,11 @@ __global__ __launch_bounds__(256) void k_prep_centroids(const float* __restrict_
 }
 
 hipError_t launch_prep_centroids(const float* c, int bh, int n, int d, uint16_t* c_hi,
-                                 uint16_t* c_lo, float* c_norm, int32_t* fix_count, hipStream_t s) {
+                                 uint16_t* c_lo, float* c_norm, const SortStart& st, hipStream_t s) {
   const int npad = centroid_rows(n);
   const int rows = bh * npad;
   hipLaunchKernelGGL(k_prep_centroids, dim3((rows + 3) / 4), dim3(256), 0, s, c, bh, n, npad, d, c_hi, c_lo,
-                     c_norm, fix_count);
+                     c_norm, st);
   return hipGetLastError();
 }
 
@@ -558,9 +567,10 @@ hipError_t launch_prep_centroids(const float* c, int bh, int n, int d, uint16_t*
 // listed tokens, keeps every centroid whose a is within 2E of that smallest
 // value (the true nearest is among them), and decides between those with
 // exact fp64 distances (ties to the lowest index).
-constexpr int kAsgTB = 4;                 // 32-token blocks per wave
+constexpr int kAsgTB = 4;                 // 32-token blocks per wave (the near-tie pass: 1)
 constexpr int kAsgCB = kCentroidPad;      // centroids per LDS chunk
-constexpr int kAsgTok = 4 * kAsgTB * 32;  // tokens per work-group
+constexpr int asg_tb(bool fix) { return fix ? 1 : kAsgTB; }
+constexpr int asg_tok(bool fix) { return 4 * asg_tb(fix) * 32; }   // tokens per work-group
 constexpr int kFixCand = 16;              // candidate centroids kept per listed token
 
 // s_waitcnt immediates (vmcnt only; expcnt and lgkmcnt not waited for)
@@ -583,6 +593,7 @@ struct AsgFix {
   int32_t* token;         // [bh, N] listed tokens
   float* dmin;            // [bh, N] their smallest matrix-core distance
   const float* C;         // [bh, n, D] fp32 centroids (the exact values)
+  int32_t* hist;          // [bh, sort_chunks(N), n] label counts per counting-sort chunk
 };
 
 template <int D, bool FIX>
@@ -602,6 +613,8 @@ __global__ __launch_bounds__(256, 2) void k_assign_bf16(const uint16_t* __restri
   static_assert(INS >= 1 && kAsgCB == 32, "chunk geometry");
   // ring slot j: hi rows [0, CB*D), lo rows [CB*D, 2*CB*D), then CB norms
   constexpr int SLOT = 2 * kAsgCB * D + 2 * kAsgCB;   // uint16 elements
+  constexpr int kAsgTB = asg_tb(FIX);        // this pass's token blocks per wave
+  constexpr int kAsgTok = asg_tok(FIX);
   __shared__ __attribute__((aligned(16))) uint16_t sC0[SLOT], sC1[SLOT], sC2[SLOT], sC3[SLOT];
   // FIX: candidate centroids per listed token (token slot = wave, block, column)
   __shared__ int32_t s_cand[FIX ? kAsgTok * kFixCand : 1];
@@ -757,24 +770,27 @@ __global__ __launch_bounds__(256, 2) void k_assign_bf16(const uint16_t* __restri
       __syncthreads();                           // s_ncand cleared
     }
 
-    // prologue: chunks 0..2 in flight, chunks 0 and 1 landed
+    // prologue: chunks 0..2 in flight, chunk 0 landed
     load_chunk(0, sC0);
     load_chunk(1, sC1);
     load_chunk(2, sC2);
     constexpr int kLoadsPerChunk = 2 * INS + 1;   // wave 0 issues one more (the norms)
-    if (wave == 0) __builtin_amdgcn_s_waitcnt(asg_wait_vm(kLoadsPerChunk));
-    else __builtin_amdgcn_s_waitcnt(asg_wait_vm(2 * INS));
+    if (wave == 0) __builtin_amdgcn_s_waitcnt(asg_wait_vm(2 * kLoadsPerChunk));
+    else __builtin_amdgcn_s_waitcnt(asg_wait_vm(4 * INS));
     lds_barrier_asg();
-    // chunk c: compute slot c % 4, load chunk c + 3 into slot (c + 3) % 4; the
-    // first chunk of each trip loads after computing (at the loop head the
-    // compiler's tracking of the loads is lost and it would wait for all of them)
+    // chunk c: compute slot c % 4, load chunk c + 3 into slot (c + 3) % 4 (the
+    // slot of chunk c - 1, which every wave finished before the last barrier),
+    // then wait only for chunk c + 1, the next one computed: chunks c + 2 and
+    // c + 3 stay in flight.  The first chunk of each trip loads after computing
+    // (at the loop head the compiler's tracking of the loads is lost and it
+    // would wait for all of them).
     int c = 0;
     auto iter = [&](auto late, const uint16_t* cur, uint16_t* nxt) __attribute__((always_inline)) -> bool {
       if constexpr (!decltype(late)::value) load_chunk(c + 3, nxt);
       compute(cur, c * kAsgCB);
       if constexpr (decltype(late)::value) load_chunk(c + 3, nxt);
-      if (wave == 0) __builtin_amdgcn_s_waitcnt(asg_wait_vm(kLoadsPerChunk));
-      else __builtin_amdgcn_s_waitcnt(asg_wait_vm(2 * INS));
+      if (wave == 0) __builtin_amdgcn_s_waitcnt(asg_wait_vm(2 * kLoadsPerChunk));
+      else __builtin_amdgcn_s_waitcnt(asg_wait_vm(4 * INS));
       lds_barrier_asg();
       return ++c < nchunk;
     };
@@ -802,6 +818,8 @@ __global__ __launch_bounds__(256, 2) void k_assign_bf16(const uint16_t* __restri
         if (half == 0 && t >= 0) {
           labels[(size_t)p * N + t] = bidx[tb];
           if (min_dist) min_dist[(size_t)p * N + t] = fmaxf(xn[tb] + best[tb], 0.f);
+          // the counting sort's histogram of this chunk (integer adds: exact)
+          atomicAdd(&fx.hist[((size_t)p * sort_chunks(N) + t / kSortChunk) * n + bidx[tb]], 1);
         }
         // near ties to the fix list: one counter bump per wave
         const uint64_t m = __ballot(tie);
@@ -857,8 +875,15 @@ __global__ __launch_bounds__(256, 2) void k_assign_bf16(const uint16_t* __restri
           }
         }
         if (m > 0) {
+          const int old = labels[(size_t)p * N + t];
           labels[(size_t)p * N + t] = bi;
           if (min_dist) min_dist[(size_t)p * N + t] = (float)bd;
+          if (old != bi) {
+            // move the token between its chunk's histogram bins
+            int32_t* hrow = fx.hist + ((size_t)p * sort_chunks(N) + t / kSortChunk) * n;
+            atomicSub(&hrow[clampi(old, 0, n - 1)], 1);
+            atomicAdd(&hrow[bi], 1);
+          }
         }
       }
       li0 += (int)gridDim.x * kAsgTok;
@@ -913,11 +938,13 @@ hipError_t launch_assign(const void* x, bool bf16, int bh, int N, int d, int n, 
                          const uint16_t* c_hi, const uint16_t* c_lo, const float* c_norm,
                          int32_t* labels, float* min_dist, const AsgFixWs& fw, hipStream_t s) {
   if (bf16) {
-    const AsgFix fx{fw.count, fw.token, fw.dmin, c};
-    const dim3 grid((N + kAsgTok - 1) / kAsgTok, bh);
-    // the near-tie pass: enough work-groups per problem for 1/16 of the tokens
-    // per sweep; each loops over the list until it is done
-    const dim3 gfix((N + 16 * kAsgTok - 1) / (16 * kAsgTok), bh);
+    const AsgFix fx{fw.count, fw.token, fw.dmin, c, fw.hist};
+    const dim3 grid((N + asg_tok(false) - 1) / asg_tok(false), bh);
+    // the near-tie pass: enough work-groups per problem (128 tokens each) for
+    // a quarter of the tokens in one sweep over the centroids, so that the
+    // few percent of near ties finish in one sweep latency; work-groups past
+    // the list's end exit at once, and each loops if the list is longer
+    const dim3 gfix((N + 4 * asg_tok(true) - 1) / (4 * asg_tok(true)), bh);
     const uint16_t* xt = static_cast<const uint16_t*>(x);
     if (d == 128) {
       hipLaunchKernelGGL((k_assign_bf16<128, false>), grid, dim3(256), 0, s, xt, N, n, c_hi, c_lo, c_norm, labels,

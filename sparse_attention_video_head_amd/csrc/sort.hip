@@ -2,12 +2,15 @@
 // row gathers / scatters that move Q, K, V into contiguous cluster blocks and
 // the output back ("Sparse VideoGen2" wiki summary, Method, stage (2)).
 //
-// Sort: (1) per-chunk label histograms in LDS, (2) per cluster (one thread
-// each) the column of chunk counts becomes the chunk-relative start slots and
-// the cluster total, (3) one work-group per problem scans the totals into
-// cluster offsets, (4) one wave per chunk walks its tokens in order and places
-// each at offset[label] + start[chunk][label] + rank, the rank among equal
-// labels coming from wave ballots.
+// Sort: (1) per-chunk label histograms (in LDS by k_sort_hist, or by the bf16
+// assignment itself as it writes the labels), (2) per block of clusters the
+// column of chunk counts becomes the chunk-relative start slots and the
+// cluster totals, (3) per chunk, a scan of the totals gives the cluster
+// offsets and one wave walks the chunk's tokens in order and places each at
+// offset[label] + start[chunk][label] + rank, the rank among equal labels
+// coming from wave ballots.  (One launch for (2) and (3) would need a
+// device-scope release per work-group, which writes back the XCD's L2: slower
+// than the launch it saves.)
 // Integer only: results are exact and deterministic.
 #include "common.hpp"
 #include "internal.hpp"
@@ -28,73 +31,94 @@ __global__ __launch_bounds__(256) void k_sort_hist(const int32_t* __restrict__ l
   for (int c = threadIdx.x; c < n; c += blockDim.x) h[c] = sh[c];
 }
 
-// One thread per (problem, cluster): the cluster's counts in every chunk are
-// replaced by the number of its tokens in the earlier chunks; the total goes
-// to `counts`.  Consecutive threads read consecutive clusters of a chunk row.
+// Column scan.  Work-group (block of 32 clusters, problem): thread (cluster
+// c, part q of 8) adds the counts of c in its eighth of the chunks, the parts
+// are scanned in LDS, and a second walk over the same chunks (8 loads in
+// flight) turns each count into the number of c's tokens in the earlier
+// chunks, in place; the totals go to `counts`.
+constexpr int kScanClusters = 32;
+constexpr int kScanParts = 8;
+
 __global__ __launch_bounds__(256) void k_sort_columns(int n, int nchunks, int32_t* __restrict__ hist,
                                                       int32_t* __restrict__ counts) {
+  __shared__ int32_t s_part[kScanParts][kScanClusters];
   const int p = blockIdx.y;
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= n) return;
+  const int cl = threadIdx.x % kScanClusters, q = threadIdx.x / kScanClusters;
+  const int c = blockIdx.x * kScanClusters + cl;
+  const int per = (nchunks + kScanParts - 1) / kScanParts;
+  const int k0 = min(q * per, nchunks), k1 = min(k0 + per, nchunks);
   int32_t* h = hist + (size_t)p * nchunks * n + c;
-  int run = 0;
-  int ch = 0;
-  for (; ch + 4 <= nchunks; ch += 4) {
-    const int v0 = h[(size_t)ch * n], v1 = h[(size_t)(ch + 1) * n];
-    const int v2 = h[(size_t)(ch + 2) * n], v3 = h[(size_t)(ch + 3) * n];
-    h[(size_t)ch * n] = run;
-    h[(size_t)(ch + 1) * n] = run + v0;
-    h[(size_t)(ch + 2) * n] = run + v0 + v1;
-    h[(size_t)(ch + 3) * n] = run + v0 + v1 + v2;
-    run += v0 + v1 + v2 + v3;
+  int sum = 0;
+  if (c < n) {
+    int k = k0;
+    for (; k + 4 <= k1; k += 4)
+      sum += (h[(size_t)k * n] + h[(size_t)(k + 1) * n]) + (h[(size_t)(k + 2) * n] + h[(size_t)(k + 3) * n]);
+    for (; k < k1; ++k) sum += h[(size_t)k * n];
   }
-  for (; ch < nchunks; ++ch) {
-    const int v = h[(size_t)ch * n];
-    h[(size_t)ch * n] = run;
-    run += v;
+  s_part[q][cl] = sum;
+  __syncthreads();
+  int run = 0, total = 0;
+#pragma unroll
+  for (int j = 0; j < kScanParts; ++j) {
+    const int v = s_part[j][cl];
+    run += j < q ? v : 0;
+    total += v;
   }
-  counts[(size_t)p * n + c] = run;
+  if (c >= n) return;
+  for (int k = k0; k < k1; k += 8) {
+    int v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = k + j < k1 ? h[(size_t)(k + j) * n] : 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (k + j < k1) {
+        h[(size_t)(k + j) * n] = run;
+        run += v[j];
+      }
+  }
+  if (q == 0) counts[(size_t)p * n + c] = total;
 }
 
-// One work-group of 1024 threads per problem: exclusive scan of the cluster
-// totals (thread i owns clusters 4i..4i+3).
-__global__ __launch_bounds__(1024) void k_sort_offsets(int n, const int32_t* __restrict__ counts,
-                                                       int32_t* __restrict__ offsets) {
+// Placement, one work-group per chunk: the four waves scan the cluster totals
+// into offsets (chunk 0 also writes them out), each cluster's first slot in
+// this chunk is its offset plus its count in the earlier chunks, and wave 0
+// walks the chunk's tokens in order and places each at that slot plus its
+// rank among equal labels (wave ballots).
+__global__ __launch_bounds__(256) void k_sort_place(const int32_t* __restrict__ labels, int N, int n,
+                                                    int nchunks, int nbits,
+                                                    const int32_t* __restrict__ start,
+                                                    const int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ perm) {
+  extern __shared__ int32_t cnt[];
   __shared__ int32_t scratch[17];
-  const int p = blockIdx.x;
-  int tot[4];
+  const int chunk = blockIdx.x, p = blockIdx.y;
+  const int32_t* st = start + ((size_t)p * nchunks + chunk) * n;
+  const int32_t* tot = counts + (size_t)p * n;
+  constexpr int E = kMaxClusters / 256;
+  int v[E];
   int local = 0;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int c = 4 * threadIdx.x + e;
-    tot[e] = c < n ? counts[(size_t)p * n + c] : 0;
-    local += tot[e];
+  for (int e = 0; e < E; ++e) {
+    const int c = E * threadIdx.x + e;
+    v[e] = c < n ? tot[c] : 0;
+    local += v[e];
   }
-  int total;
-  int run = block_exclusive_scan(local, scratch, &total);
+  int grand;
+  int r = block_exclusive_scan(local, scratch, &grand);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int c = 4 * threadIdx.x + e;
-    if (c < n) offsets[(size_t)p * (n + 1) + c] = run;
-    run += tot[e];
+  for (int e = 0; e < E; ++e) {
+    const int c = E * threadIdx.x + e;
+    if (c < n) {
+      cnt[c] = r + st[c];
+      if (chunk == 0) offsets[(size_t)p * (n + 1) + c] = r;
+    }
+    r += v[e];
   }
-  if (threadIdx.x == 0) offsets[(size_t)p * (n + 1) + n] = total;
-}
-
-// One wave per chunk: stable placement.  The first slot of each cluster inside
-// this chunk is its offset plus its count in the earlier chunks.
-__global__ __launch_bounds__(64) void k_sort_place(const int32_t* __restrict__ labels, int N, int n,
-                                                   int nchunks, int nbits,
-                                                   const int32_t* __restrict__ start,
-                                                   const int32_t* __restrict__ offsets,
-                                                   int32_t* __restrict__ perm) {
-  extern __shared__ int32_t cnt[];
-  const int chunk = blockIdx.x, p = blockIdx.y;
-  const int lane = threadIdx.x;
-  const int32_t* st = start + ((size_t)p * nchunks + chunk) * n;
-  const int32_t* off = offsets + (size_t)p * (n + 1);
-  for (int c = lane; c < n; c += kWave) cnt[c] = off[c] + st[c];
+  if (chunk == 0 && threadIdx.x == 0) offsets[(size_t)p * (n + 1) + n] = grand;
   __syncthreads();
+  if (threadIdx.x >= kWave) return;
+  const int lane = threadIdx.x;
   const int32_t* lab = labels + (size_t)p * N;
   int32_t* out = perm + (size_t)p * N;
   const int t0 = chunk * kSortChunk, t1 = min(N, t0 + kSortChunk);
@@ -120,17 +144,18 @@ __global__ __launch_bounds__(64) void k_sort_place(const int32_t* __restrict__ l
   }
 }
 
-hipError_t launch_counting_sort(const int32_t* labels, int bh, int N, int n, int32_t* hist_ws,
+hipError_t launch_counting_sort(const int32_t* labels, int bh, int N, int n, int32_t* hist_ws, bool have_hist,
                                 int32_t* perm, int32_t* offsets, int32_t* counts, hipStream_t s) {
   const int nchunks = sort_chunks(N);
   int nbits = 0;
   while ((1 << nbits) < n) ++nbits;
   const size_t lds = (size_t)n * sizeof(int32_t);
-  hipLaunchKernelGGL(k_sort_hist, dim3(nchunks, bh), dim3(256), lds, s, labels, N, n, nchunks, hist_ws);
-  hipLaunchKernelGGL(k_sort_columns, dim3((n + 255) / 256, bh), dim3(256), 0, s, n, nchunks, hist_ws, counts);
-  hipLaunchKernelGGL(k_sort_offsets, dim3(bh), dim3(1024), 0, s, n, counts, offsets);
-  hipLaunchKernelGGL(k_sort_place, dim3(nchunks, bh), dim3(64), lds, s, labels, N, n, nchunks, nbits,
-                     hist_ws, offsets, perm);
+  if (!have_hist)
+    hipLaunchKernelGGL(k_sort_hist, dim3(nchunks, bh), dim3(256), lds, s, labels, N, n, nchunks, hist_ws);
+  hipLaunchKernelGGL(k_sort_columns, dim3((n + kScanClusters - 1) / kScanClusters, bh), dim3(256), 0, s, n,
+                     nchunks, hist_ws, counts);
+  hipLaunchKernelGGL(k_sort_place, dim3(nchunks, bh), dim3(256), lds, s, labels, N, n, nchunks, nbits, hist_ws,
+                     counts, offsets, perm);
   return hipGetLastError();
 }
 

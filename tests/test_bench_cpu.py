@@ -46,3 +46,15 @@ def test_committed_profile_parses():
             fields[k.strip()] = v.strip()
     assert len(fields["attn.hip sha256[:16]"]) == 16
     assert float(fields["calibrated HBM bytes per launch"]) > 0
+
+
+def test_cpu_baseline_sample_on_the_tiny_config():
+    """The oracle leg on a small layer: every stage timed, the sample named."""
+    from sparse_attention_video_head_amd import synth
+    cfg = synth.CONFIGS["tiny"]
+    host = synth.make_layer(cfg)
+    r = bench.cpu_baseline(host, cfg, 0.9, budget_s=5.0)
+    assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s" and r["value"] > 0
+    assert set(r["stage_s_per_head"]) == {"kmeanspp", "lloyd", "permute_select", "attention", "unpermute"}
+    assert f"all {cfg.iters} Lloyd rounds" in r["sample"] and "32 picks per side" in r["sample"]
+    assert f"on {cfg.n_q} of {cfg.n_q} Q-clusters" in r["sample"]
