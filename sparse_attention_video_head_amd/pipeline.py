@@ -20,24 +20,6 @@ import torch
 from . import binding as B
 
 
-def _problem_parts(bh: int, split: bool):
-    """Problem ranges [lo, hi) run as separate calls: [0, s) and [s, bh) with s
-    the largest power of two below bh, so that every range starts at 0 or at a
-    power of two at least as large as the range (see _part_seed)."""
-    if not split or bh < 2:
-        return [(0, bh)]
-    s = 1 << ((bh - 1).bit_length() - 1)
-    return [(0, s), (s, bh)]
-
-
-def _part_seed(seed: int, lo: int) -> int:
-    """The seed under which problem i of a call on problems [lo, hi) draws the
-    k-means++ numbers that problem lo + i of one call on every problem draws:
-    the generator's state is seed XOR (problem * 2^32 + pick), and with lo a
-    power of two larger than every i (or 0), lo XOR i = lo + i."""
-    return (seed ^ (lo << 32)) & ((1 << 64) - 1)
-
-
 class SVG2Layer:
     def __init__(self, bh: int, n_tokens: int, head_dim: int, dtype: torch.dtype, n_q: int, n_k: int,
                  device="cuda", two_streams: bool = True, fp8_attention: bool = False):
@@ -62,12 +44,8 @@ class SVG2Layer:
         self.sel_count, self.sel_idx = e(bh, n_q), e(bh, n_q, n_k)
         self.pairs = e(bh, dt=torch.int64)
         u8 = lambda n: torch.empty(max(int(n), 1), dtype=torch.uint8, device=dev)
-        # k-means runs per side in problem ranges, each on a stream of its own:
-        # the dependent launches of one range (two per k-means++ pick) leave
-        # gaps that the other ranges' launches fill
-        self.parts = _problem_parts(bh, two_streams)
-        self.ws_kq = [u8(L.svg2_kmeans_workspace_size(hi - lo, n_tokens, head_dim, n_q)) for lo, hi in self.parts]
-        self.ws_kk = [u8(L.svg2_kmeans_workspace_size(hi - lo, n_tokens, head_dim, n_k)) for lo, hi in self.parts]
+        self.ws_kq = u8(L.svg2_kmeans_workspace_size(bh, n_tokens, head_dim, n_q))
+        self.ws_kk = u8(L.svg2_kmeans_workspace_size(bh, n_tokens, head_dim, n_k))
         self.ws_pq = u8(L.svg2_permute_workspace_size(bh, n_tokens, n_q))
         self.ws_pk = u8(L.svg2_permute_workspace_size(bh, n_tokens, n_k))
         self.ws_sel = u8(L.svg2_select_topp_workspace_size(bh, n_q, n_k))
@@ -78,7 +56,6 @@ class SVG2Layer:
         self.dense_sel = torch.zeros(bh, 1, 1, dtype=torch.int32, device=dev)
         self.ws_dense = u8(L.svg2_varblock_attn_workspace_size(bh, n_tokens, 1, 1, head_dim))
         self.side = torch.cuda.Stream(device=dev) if two_streams else None
-        self.streams = [torch.cuda.Stream(device=dev) for _ in range(2 * len(self.parts) - 1)] if two_streams else []
         # FP8 attention: E4M3 copies of Q', K', V' with per-problem scales
         self.fp8 = fp8_attention
         if fp8_attention:
@@ -89,34 +66,25 @@ class SVG2Layer:
             self.ws_q8 = u8(L.svg2_quantize_fp8_workspace_size(bh))
 
     # ------------------------------------------------------------ steps
-    def _run_parts(self, jobs):
-        """Runs the callables on the current stream and the side streams, one
-        each, after the work queued so far; the current stream waits for all."""
-        if not self.streams:
-            for job in jobs:
-                job()
+    def kmeans(self, q, k, iters: int, warm: bool, seed_q: int, seed_k: int):
+        def side_q():
+            B.kmeans(q, self.n_q, iters, init=self.cq if warm else None, seed=seed_q, centroids=self.cq,
+                     labels=self.labels_q, counts=self.counts_q, workspace=self.ws_kq)
+
+        def side_k():
+            B.kmeans(k, self.n_k, iters, init=self.ck if warm else None, seed=seed_k, centroids=self.ck,
+                     labels=self.labels_k, counts=self.counts_k, workspace=self.ws_kk)
+
+        if self.side is None:
+            side_q()
+            side_k()
             return
         main = torch.cuda.current_stream(self.dev)
-        for st, job in zip(self.streams, jobs[1:]):
-            st.wait_stream(main)
-            with torch.cuda.stream(st):
-                job()
-        jobs[0]()
-        for st in self.streams[:len(jobs) - 1]:
-            main.wait_stream(st)
-
-    def kmeans(self, q, k, iters: int, warm: bool, seed_q: int, seed_k: int):
-        jobs = []
-        for side, x, n, c, lab, cnt, ws, seed in (("k", k, self.n_k, self.ck, self.labels_k, self.counts_k,
-                                                   self.ws_kk, seed_k),
-                                                  ("q", q, self.n_q, self.cq, self.labels_q, self.counts_q,
-                                                   self.ws_kq, seed_q)):
-            for (lo, hi), w in zip(self.parts, ws):
-                def job(x=x, n=n, c=c, lab=lab, cnt=cnt, w=w, seed=seed, lo=lo, hi=hi):
-                    B.kmeans(x[lo:hi], n, iters, init=c[lo:hi] if warm else None, seed=_part_seed(seed, lo),
-                             centroids=c[lo:hi], labels=lab[lo:hi], counts=cnt[lo:hi], workspace=w)
-                jobs.append(job)
-        self._run_parts(jobs)
+        self.side.wait_stream(main)
+        with torch.cuda.stream(self.side):
+            side_k()
+        side_q()
+        main.wait_stream(self.side)
 
     def permute(self, q, k, v, quantize: bool = True):
         def side_q():
@@ -153,25 +121,28 @@ class SVG2Layer:
         f8 = self.fp8
         qo, ko, vo = (self.q8, self.k8, self.v8) if f8 else (self.qp, self.kp, self.vp)
         sq, sk, sv = (self.s8[0], self.s8[1], self.s8[2]) if f8 else (None, None, None)
-        jobs = []
-        for (lo, hi), w in zip(self.parts, self.ws_kk):
-            def job_k(lo=lo, hi=hi, w=w):
-                r = slice(lo, hi)
-                B.kmeans_permute(k[r], self.n_k, iters, y=v[r], init=self.ck[r] if warm else None,
-                                 seed=_part_seed(seed_k, lo), centroids=self.ck[r], labels=self.labels_k[r],
-                                 counts=self.counts_k[r], x_out=ko[r], y_out=vo[r], perm=self.perm_k[r],
-                                 offsets=self.off_k[r], workspace=w, fp8=f8, x_scale=sk[r] if f8 else None,
-                                 y_scale=sv[r] if f8 else None)
-            jobs.append(job_k)
-        for (lo, hi), w in zip(self.parts, self.ws_kq):
-            def job_q(lo=lo, hi=hi, w=w):
-                r = slice(lo, hi)
-                B.kmeans_permute(q[r], self.n_q, iters, init=self.cq[r] if warm else None,
-                                 seed=_part_seed(seed_q, lo), centroids=self.cq[r], labels=self.labels_q[r],
-                                 counts=self.counts_q[r], x_out=qo[r], perm=self.perm_q[r], offsets=self.off_q[r],
-                                 workspace=w, fp8=f8, x_scale=sq[r] if f8 else None)
-            jobs.append(job_q)
-        self._run_parts(jobs)
+
+        def side_q():
+            B.kmeans_permute(q, self.n_q, iters, init=self.cq if warm else None, seed=seed_q, centroids=self.cq,
+                             labels=self.labels_q, counts=self.counts_q, x_out=qo, perm=self.perm_q,
+                             offsets=self.off_q, workspace=self.ws_kq, fp8=f8, x_scale=sq)
+
+        def side_k():
+            B.kmeans_permute(k, self.n_k, iters, y=v, init=self.ck if warm else None, seed=seed_k,
+                             centroids=self.ck, labels=self.labels_k, counts=self.counts_k, x_out=ko,
+                             y_out=vo, perm=self.perm_k, offsets=self.off_k, workspace=self.ws_kk, fp8=f8,
+                             x_scale=sk, y_scale=sv)
+
+        if self.side is None:
+            side_q()
+            side_k()
+            return
+        main = torch.cuda.current_stream(self.dev)
+        self.side.wait_stream(main)
+        with torch.cuda.stream(self.side):
+            side_k()
+        side_q()
+        main.wait_stream(self.side)
 
     def select(self, top_p: float):
         B.select_topp(self.cq, self.counts_q, self.ck, self.counts_k, top_p, scale=self.scale,
