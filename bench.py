@@ -36,24 +36,39 @@ PEAK_CLOCK_MHZ = 2400.0         # the clock the published peaks assume
 
 
 class ClockSampler:
-    """Samples the shader clock (``rocm-smi -g --json``, in a child process)
-    every ~0.2 s between start() and stop(); under sustained matrix-core load
-    the clock drops well below the one the published peak assumes."""
+    """Samples the shader clock every ~0.2 s between start() and stop(), read
+    in-process from the amdgpu driver's ``pp_dpm_sclk`` file (the level marked
+    ``*`` is the current one); under sustained matrix-core load the clock drops
+    well below the one the published peak assumes.  No child process is
+    started, so the sampler is also safe under a profiler that preloads itself."""
 
     def __init__(self):
         self.mhz, self._stop, self._th = [], False, None
+        self._path = self._find()
+
+    @staticmethod
+    def _find():
+        import glob
+        for p in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+            try:
+                with open(p) as f:
+                    if "*" in f.read():
+                        return p
+            except OSError:
+                continue
+        return None
 
     def _run(self):
         import re
-        import subprocess
-        while not self._stop:
+        while not self._stop and self._path:
             try:
-                out = subprocess.run(["rocm-smi", "-g", "--json"], capture_output=True, text=True,
-                                     timeout=10).stdout
-                m = re.search(r"\((\d+)\s*Mhz\)", out, re.IGNORECASE)
-                if m:
-                    self.mhz.append(int(m.group(1)))
-            except Exception:
+                with open(self._path) as f:
+                    for line in f:
+                        if "*" in line:
+                            m = re.search(r"(\d+)\s*Mhz", line, re.IGNORECASE)
+                            if m:
+                                self.mhz.append(int(m.group(1)))
+            except OSError:
                 return
             time.sleep(0.2)
 
