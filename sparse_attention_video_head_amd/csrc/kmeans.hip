@@ -315,8 +315,11 @@ __global__ __launch_bounds__(256) void k_seed_update(
 // exceeds u_{k+1} * sum D2 (block sums, then the 256 tokens of the block).
 // Then ||c_{k+1} - c_a||^2 for every earlier pick a, from the centroid rows.
 // kSampleSplit work-groups per problem take the same (deterministic) pick and
-// share the distances; work-group 0 alone writes the pick.
-constexpr int kSampleThreads = 1024;
+// share the distances; work-group 0 alone writes the pick.  The work-groups are
+// small (4 waves) so that they find room on CUs that the other side's update
+// kernel still occupies: with the Q and K sides on two streams, one side's
+// sampler then overlaps the other side's update.
+constexpr int kSampleThreads = 256;
 constexpr int kSampleSplit = 8;
 
 template <typename T, int D>
