@@ -47,7 +47,7 @@ struct Carve {
 
 struct KmeansWs {
   double* d2;
-  int32_t* near;      // bh * N ints: the nearest pick of each token
+  int32_t* near;      // bh * N ints of space: the 16-bit nearest pick of each token
   int32_t* picks;
   double* cc;
   double* bsum;

@@ -32,7 +32,7 @@ hipError_t launch_scatter_rows(const void* src, void* dst, int esize, int d, int
 
 // --------------------------------------------------------------- kmeans.hip
 // k-means++ seeding (two kernels per pick).  d2_ws: bh*N doubles; near_ws:
-// 2*bh*N ints (nearest pick, then ||x||^2 as float); picks_ws: bh*n ints;
+// bh*N ints of space, holding bh*N 16-bit nearest-pick numbers; picks_ws: bh*n ints;
 // cc_ws: bh*n doubles; bsum_ws: bh*ceil(N/256) doubles.  Writes centroids
 // [bh,n,d] fp32 and seed_index [bh,n] (may be null).
 hipError_t launch_kmeanspp(const void* x, bool bf16, int bh, int N, int d, int n, uint64_t seed,

@@ -72,8 +72,8 @@ template <int D> struct ExactDist<float, D> {
 //   k_seed_sample(k)  one work-group per problem: pick k+1 by inverse-CDF
 //                     sampling over the block sums, then the distances from
 //                     pick k+1 to every earlier pick for the next update.
-// Per token the state is D2 (exact fp64) and the nearest pick's number
-// (12 bytes, streamed once per pick).  A pick c can lower D2(x) only if ||c - c_near||^2 < 4 D2(x)
+// Per token the state is D2 (exact fp64) and the nearest pick's number as a
+// 16-bit index (n <= 4096; 10 bytes, streamed once per pick).  A pick c can lower D2(x) only if ||c - c_near||^2 < 4 D2(x)
 // (triangle inequality, Elkan 2003), so other tokens are skipped without
 // reading x; the skip leaves D2 equal to evaluating every token.  The tokens
 // that pass the test (typically 10-30%, scattered over nearly every wave) are
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(256) void k_seed_first(
       const T* xr = Xp + (size_t)tok * D;
       d2[i] = ExactDist<T, D>::run(xr, s_cd);
       D2g[(size_t)p * N + tok] = d2[i];
-      Ag[(size_t)p * N + tok] = 0;
+      reinterpret_cast<uint16_t*>(Ag)[(size_t)p * N + tok] = 0;
     }
   }
   const double lsum = ((d2[0] + d2[1]) + d2[2]) + d2[3];
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(256) void k_seed_update(
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const T* Xp = X + (size_t)p * N * D;
   double* D2 = D2g + (size_t)p * N;
-  int32_t* A = Ag + (size_t)p * N;
+  uint16_t* A = reinterpret_cast<uint16_t*>(Ag) + (size_t)p * N;
   const double* cc = ccg + (size_t)p * n;
   const int nblk = (N + kSeedBlk - 1) / kSeedBlk;
 
@@ -207,9 +207,9 @@ __global__ __launch_bounds__(256) void k_seed_update(
   if ((N % kSeedTPL) == 0 && t0 + kSeedTPL <= N) {
     const double2 d01 = *reinterpret_cast<const double2*>(D2 + t0);
     const double2 d23 = *reinterpret_cast<const double2*>(D2 + t0 + 2);
-    const int4 av = *reinterpret_cast<const int4*>(A + t0);
+    const uint2 av = *reinterpret_cast<const uint2*>(A + t0);
     d2[0] = d01.x; d2[1] = d01.y; d2[2] = d23.x; d2[3] = d23.y;
-    a[0] = av.x; a[1] = av.y; a[2] = av.z; a[3] = av.w;
+    a[0] = (int)(av.x & 0xffffu); a[1] = (int)(av.x >> 16); a[2] = (int)(av.y & 0xffffu); a[3] = (int)(av.y >> 16);
   } else {
 #pragma unroll
     for (int i = 0; i < kSeedTPL; ++i) {
@@ -295,7 +295,7 @@ __global__ __launch_bounds__(256) void k_seed_update(
         acc = group16_sum(acc);
         if (acc < dv && sub == 0) {
           D2[tb + loc[j]] = acc;
-          A[tb + loc[j]] = k;
+          A[tb + loc[j]] = (uint16_t)k;
           s_d2[loc[j]] = acc;
         }
       }
