@@ -93,15 +93,29 @@ __global__ __launch_bounds__(256) void k_sort_place(const int32_t* __restrict__ 
   extern __shared__ int32_t cnt[];
   __shared__ int32_t scratch[17];
   const int chunk = blockIdx.x, p = blockIdx.y;
+  const int t0 = chunk * kSortChunk, t1 = min(N, t0 + kSortChunk);
+  // wave 0 loads all of the chunk's labels first: they arrive during the scan
+  // below, and the walk then pays no memory round trip per 64 tokens
+  constexpr int kSteps = kSortChunk / kWave;
+  int labs[kSteps];
+  if (threadIdx.x < kWave) {
+    const int32_t* lab = labels + (size_t)p * N;
+#pragma unroll
+    for (int i = 0; i < kSteps; ++i) {
+      const int t = t0 + i * kWave + (int)threadIdx.x;
+      labs[i] = t < t1 ? lab[t] : 0;
+    }
+  }
   const int32_t* st = start + ((size_t)p * nchunks + chunk) * n;
   const int32_t* tot = counts + (size_t)p * n;
   constexpr int E = kMaxClusters / 256;
-  int v[E];
+  int v[E], sv[E];
   int local = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int c = E * threadIdx.x + e;
     v[e] = c < n ? tot[c] : 0;
+    sv[e] = c < n ? st[c] : 0;
     local += v[e];
   }
   int grand;
@@ -110,7 +124,7 @@ __global__ __launch_bounds__(256) void k_sort_place(const int32_t* __restrict__ 
   for (int e = 0; e < E; ++e) {
     const int c = E * threadIdx.x + e;
     if (c < n) {
-      cnt[c] = r + st[c];
+      cnt[c] = r + sv[e];
       if (chunk == 0) offsets[(size_t)p * (n + 1) + c] = r;
     }
     r += v[e];
@@ -119,14 +133,13 @@ __global__ __launch_bounds__(256) void k_sort_place(const int32_t* __restrict__ 
   __syncthreads();
   if (threadIdx.x >= kWave) return;
   const int lane = threadIdx.x;
-  const int32_t* lab = labels + (size_t)p * N;
   int32_t* out = perm + (size_t)p * N;
-  const int t0 = chunk * kSortChunk, t1 = min(N, t0 + kSortChunk);
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int base = t0; base < t1; base += kWave) {
-    const int t = base + lane;
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i) {
+    const int t = t0 + i * kWave + lane;
     const bool valid = t < t1;
-    const int l = valid ? clampi(lab[t], 0, n - 1) : 0;
+    const int l = valid ? clampi(labs[i], 0, n - 1) : 0;
     uint64_t peers = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
       const bool bit = (l >> b) & 1;
