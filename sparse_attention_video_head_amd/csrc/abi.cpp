@@ -158,18 +158,28 @@ int kmeans_run(const void* x, int32_t dtype, int32_t bh, int32_t n_tokens, int32
     if (st) return st;
   }
   for (int it = 0; it < n_iters; ++it) {
-    if (bf16) {
-      const SortStart ss{w.fix.count, w.hist, (size_t)bh * sort_chunks(N) * n};
-      st = hip_status(launch_prep_centroids(centroids, bh, n, d, w.c_hi, w.c_lo, w.c_norm, ss, stream));
+    // After k-means++ the first round's labels are the seeding's nearest picks
+    // (the same exact decision), unless that round must also report min_dist.
+    const bool from_seeds = !init_centroids && it == 0 && !(it == n_iters - 1 && min_dist);
+    if (from_seeds) {
+      st = hip_status(launch_labels_from_seeding(w.near, bh, N, labels, stream));
+      if (st) return st;
+    } else {
+      if (bf16) {
+        const SortStart ss{w.fix.count, w.hist, (size_t)bh * sort_chunks(N) * n};
+        st = hip_status(launch_prep_centroids(centroids, bh, n, d, w.c_hi, w.c_lo, w.c_norm, ss, stream));
+        if (st) return st;
+      }
+      st = hip_status(launch_assign(x, bf16, bh, N, d, n, centroids, w.c_hi, w.c_lo, w.c_norm, labels,
+                                    it == n_iters - 1 ? min_dist : nullptr, w.fix, stream));
       if (st) return st;
     }
-    st = hip_status(launch_assign(x, bf16, bh, N, d, n, centroids, w.c_hi, w.c_lo, w.c_norm, labels,
-                                  it == n_iters - 1 ? min_dist : nullptr, w.fix, stream));
-    if (st) return st;
     const bool last = it == n_iters - 1 && mv.x_out;
     int32_t* pm = last ? perm_out : w.perm;
     int32_t* of = last ? offsets_out : w.offsets;
-    st = hip_status(launch_counting_sort(labels, bh, N, n, w.hist, bf16, pm, of, counts, stream));
+    // the bf16 assignment adds the sort's label histograms as it writes the labels
+    const bool have_hist = bf16 && !from_seeds;
+    st = hip_status(launch_counting_sort(labels, bh, N, n, w.hist, have_hist, pm, of, counts, stream));
     if (st) return st;
     st = hip_status(launch_centroid_mean(x, bf16, bh, N, d, n, pm, of, w.partial, centroids, stream,
                                          last ? mv : MeanMove{}));

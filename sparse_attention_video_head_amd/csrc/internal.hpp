@@ -38,6 +38,9 @@ hipError_t launch_scatter_rows(const void* src, void* dst, int esize, int d, int
 hipError_t launch_kmeanspp(const void* x, bool bf16, int bh, int N, int d, int n, uint64_t seed,
                            double* d2_ws, int32_t* near_ws, float* centroids, int32_t* seed_index,
                            int32_t* picks_ws, double* cc_ws, double* bsum_ws, hipStream_t s);
+// Labels of the first Lloyd round after seeding: each token's nearest pick,
+// from near_ws as left by launch_kmeanspp.
+hipError_t launch_labels_from_seeding(const int32_t* near_ws, int bh, int N, int32_t* labels, hipStream_t s);
 // centroid split for the matrix-core assignment: c_hi + c_lo (bf16 pair) and ||c||^2,
 // kCentroidPad-row padded per problem (padding rows: zeros, ||c||^2 = +inf)
 constexpr int kCentroidPad = 32;

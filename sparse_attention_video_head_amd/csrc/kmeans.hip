@@ -6,6 +6,8 @@
 //     its members (the counting sort of sort.hip groups the members).
 #include <limits.h>
 
+#include <algorithm>
+
 #include <type_traits>
 
 #include "common.hpp"
@@ -483,6 +485,25 @@ hipError_t launch_kmeanspp(const void* x, bool bf16, int bh, int N, int d, int n
     if (d == 128) { SVG2_SEED(float, 128) } else { SVG2_SEED(float, 64) }
   }
 #undef SVG2_SEED
+  return hipGetLastError();
+}
+
+// The first Lloyd assignment after k-means++ seeding: the seeding state
+// already holds, for every token, the pick nearest to it by the exact fp64
+// distance (ties to the earlier pick, i.e. the smaller centroid number), and
+// the centroids of that round are exactly the picked rows.  So that round's
+// labels are the state's nearest-pick numbers, and the assignment is skipped.
+__global__ __launch_bounds__(256) void k_labels_from_picks(const uint16_t* __restrict__ near, size_t total,
+                                                           int32_t* __restrict__ labels) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x)
+    labels[i] = (int32_t)near[i];
+}
+
+hipError_t launch_labels_from_seeding(const int32_t* near_ws, int bh, int N, int32_t* labels, hipStream_t s) {
+  const size_t total = (size_t)bh * N;
+  const int grid = (int)std::min<size_t>((total + 255) / 256, 8192);
+  hipLaunchKernelGGL(k_labels_from_picks, dim3(grid), dim3(256), 0, s, reinterpret_cast<const uint16_t*>(near_ws),
+                     total, labels);
   return hipGetLastError();
 }
 
