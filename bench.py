@@ -698,7 +698,14 @@ def main():
     b.record()
     torch.cuda.synchronize()
     kmeans_cold_ms = a.elapsed_time(b)
-    seeding_ms = kmeans_cold_ms - cfg.iters * ms_per_iter
+    # k-means++ alone (both sides, no Lloyd round)
+    a, b = E(), E()
+    torch.cuda.synchronize()
+    a.record()
+    layer.kmeans(q, k, 0, False, **seeds)
+    b.record()
+    torch.cuda.synchronize()
+    seeding_ms = a.elapsed_time(b)
     fused_move_ms = float(cold_stage[0]) - kmeans_cold_ms
     # the stand-alone permutation (sort + row gather of Q, K and V)
     def median_ms(fn, runs=3):
