@@ -87,6 +87,7 @@ constexpr int kSeedWavesPerWG = 4;
 constexpr int kSeedWG = kSeedWavesPerWG * kSeedBlk;   // 1024 tokens per work-group
 constexpr int kSeedGroup = 16;                        // lanes per candidate row
 constexpr int kSeedUnroll = 4;                        // candidate rows in flight per group
+constexpr int kSeedCcLds = 1024;                      // earlier picks whose distances fit the LDS copy
 
 __device__ __forceinline__ int first_pick(uint64_t seed, int p, int N) {
   return min((int)(seed_uniform(seed, p, 0) * (double)N), N - 1);
@@ -188,6 +189,7 @@ __global__ __launch_bounds__(256) void k_seed_update(
   __shared__ double s_cd[D];
   __shared__ double s_d2[kSeedWG];
   __shared__ uint16_t s_list[kSeedWG];
+  __shared__ double s_cc[kSeedCcLds];
   __shared__ int s_nc;
   const int p = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -225,14 +227,22 @@ __global__ __launch_bounds__(256) void k_seed_update(
     s_c[e] = v;
     s_cd[e] = (double)v;
   }
+  // the distances from the new pick to the earlier ones, staged in LDS with
+  // the state loads (one memory round trip instead of a dependent gather)
+  const bool cc_lds = k <= kSeedCcLds;
+  if (cc_lds)
+    for (int e = tid; e < k; e += 256) s_cc[e] = cc[e];
   if (tid == 0) s_nc = 0;
+#pragma unroll
+  for (int i = 0; i < kSeedTPL; ++i) s_d2[l0 + i] = d2[i];
+  __syncthreads();
   unsigned m = 0;
 #pragma unroll
   for (int i = 0; i < kSeedTPL; ++i) {
-    if (t0 + i < N && cc[clampi(a[i], 0, k - 1)] < 4.0 * d2[i] * (1.0 + 0x1p-20)) m |= 1u << i;
-    s_d2[l0 + i] = d2[i];
+    const int ai = clampi(a[i], 0, k - 1);
+    const double cai = cc_lds ? s_cc[ai] : cc[ai];
+    if (t0 + i < N && cai < 4.0 * d2[i] * (1.0 + 0x1p-20)) m |= 1u << i;
   }
-  __syncthreads();
   float cn = 0.f;
   if (kBF16) {
     for (int e = lane; e < D; e += kWave) cn = fmaf(s_c[e], s_c[e], cn);
