@@ -404,6 +404,34 @@ def test_kmeans_permute_fp8_equals_quantized_rows(d, N, n, iters, with_y):
         assert got["y_perm"] is None and got["y_scale"] is None
 
 
+@pytest.mark.parametrize("dt,d,N,n", [("bf16", 128, 6000, 50), ("f32", 64, 4096, 64), ("bf16", 64, 3001, 37)])
+def test_first_round_after_seeding_vs_oracle(dt, d, N, n):
+    """After k-means++ the first round's labels are the seeding's nearest picks
+    (no assignment runs); asked for min_dist, the same round runs the
+    assignment.  Both must equal the oracle's assignment of the tokens to the
+    picked rows outside the tie band, and equal each other bit for bit."""
+    bh = 2
+    q, _, _ = mixture(bh, N, d, comps=max(4, n // 2), seed=3 * N + n, dtype=dtype_of(dt))
+    seed = 0x5EED + n
+    qd = q.to(DEV)
+    fast = B.kmeans(qd, n, 1, seed=seed, seed_index=True)
+    full = B.kmeans(qd, n, 1, seed=seed, seed_index=True, min_dist=True)
+    torch.cuda.synchronize()
+    assert torch.equal(fast["seed_index"], full["seed_index"])
+    for h in range(bh):
+        X = np64(q[h])
+        C0 = X[fast["seed_index"][h].cpu().numpy()]
+        a = oracle.assign(X, C0)
+        for r in (fast, full):
+            lab = r["labels"][h].cpu().numpy()
+            check_labels_in_tie_band(X, C0, lab, a, max_share=1e-3 + 1.0 / N)
+            np.testing.assert_array_equal(r["counts"][h].cpu().numpy(), np.bincount(lab, minlength=n))
+        np.testing.assert_allclose(full["min_dist"][h].cpu().numpy(), a.min_dist, rtol=1e-4, atol=1e-3)
+    assert torch.equal(fast["labels"], full["labels"])
+    assert torch.equal(fast["counts"], full["counts"])
+    assert torch.equal(fast["centroids"], full["centroids"])
+
+
 @pytest.mark.parametrize("dt,d,N,n,heads", [("f32", 64, 4096, 64, 1), ("bf16", 128, 16384, 250, 2),
                                            ("bf16", 128, 3000, 100, 2), ("bf16", 64, 700, 700, 1)])
 def test_kmeanspp_picks_match_oracle(dt, d, N, n, heads):
