@@ -342,6 +342,7 @@ def test_kmeans_chained_rounds_equal_one_call():
 
 @pytest.mark.parametrize("dt,d,N,n,iters,warm,with_y", [
     ("bf16", 128, 5000, 40, 3, False, True), ("bf16", 128, 3001, 37, 1, True, True),
+    ("bf16", 128, 3001, 37, 1, False, True),
     ("bf16", 64, 2000, 17, 2, False, False), ("f32", 64, 4097, 64, 2, True, True),
     ("bf16", 128, 700, 700, 1, False, True), ("bf16", 128, 1000, 1, 2, True, False),
 ])
@@ -404,7 +405,8 @@ def test_kmeans_permute_fp8_equals_quantized_rows(d, N, n, iters, with_y):
         assert got["y_perm"] is None and got["y_scale"] is None
 
 
-@pytest.mark.parametrize("dt,d,N,n", [("bf16", 128, 6000, 50), ("f32", 64, 4096, 64), ("bf16", 64, 3001, 37)])
+@pytest.mark.parametrize("dt,d,N,n", [("bf16", 128, 6000, 50), ("f32", 64, 4096, 64), ("bf16", 64, 3001, 37),
+                                      ("bf16", 128, 2000, 1)])
 def test_first_round_after_seeding_vs_oracle(dt, d, N, n):
     """After k-means++ the first round's labels are the seeding's nearest picks
     (no assignment runs); asked for min_dist, the same round runs the
