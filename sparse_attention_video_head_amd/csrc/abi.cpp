@@ -109,6 +109,7 @@ AttnWs carve_attn(Carve& c, int bh, int N, int n_q) {
   w.xcount = c.take<int32_t>((size_t)bh * kAttnXcds);
   w.queue = c.take<int32_t>(2 * kAttnXcds);
   w.flat = c.take<int32_t>((size_t)kAttnXcds * bh * mx * 2);
+  w.kmax = c.take<uint32_t>((size_t)bh);
   return w;
 }
 

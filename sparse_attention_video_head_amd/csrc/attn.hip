@@ -13,7 +13,10 @@
 //   online softmax     fp32, base 2 (scale * log2 e folded in), per lane: one
 //                      query, 16 of the tile's keys; one cross-half exchange
 //                      for the max; the row sum adds the bf16-rounded P that
-//                      weight V, so the normaliser is the sum of the weights
+//                      weight V, so the normaliser is the sum of the weights.
+//                      Where the Cauchy-Schwarz bound of a wave's scores is
+//                      small, the reference is fixed at that bound and no
+//                      maximum is taken (k_key_norm_max gives max ||k||).
 //   O^T += V^T P^T     P re-used straight from the S accumulator (no shuffle):
 //                      the key order inside each 16-key MFMA step is permuted,
 //                      and V^T is staged in LDS in the same permuted order.
@@ -45,8 +48,10 @@ constexpr int kSortTilesMax = (1 << 19) - 1;
 __global__ __launch_bounds__(256) void k_attn_lengths(const int32_t* __restrict__ k_off, int n_k, int N,
                                                       const int32_t* __restrict__ sel_count,
                                                       const int32_t* __restrict__ sel_idx, int n_q,
-                                                      int tile, int32_t* __restrict__ tiles) {
+                                                      int tile, int32_t* __restrict__ tiles,
+                                                      uint32_t* __restrict__ kmax) {
   const int p = blockIdx.y;
+  if (kmax && blockIdx.x == 0 && threadIdx.x == 0) kmax[p] = 0u;    // for k_key_norm_max
   const int i = blockIdx.x * (blockDim.x / kWave) + (int)(threadIdx.x / kWave);
   if (i >= n_q) return;
   const int lane = lane_id();
@@ -64,6 +69,38 @@ __global__ __launch_bounds__(256) void k_attn_lengths(const int32_t* __restrict_
 #pragma unroll
   for (int o = kWave / 2; o > 0; o >>= 1) keys += __shfl_xor(keys, o);
   if (lane == 0) tiles[(size_t)p * n_q + i] = (int32_t)min((keys + tile - 1) / tile, (long long)kSortTilesMax);
+}
+
+// Largest squared key norm of each problem, for the bf16 kernel's fixed
+// softmax reference (below): 512 rows per work-group, D/8 lanes per row
+// (16 bytes each), fp32 sums of the squares, one atomic max per wave on the
+// value's bits (non-negative floats order like their bit patterns).
+template <int D>
+__global__ __launch_bounds__(256) void k_key_norm_max(const uint16_t* __restrict__ K, int N,
+                                                      uint32_t* __restrict__ kmax) {
+  constexpr int LPR = D / 8;                 // lanes per row
+  constexpr int RPP = 256 / LPR;             // rows per pass of the work-group
+  const int p = blockIdx.y;
+  const int sub = threadIdx.x % LPR;
+  const uint16_t* Kp = K + (size_t)p * N * D;
+  float best = 0.f;
+  const int r0 = blockIdx.x * 512;
+  for (int r = r0 + (int)threadIdx.x / LPR; r < min(N, r0 + 512); r += RPP) {
+    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(Kp + (size_t)r * D + sub * 8);
+    float s2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a = bf16_lo(w[e]), b = bf16_hi(w[e]);
+      s2 = fmaf(a, a, s2);
+      s2 = fmaf(b, b, s2);
+    }
+#pragma unroll
+    for (int m = LPR / 2; m >= 1; m >>= 1) s2 += __shfl_xor(s2, m);
+    best = fmaxf(best, s2);
+  }
+#pragma unroll
+  for (int m = kWave / 2; m >= 1; m >>= 1) best = fmaxf(best, __shfl_xor(best, m));
+  if (lane_id() == 0) atomicMax(kmax + p, __float_as_uint(best));
 }
 
 // Clusters of problem p in decreasing order of key tiles (ties: lower cluster
@@ -308,6 +345,9 @@ struct KeyCursor {
 // <= 2^kLazyTau and O / l are rescaled rarely.  The result is the same
 // softmax; only the intermediate scaling differs.
 constexpr float kLazyTau = 8.f;
+// Largest score bound (log2 units) at which the bf16 kernel fixes a query's
+// reference instead of tracking the running maximum.
+constexpr float kFixedBound = 32.f;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) uint16_t lds_u16_t;
@@ -535,7 +575,7 @@ __global__ __launch_bounds__(256, 3) void k_attn_bf16(
     int N, const int32_t* __restrict__ q_off, int n_q, const int32_t* __restrict__ k_off, int n_k,
     const int32_t* __restrict__ sel_count, const int32_t* __restrict__ sel_idx, float scale_log2,
     uint16_t* __restrict__ O, float* __restrict__ lse, OutMap om, const int32_t* __restrict__ flat,
-    int32_t* __restrict__ queue, size_t cap) {
+    int32_t* __restrict__ queue, size_t cap, const uint32_t* __restrict__ kmax) {
   constexpr int BN = kAttnBN;
   constexpr int KS = D / 16;           // 16-wide k-steps of Q.K
   constexpr int DT = D / 32;           // 32-row tiles of O^T
@@ -618,6 +658,33 @@ __global__ __launch_bounds__(256, 3) void k_attn_bf16(
       float thr = -__builtin_inff();
       const float inv_scale_log2 = 1.f / scale_log2;
       float l_a = 0.f, l_b = 0.f;                    // this lane's share of the row sum
+      // Fixed reference.  Every score of this query lies in [-sbound, sbound]
+      // after the scale, sbound = scale_log2 * ||q|| * max ||k|| (Cauchy-Schwarz,
+      // with a margin for the matrix core's fp32 sums).  So with the reference
+      // at sbound the weights 2^(s * scale_log2 - sbound) are at most 1, and the
+      // largest weight of the row is at least 2^(-2 sbound).  When sbound is at
+      // most kFixedBound for every query of the wave, the reference is fixed
+      // there for the whole key list and the per-tile maximum is not computed
+      // (the largest weight then stays above 2^-64, far from underflow).
+      bool fixed_ref;
+      {
+        float qn = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const u32x4_t w = __builtin_bit_cast(u32x4_t, qf[ks]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float a = bf16_lo(w[e]), b = bf16_hi(w[e]);
+            qn = fmaf(a, a, qn);
+            qn = fmaf(b, b, qn);
+          }
+        }
+        const auto sq = __builtin_amdgcn_permlane32_swap(__float_as_uint(qn), __float_as_uint(qn), false, false);
+        qn = __uint_as_float(sq[0]) + __uint_as_float(sq[1]);
+        const float sbound = scale_log2 * sqrtf(qn * __uint_as_float(kmax[p])) * (1.f + 0x1p-10f) + 0x1p-20f;
+        fixed_ref = __ballot(!(sbound <= kFixedBound)) == 0ull;
+        if (fixed_ref) m_ref = sbound;
+      }
       f32x16_t o[DT];
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
@@ -721,7 +788,7 @@ __global__ __launch_bounds__(256, 3) void k_attn_bf16(
         }
       };
       // Scores, softmax and O^T += V^T P^T of the tile in slot s.
-      auto step = [&](int s, int filled) __attribute__((always_inline)) {
+      auto step = [&](int s, int filled, auto fixed_c) __attribute__((always_inline)) {
         f32x16_t sc;
         scores(s, sc);
         __builtin_amdgcn_s_setprio(0);
@@ -733,26 +800,28 @@ __global__ __launch_bounds__(256, 3) void k_attn_bf16(
           for (int i = 0; i < 16; ++i)
             if ((i >> 2) * 8 + (i & 3) >= lim) sc[i] = -__builtin_inff();
         }
-        // raw max of the tile's scores for this query (v_maximum3: scores are
-        // never NaN, and the NaN-propagating maximum needs no canonicalising)
-        float mx = sc[0];
+        if constexpr (!decltype(fixed_c)::value) {
+          // raw max of the tile's scores for this query (v_maximum3: scores are
+          // never NaN, and the NaN-propagating maximum needs no canonicalising)
+          float mx = sc[0];
 #pragma unroll
-        for (int i = 1; i < 16; ++i) mx = __builtin_elementwise_maximum(mx, sc[i]);
-        {
-          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-          mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        }
-        if (mx > thr) {
-          const float m_new = mx * scale_log2;
-          const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
-          l_a *= alpha;
-          l_b *= alpha;
+          for (int i = 1; i < 16; ++i) mx = __builtin_elementwise_maximum(mx, sc[i]);
+          {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+          }
+          if (mx > thr) {
+            const float m_new = mx * scale_log2;
+            const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
+            l_a *= alpha;
+            l_b *= alpha;
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
-          m_ref = m_new;
-          thr = (m_new + kLazyTau) * inv_scale_log2;
+              for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+            m_ref = m_new;
+            thr = (m_new + kLazyTau) * inv_scale_log2;
+          }
         }
         const float neg = -m_ref;
         const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
@@ -808,7 +877,7 @@ __global__ __launch_bounds__(256, 3) void k_attn_bf16(
 
       // step t (tile t in slot s = t % 3, compile-time): load tile t+2 into slot
       // (s+2) % 3, compute tile t, wait for tile t+1, barrier
-      auto iter = [&](auto sc_) __attribute__((always_inline)) -> bool {
+      auto iter = [&](auto sc_, auto fixed_c) __attribute__((always_inline)) -> bool {
         constexpr int s = decltype(sc_)::value;
         int f2 = 0;
         if (f1 > 0) {
@@ -819,16 +888,27 @@ __global__ __launch_bounds__(256, 3) void k_attn_bf16(
           for (int q = 0; q < INS; ++q) key[q] = -1;
         }
         load_tile((s + 2) % 3, first, key);
-        if (active) step(s, f0);
+        if (active) step(s, f0, fixed_c);
         __builtin_amdgcn_s_waitcnt(kWaitTile);       // tiles <= t+1 have landed
         lds_barrier();
         f0 = f1;
         f1 = f2;
         return f0 > 0;
       };
+      // one loop per reference mode, so that neither carries the other's
+      // registers; a work-group's waves may run different ones (the loops take
+      // the same barriers in the same order)
       if (f0 > 0) {
-        while (iter(std::integral_constant<int, 0>{}) && iter(std::integral_constant<int, 1>{}) &&
-               iter(std::integral_constant<int, 2>{})) {
+        if (fixed_ref) {
+          const std::true_type fx;
+          while (iter(std::integral_constant<int, 0>{}, fx) && iter(std::integral_constant<int, 1>{}, fx) &&
+                 iter(std::integral_constant<int, 2>{}, fx)) {
+          }
+        } else {
+          const std::false_type fx;
+          while (iter(std::integral_constant<int, 0>{}, fx) && iter(std::integral_constant<int, 1>{}, fx) &&
+                 iter(std::integral_constant<int, 2>{}, fx)) {
+          }
         }
       }
       __builtin_amdgcn_s_waitcnt(0xF70);             // no tile load outlives the loop
@@ -1272,8 +1352,13 @@ hipError_t launch_varblock_attn(const void* q, const void* k, const void* v, boo
   const int bm = attn_block_rows(bf16);
   const int max_items = attn_max_items(N, n_q, bm);
   hipLaunchKernelGGL(k_attn_lengths, dim3((n_q + 3) / 4, bh), dim3(256), 0, s, k_off, n_k, N, sel_count,
-                     sel_idx, n_q, bf16 ? kAttnBN : 32, ws.tiles);
+                     sel_idx, n_q, bf16 ? kAttnBN : 32, ws.tiles, ws.kmax);
   if (bf16) {
+    const dim3 gk((N + 511) / 512, bh);
+    if (d == 128)
+      hipLaunchKernelGGL(k_key_norm_max<128>, gk, dim3(256), 0, s, static_cast<const uint16_t*>(k), N, ws.kmax);
+    else
+      hipLaunchKernelGGL(k_key_norm_max<64>, gk, dim3(256), 0, s, static_cast<const uint16_t*>(k), N, ws.kmax);
     hipLaunchKernelGGL(k_attn_plan_xcd, dim3(bh), dim3(1024), 0, s, q_off, n_q, N, bm, max_items, ws.tiles,
                        ws.xcount, ws.xitems);
     hipLaunchKernelGGL(k_attn_flatten, dim3(kAttnXcds), dim3(256), 0, s, ws.xcount, ws.xitems, bh, max_items,
@@ -1285,7 +1370,7 @@ hipError_t launch_varblock_attn(const void* q, const void* k, const void* v, boo
   hipLaunchKernelGGL(k_attn_bf16<D>, grid_p, dim3(256), 0, s, static_cast<const uint16_t*>(q),        \
                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), N, q_off, n_q, \
                      k_off, n_k, sel_count, sel_idx, sl2, static_cast<uint16_t*>(out), lse, om, ws.flat, \
-                     ws.queue, cap)
+                     ws.queue, cap, ws.kmax)
     if (d == 128) SVG2_ATTN(128); else SVG2_ATTN(64);
 #undef SVG2_ATTN
   } else {
@@ -1310,7 +1395,7 @@ hipError_t launch_varblock_attn_fp8(const void* q, const void* k, const void* v,
                                     float* lse, const OutMap& om, const AttnWs& ws, hipStream_t s) {
   const int max_items = attn_max_items(N, n_q, kAttnBM);
   hipLaunchKernelGGL(k_attn_lengths, dim3((n_q + 3) / 4, bh), dim3(256), 0, s, k_off, n_k, N, sel_count, sel_idx,
-                     n_q, kAttnF8BN, ws.tiles);
+                     n_q, kAttnF8BN, ws.tiles, nullptr);
   hipLaunchKernelGGL(k_attn_plan_xcd, dim3(bh), dim3(1024), 0, s, q_off, n_q, N, kAttnBM, max_items, ws.tiles,
                      ws.xcount, ws.xitems);
   hipLaunchKernelGGL(k_attn_flatten, dim3(kAttnXcds), dim3(256), 0, s, ws.xcount, ws.xitems, bh, max_items,

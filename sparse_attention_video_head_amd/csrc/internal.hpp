@@ -111,6 +111,7 @@ struct AttnWs {
   int32_t* xcount;       // [bh, kAttnXcds]
   int32_t* queue;        // [2 kAttnXcds]
   int32_t* flat;         // [kAttnXcds, bh * attn_max_items(N, n_q, 128), 2]
+  uint32_t* kmax;        // [bh] largest squared key norm per problem (fp32 bits)
 };
 // Where the attention writes output row r of problem p: row t = perm[p, r]
 // (r itself when perm is null) at element offset (p / heads) * bs +

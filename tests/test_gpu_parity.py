@@ -198,6 +198,40 @@ def test_varblock_attn_vs_oracle(dt, d, N, n_q, n_k, top_p):
         assert np.all(gl[~fin] == -np.inf) and np.all(got[~fin] == 0)
 
 
+@pytest.mark.parametrize("boost", [1.0, 4.0, 12.0])
+def test_varblock_attn_reference_modes_vs_oracle(boost):
+    """The bf16 kernel fixes a query's softmax reference at the Cauchy-Schwarz
+    bound of its scores when that bound is small for its whole wave (32 rows),
+    and tracks the running maximum otherwise.  In every Q-cluster the rows of
+    every other 32-row block are multiplied by `boost` (the products, rounded
+    to bf16, are the inputs of both sides), so that with boost > 1 the waves of
+    one work-group run both modes, and with 12 the large scores also meet the
+    lazy rescale; each must match the oracle."""
+    bh, N, d, n_q, n_k = 2, 3000, 128, 24, 60
+    q, k, v, qo, ko, cnt, idx, lists, qo_np, ko_np = _attn_case("bf16", d, bh, N, n_q, n_k, 0.9, seed=404)
+    qf = q.float()
+    for h in range(bh):
+        for i in range(n_q):
+            a, b = int(qo_np[h][i]), int(qo_np[h][i + 1])
+            for r0 in range(a + 32, b, 64):
+                qf[h, r0:min(r0 + 32, b)] *= boost
+    q = qf.to(torch.bfloat16)
+    out, lse = B.varblock_attn(q.to(DEV), k.to(DEV), v.to(DEV), qo, ko, cnt, idx, lse=True)
+    torch.cuda.synchronize()
+    s = 1 / math.sqrt(d)
+    for h in range(bh):
+        ref, ref_lse = oracle.block_attention(np64(q[h]), np64(k[h]), np64(v[h]), qo_np[h], ko_np[h], lists[h], s)
+        got = np64(out[h])
+        assert np.max(np.abs(got - ref)) <= 2e-2
+        assert rel_l2(got, ref) <= 1e-2
+        gl = lse[h].cpu().numpy().astype(np.float64)
+        fin = np.isfinite(ref_lse)
+        # the bf16 normaliser bound of test_varblock_attn_vs_oracle, plus the
+        # fp32 rounding of the scores, which grows with their size (scores of
+        # ~200 here at boost 12): 3e-5 relative
+        np.testing.assert_allclose(gl[fin], ref_lse[fin], rtol=3e-5, atol=2.5e-3)
+
+
 @pytest.mark.parametrize("dt,d,layout", [("bf16", 128, "contiguous"), ("bf16", 128, "bnhd"), ("f32", 64, "bnhd"),
                                          ("bf16", 64, "contiguous")])
 def test_varblock_attn_unpermute_vs_oracle(dt, d, layout):
