@@ -341,6 +341,7 @@ size_t svg2_select_topp_workspace_size(int32_t bh, int32_t n_q, int32_t n_k) {
   if (bh < 1 || n_q < 1 || n_q > kMaxClusters || n_k < 1 || n_k > kMaxClusters) return 0;
   Carve c(nullptr);
   c.take<int64_t>((size_t)bh * n_q);
+  c.take<double>((size_t)bh * n_q * n_k);
   return c.off;
 }
 
@@ -364,9 +365,10 @@ int svg2_select_topp(const float* q_centroids, const int32_t* q_counts, int32_t 
   if (!aligned(workspace, kAlign)) return SVG2_ERR_INVALID_ARG;
   Carve c(workspace);
   int64_t* row_pairs = c.take<int64_t>((size_t)bh * n_q);
+  double* logits = c.take<double>((size_t)bh * n_q * n_k);
   return hip_status(launch_select_topp(q_centroids, q_counts, n_q, k_centroids, k_counts, n_k, bh, head_dim,
                                        (double)scale, (double)top_p, sel_count, sel_idx, probs, row_pairs,
-                                       pair_count, stream));
+                                       logits, pair_count, stream));
 }
 
 // ------------------------------------------------------------------ attention

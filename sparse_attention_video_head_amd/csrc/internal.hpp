@@ -93,7 +93,7 @@ hipError_t launch_amax_bf16(const void* x, int bh, int N, int d, uint32_t* amax_
 hipError_t launch_select_topp(const float* cq, const int32_t* q_counts, int n_q, const float* ck,
                               const int32_t* k_counts, int n_k, int bh, int d, double scale,
                               double top_p, int32_t* sel_count, int32_t* sel_idx, float* probs,
-                              int64_t* row_pairs_ws, int64_t* pair_count, hipStream_t s);
+                              int64_t* row_pairs_ws, double* logits_ws, int64_t* pair_count, hipStream_t s);
 
 // ----------------------------------------------------------------- attn.hip
 int attn_block_rows(bool bf16);
