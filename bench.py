@@ -725,6 +725,11 @@ def main():
     # the stand-alone inverse permutation (the layer fuses it into the
     # attention's stores, where it costs no pass of its own)
     unpermute_ms = median_ms(layer.unpermute)
+    # a plain device copy of one K-sized tensor: what one read-and-write pass
+    # over HBM reaches on this device, beside the 8 TB/s published peak
+    k_copy = torch.empty_like(k)
+    copy_ms = median_ms(lambda: k_copy.copy_(k))
+    del k_copy
     # the Lloyd round's kernels one side at a time (one stream, final labels):
     # the update alone (counting sort + segmented mean) and a whole round
     # (centroid halves + assignment + update); the assignment is the difference
@@ -829,6 +834,7 @@ def main():
         "permute_ms_standalone": round(permute_ms, 4),
         "permute_gbps": round(permute_bytes / (permute_ms * 1e-3) / 1e9, 1),
         "unpermute_gbps": round(unpermute_bytes / (unpermute_ms * 1e-3) / 1e9, 1),
+        "device_copy_gbps": round(2 * k.numel() * k.element_size() / (copy_ms * 1e-3) / 1e9, 1),
         "roofline": {"bound": "mfma",
                      "kernel": "k_attn_fp8" if args.fp8 else ("k_attn_bf16" if cfg.dtype == "bf16" else "k_attn_f32"),
                      "achieved": round(attn_tflops, 2), "peak": peak, "unit": "TFLOP/s",

@@ -72,9 +72,13 @@ __global__ __launch_bounds__(256) void k_attn_lengths(const int32_t* __restrict_
 }
 
 // Largest squared key norm of each problem, for the bf16 kernel's fixed
-// softmax reference (below): 512 rows per work-group, D/8 lanes per row
-// (16 bytes each), fp32 sums of the squares, one atomic max per wave on the
-// value's bits (non-negative floats order like their bit patterns).
+// softmax reference (below): 2048 rows per work-group, D/8 lanes per row
+// (16 bytes each), 8 rows' loads in flight per lane, fp32 sums of the squares,
+// the work-group's maximum in LDS, then one atomic max per work-group on the
+// value's bits (non-negative floats order like their bit patterns).  Atomics
+// on one address are served one at a time, so there are few of them.
+constexpr int kNormRows = 2048;
+
 template <int D>
 __global__ __launch_bounds__(256) void k_key_norm_max(const uint16_t* __restrict__ K, int N,
                                                       uint32_t* __restrict__ kmax) {
@@ -84,9 +88,12 @@ __global__ __launch_bounds__(256) void k_key_norm_max(const uint16_t* __restrict
   const int sub = threadIdx.x % LPR;
   const uint16_t* Kp = K + (size_t)p * N * D;
   float best = 0.f;
-  const int r0 = blockIdx.x * 512;
-  for (int r = r0 + (int)threadIdx.x / LPR; r < min(N, r0 + 512); r += RPP) {
-    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(Kp + (size_t)r * D + sub * 8);
+  const int rb = blockIdx.x * kNormRows + (int)threadIdx.x / LPR;
+#pragma unroll 8
+  for (int it = 0; it < kNormRows / RPP; ++it) {
+    const int r = rb + it * RPP;
+    u32x4_t w = {0u, 0u, 0u, 0u};
+    if (r < N) w = *reinterpret_cast<const u32x4_t*>(Kp + (size_t)r * D + sub * 8);
     float s2 = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -100,7 +107,13 @@ __global__ __launch_bounds__(256) void k_key_norm_max(const uint16_t* __restrict
   }
 #pragma unroll
   for (int m = kWave / 2; m >= 1; m >>= 1) best = fmaxf(best, __shfl_xor(best, m));
-  if (lane_id() == 0) atomicMax(kmax + p, __float_as_uint(best));
+  __shared__ float s_best[256 / kWave];
+  if (lane_id() == 0) s_best[threadIdx.x / kWave] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 256 / kWave; ++w) best = fmaxf(best, s_best[w]);
+    atomicMax(kmax + p, __float_as_uint(best));
+  }
 }
 
 // Clusters of problem p in decreasing order of key tiles (ties: lower cluster
@@ -1354,7 +1367,7 @@ hipError_t launch_varblock_attn(const void* q, const void* k, const void* v, boo
   hipLaunchKernelGGL(k_attn_lengths, dim3((n_q + 3) / 4, bh), dim3(256), 0, s, k_off, n_k, N, sel_count,
                      sel_idx, n_q, bf16 ? kAttnBN : 32, ws.tiles, ws.kmax);
   if (bf16) {
-    const dim3 gk((N + 511) / 512, bh);
+    const dim3 gk((N + kNormRows - 1) / kNormRows, bh);
     if (d == 128)
       hipLaunchKernelGGL(k_key_norm_max<128>, gk, dim3(256), 0, s, static_cast<const uint16_t*>(k), N, ws.kmax);
     else
