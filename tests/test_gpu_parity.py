@@ -108,6 +108,8 @@ def test_unpermute_bit_exact(dt, d):
 @pytest.mark.parametrize("n_q,n_k,d,top_p,spread", [
     (40, 250, 128, 0.9, 1.0), (17, 1000, 128, 0.8, 0.5), (8, 64, 64, 0.95, 1.5), (5, 1, 64, 0.5, 1.0),
     (12, 4096, 128, 0.9, 0.7), (9, 300, 128, 1.0, 1.0), (9, 300, 128, 1e-6, 1.0),
+    # sort sizes: 128 entries (one thread each, a cross-wave stage) and 2048 (the shared-memory network)
+    (6, 100, 64, 0.9, 1.0), (7, 1500, 128, 0.95, 0.8),
 ])
 def test_select_topp_exact(n_q, n_k, d, top_p, spread):
     bh = 2
