@@ -22,24 +22,31 @@ __global__ void k_quant_zero(uint32_t* amax, int bh) {
 }
 
 // max |x| per problem: non-negative floats order like their bit patterns, so
-// an unsigned atomic max of the bits is exact and order-independent
+// an unsigned atomic max of the bits is exact and order-independent.  Each
+// work-group covers kAmaxSub blocks of kQuantPerWG elements and issues one
+// atomic: atomics on one address are served one at a time, so there are few.
+constexpr int kAmaxSub = 16;
+
 __global__ __launch_bounds__(kQuantThreads) void k_quant_amax(const uint16_t* __restrict__ x, size_t per_problem,
                                                               uint32_t* __restrict__ amax) {
   __shared__ float s_red[17];
   const int p = blockIdx.y;
   const uint16_t* xp = x + (size_t)p * per_problem;
-  const size_t base = (size_t)blockIdx.x * kQuantPerWG;
   float m = 0.f;
+  for (int sb = 0; sb < kAmaxSub; ++sb) {
+    const size_t base = ((size_t)blockIdx.x * kAmaxSub + sb) * kQuantPerWG;
+    if (base >= per_problem) break;
 #pragma unroll
-  for (int u = 0; u < kQuantUnroll; ++u) {
-    const size_t e = base + ((size_t)u * kQuantThreads + threadIdx.x) * kQuantVec;
-    if (e + kQuantVec <= per_problem) {
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(xp + e);
+    for (int u = 0; u < kQuantUnroll; ++u) {
+      const size_t e = base + ((size_t)u * kQuantThreads + threadIdx.x) * kQuantVec;
+      if (e + kQuantVec <= per_problem) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(xp + e);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) m = fmaxf(m, fmaxf(fabsf(bf16_lo(v[w])), fabsf(bf16_hi(v[w]))));
-    } else {
-      for (size_t i = e; i < per_problem && i < e + kQuantVec; ++i)
-        m = fmaxf(m, fabsf(__uint_as_float((uint32_t)xp[i] << 16)));
+        for (int w = 0; w < 4; ++w) m = fmaxf(m, fmaxf(fabsf(bf16_lo(v[w])), fabsf(bf16_hi(v[w]))));
+      } else {
+        for (size_t i = e; i < per_problem && i < e + kQuantVec; ++i)
+          m = fmaxf(m, fabsf(__uint_as_float((uint32_t)xp[i] << 16)));
+      }
     }
   }
   m = wave_max(m);
@@ -78,7 +85,8 @@ __global__ __launch_bounds__(kQuantThreads) void k_quant_fp8(const uint16_t* __r
 
 hipError_t launch_amax_bf16(const void* x, int bh, int N, int d, uint32_t* amax_ws, hipStream_t s) {
   const size_t per = (size_t)N * d;
-  const dim3 grid((unsigned)((per + kQuantPerWG - 1) / kQuantPerWG), bh);
+  const size_t per_wg = (size_t)kQuantPerWG * kAmaxSub;
+  const dim3 grid((unsigned)((per + per_wg - 1) / per_wg), bh);
   hipLaunchKernelGGL(k_quant_zero, dim3((bh + 255) / 256), dim3(256), 0, s, amax_ws, bh);
   hipLaunchKernelGGL(k_quant_amax, grid, dim3(kQuantThreads), 0, s, static_cast<const uint16_t*>(x), per, amax_ws);
   return hipGetLastError();
