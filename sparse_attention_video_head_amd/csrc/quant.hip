@@ -96,7 +96,7 @@ hipError_t launch_quantize_fp8(const void* x, int bh, int N, int d, uint8_t* x8,
                                hipStream_t s) {
   const size_t per = (size_t)N * d;
   const dim3 grid((unsigned)((per + kQuantPerWG - 1) / kQuantPerWG), bh);
-  launch_amax_bf16(x, bh, N, d, amax_ws, s);
+  if (const hipError_t e = launch_amax_bf16(x, bh, N, d, amax_ws, s); e != hipSuccess) return e;
   hipLaunchKernelGGL(k_quant_fp8, grid, dim3(kQuantThreads), 0, s, static_cast<const uint16_t*>(x), per, amax_ws,
                      x8, scale);
   return hipGetLastError();
